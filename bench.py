@@ -1,0 +1,219 @@
+"""Benchmark of the Gated DeltaNet token-mixer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the hot path over one batch of seeded synthetic input
+already resident in HBM: cu_seqlens localisation, causal conv1d + SiLU with
+halo, chunked gated delta rule forward (and, for a workload with backward,
+the chunk and conv backward).  Default workload: the 131072-token single
+sequence with 16 q/k heads and 32 value heads, dk = dv = 128, bfloat16.
+
+Prints one JSON line with throughput (tokens/s), per-call times from HIP
+events on the launch stream, the roofline position of the dominant call and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s conv1d+chunk_gated_delta fwd(+bwd), 1 GPU; % bf16 MFMA / HBM peak"
+HBM_PEAK = 8.0e12           # B/s, MI355X published
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense FLOP/s, MI355X published
+BT = 64
+
+
+def chunk_fwd_flops_per_token_head(dk, dv, C=BT):
+    """Algorithmic FLOP of the chunked forward per token and value head: the
+    products of the page's chunk algorithm, triangular ones counted at half.
+      kh kh^T, qh kh^T (lower halves)   2 * C*dk
+      T (I+L)^-1 (triangular solve)     2*C*C/3
+      u = T vb, w = T kb (lower halves) C*dv + C*dk
+      w S, qh S                          4*dk*dv
+      P v_new (lower half)               C*dv
+      kh^T v_new (state update)          2*dk*dv
+    = C*(3dk + 2dv) + 2C^2/3 + 6*dk*dv."""
+    return C * (3 * dk + 2 * dv) + 2 * C * C / 3 + 6 * dk * dv
+
+
+def conv_bytes_per_token(C, s):
+    return 2 * C * s  # read x, write y
+
+
+def chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s):
+    """Algorithmic HBM bytes of one chunk forward: read q, k, v, g, beta;
+    write o; read h0 and write ht once per sequence."""
+    per_tok = 2 * Hk * dk * s + 2 * Hv * dv * s + 8 * Hv
+    return T * per_tok + 2 * N * Hv * dk * dv * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long131k_hk16_hv32_d128_bf16")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the oracle sample (0: chosen for ~10-30 s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from linear_attention_sequence_causal_amd import gdn, workloads
+
+    gdn.load_library()
+    spec = workloads.config(args.workload)
+    inp = workloads.make(spec)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    dtype = workloads.ACT_DTYPES[spec.act]
+    T, Hk, Hv, dk, dv, K = inp["T"], spec.Hk, spec.Hv, spec.dk, spec.dv, spec.K
+    C = spec.C
+    x, w = inp["x"].to(dev), inp["w"].to(dev)
+    halo = None if inp["halo"] is None else inp["halo"].to(dev)
+    g, beta = inp["g"].to(dev), inp["beta"].to(dev)
+    h0 = None if inp["h0"] is None else inp["h0"].to(dev)
+    cu_glob = torch.tensor(inp["cu_global"], dtype=torch.int32, device=dev)
+    total = int(inp["cu_global"][-1])
+    do = None if inp["do"] is None else inp["do"].to(dev)
+    dht = None if inp["dht"] is None else inp["dht"].to(dev)
+    N = inp["cap"]
+    stream = torch.cuda.current_stream()
+
+    # preallocated outputs and workspaces: the timed region allocates nothing
+    y = torch.empty_like(x)
+    o = torch.empty((T, Hv, dv), dtype=dtype, device=dev)
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(gdn.chunk_workspace_size(T, N, Hk, Hv, dk, dv, dtype), 1),
+                       dtype=torch.uint8, device=dev)
+    if spec.world_size == 1 and spec.n_halo:
+        meta_fixed = gdn.make_meta(dev, n_halo=spec.n_halo)
+    else:
+        meta_fixed = None
+
+    local_buf = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    meta_buf = torch.empty(gdn.META_BYTES, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        local, meta = gdn.gdn_localize_cu_seqlens(cu_glob, total, spec.world_size, spec.rank, K,
+                                                  out=(local_buf, meta_buf))
+        m = meta if spec.world_size > 1 else meta_fixed
+        mark(1)
+        gdn.gdn_conv1d_silu_halo(x, w, local, halo=halo, meta=m, out=y)
+        mark(2)
+        gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht, ws=ws_f)
+        mark(3)
+        if spec.backward:
+            gr = gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht)
+            mark(4)
+            gdn.gdn_conv1d_silu_halo_bwd(x, w, local, gr["dy"], halo=halo, meta=m)
+            mark(5)
+
+    names = ["localize", "conv_fwd", "chunk_fwd"] + (["chunk_bwd", "conv_bwd"] if spec.backward else [])
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_call = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, n in enumerate(names)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+
+    s_bytes = 2 if dtype == torch.bfloat16 else 4
+    flops = chunk_fwd_flops_per_token_head(dk, dv) * T * Hv
+    t_chunk = per_call["chunk_fwd"] * 1e-3
+    achieved = flops / t_chunk
+    peak = MFMA_PEAK[spec.act]
+    conv_b = conv_bytes_per_token(C, s_bytes) * T + C * K * s_bytes
+    t_conv = per_call["conv_fwd"] * 1e-3
+    roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "kernel": "gdn_chunk_fwd (all launches of the call)"}
+    chunk_hbm = chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
+    extra = {
+        "chunk_fwd_hbm": {"achieved": chunk_hbm / t_chunk / 1e9, "peak": HBM_PEAK / 1e9,
+                          "unit": "GB/s", "frac": chunk_hbm / t_chunk / HBM_PEAK},
+        "conv_fwd": {"bound": "hbm", "achieved": conv_b / t_conv / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": conv_b / t_conv / HBM_PEAK},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, inp, args.cpu_sample_tokens)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.act, "data": "synthetic",
+        "config": {"workload": spec.name, "tokens": T, "sequences": len(inp["lengths"]),
+                   "qk_heads": Hk, "v_heads": Hv, "dk": dk, "dv": dv, "conv_k": K,
+                   "passes": "fwd+bwd" if spec.backward else "fwd",
+                   "world_size": spec.world_size, "rank": spec.rank},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_call_ms": per_call,
+        "rooflines_other": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(spec, inp, sample_tokens):
+    """The fp64 oracle (conv + token recurrence forward) on the first
+    `sample_tokens` tokens of the first sequence(s), all heads; tokens/s of
+    the sample."""
+    from oracle import capi
+    T = inp["T"]
+    if sample_tokens <= 0:
+        # ~7*dk*dv fp64 FLOP per token and head; aim for ~15 s at ~1 GFLOP/s/thread
+        thr = capi.max_threads()
+        per_tok = 7.0 * spec.dk * spec.dv * spec.Hv
+        sample_tokens = int(min(T, max(256, 15 * 1e9 * min(thr, spec.Hv) / per_tok)))
+    n = min(sample_tokens, T)
+    x = inp["x"][:n].double().numpy()
+    w = inp["w"].double().numpy()
+    cu = [0, n]
+    Hk, Hv, dk, dv = spec.Hk, spec.Hv, spec.dk, spec.dv
+    threads = min(capi.max_threads(), Hv)
+    t0 = time.perf_counter()
+    yv = capi.conv1d_silu(x, w, None, None, 0, cu)
+    q = yv[:, :Hk * dk].reshape(n, Hk, dk)
+    k = yv[:, Hk * dk:2 * Hk * dk].reshape(n, Hk, dk)
+    v = yv[:, 2 * Hk * dk:].reshape(n, Hv, dv)
+    capi.gdn_fwd(q, k, v, inp["g"][:n].double().numpy(), inp["beta"][:n].double().numpy(), None,
+                 cu, dk ** -0.5, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d tokens of the workload, all %d value heads, conv + gated delta "
+                      "rule forward in fp64 (%.1f s)" % (n, Hv, dt),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * gdn.h -- C ABI of libgdn, one rank's hot path of a context-parallel Gated
+ * DeltaNet token mixer on MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [FLA-CP]  flash-linear-attention "fla/ops/cp/context.py":
+ *             get_cp_cu_seqlens, FLACPContext.
+ *   [HP-CP]   hyper-parallel "linear_attention_context_parallel.py":
+ *             _causal_conv1d_with_cp_halo, _l2norm_torch,
+ *             _prepare_gdn_chunks_for_summary, _run_prepared_gdn_chunks,
+ *             _RecvInitialStateP2PFunction, _SendFinalStateP2PFunction,
+ *             LinearAttentionP2PCPWrapper.forward (the data flow conv ->
+ *             split -> GQA expansion -> gated delta rule).
+ *
+ * General rules for every entry point
+ *   - Pointers are device pointers unless stated otherwise.  The caller owns
+ *     every buffer, workspaces included; the library allocates no device or
+ *     host memory and keeps no state apart from a thread-local error string.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream) and never synchronises the host.  Outputs are
+ *     valid once the stream reaches them.
+ *   - A call returns GDN_OK or a negative gdn_status without launching
+ *     anything when a host-visible argument is invalid; gdn_last_error()
+ *     then describes the problem.  Conditions only the device can see (the
+ *     contents of cu_seqlens) are reported through gdn_cp_meta.status.
+ *   - Activations are `gdn_dtype` (float32 or bfloat16); g, beta, states and
+ *     parameter gradients are float32.  Accumulation is float32.
+ *   - Concurrent calls on different streams are safe when their buffers
+ *     (workspaces included) do not overlap.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,        /* an argument is out of its documented range */
+  GDN_EUNSUPPORTED = -2,  /* a valid shape this build has no kernel for */
+  GDN_EHIP = -3,          /* a HIP launch or runtime call failed */
+  GDN_EWORKSPACE = -4     /* workspace missing or smaller than required */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Device-side status codes written to gdn_cp_meta.status. */
+#define GDN_META_OK 0
+#define GDN_META_NOT_MONOTONE 1     /* cu_seqlens decreases somewhere */
+#define GDN_META_BAD_TOTAL 2        /* cu_seqlens[0] != 0 or cu_seqlens[num_seqs] != total */
+
+/*
+ * Per-rank context-parallel record, [FLA-CP] FLACPContext minus the process
+ * group.  Lives in device memory; written by gdn_localize_cu_seqlens and read
+ * by the conv kernels (n_halo).  Callers that build one by hand (a halo
+ * without a shard split) fill it on the host and copy it over.
+ */
+typedef struct {
+  int64_t rank_start;           /* part_len * rank                                  */
+  int64_t rank_end;             /* rank_start + part_len                            */
+  int64_t pre_num_conv_tokens;  /* max(0, rank_start - start of first local seq)    */
+  int32_t num_local_seqs;       /* local sequences (empty pieces dropped)           */
+  int32_t first_seq_global_idx; /* global index of local sequence 0                 */
+  int32_t is_first_rank;        /* rank owns the first token of local sequence 0    */
+  int32_t is_last_rank;         /* rank owns the last token of the last local seq   */
+  int32_t pre_num_ranks;        /* ranks before this one holding local sequence 0   */
+  int32_t post_num_ranks;       /* ranks after this one holding the last local seq  */
+  int32_t n_halo;               /* min(K-1, pre_num_conv_tokens): usable halo rows  */
+  int32_t status;               /* GDN_META_* (device-side validation)              */
+} gdn_cp_meta;
+
+/*
+ * Localise a packed batch to one token shard.  [FLA-CP] get_cp_cu_seqlens,
+ * steps 2-5: part_len = total_tokens / world_size, shard
+ * [part_len*rank, part_len*(rank+1)); the sequences overlapping it are found
+ * by two sorted searches (ends vs rank_start, side right; starts vs rank_end,
+ * side left), their boundaries clamped to the shard, rebased and de-duplicated
+ * (so empty pieces vanish and local index != global index), then the
+ * first/last-owner metadata are derived.  Integer work in int64, bit-exact.
+ *
+ *   cu_seqlens        int32 [num_seqs+1], non-decreasing, cu[0] = 0,
+ *                     cu[num_seqs] = total_tokens.
+ *   total_tokens      host copy of cu_seqlens[num_seqs] (as the page reads
+ *                     the CPU copy); must be > 0 and divisible by world_size.
+ *   conv_kernel_size  K >= 1 of the conv that follows (for n_halo).
+ *   local_cu_seqlens  out, int32 [num_seqs+1]: entries 0..num_local_seqs hold
+ *                     the local boundaries (0 .. part_len); the remaining
+ *                     entries are filled with part_len, so any consumer may
+ *                     treat the array as num_seqs sequences, the trailing
+ *                     ones empty.
+ *   meta              out, one gdn_cp_meta.
+ * Errors: GDN_EINVAL for num_seqs < 1, world_size < 1, rank outside
+ * [0, world_size), conv_kernel_size < 1, total_tokens <= 0, a remainder
+ * (total % world_size != 0, where the page would leave tokens unowned) or
+ * null pointers.  A cu_seqlens that is not monotone or does not end at
+ * total_tokens sets meta->status (then the other outputs are undefined).
+ */
+int gdn_localize_cu_seqlens(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t world_size, int32_t rank, int32_t conv_kernel_size,
+                            int32_t* local_cu_seqlens, gdn_cp_meta* meta, hipStream_t stream);
+
+/*
+ * Causal depthwise conv1d + SiLU with a carried-in halo.  [HP-CP]
+ * _causal_conv1d_with_cp_halo: per channel c and token t of sequence n
+ * (tokens [cu[n], cu[n+1])):
+ *   z[t,c] = bias[c] + sum_{j<K} w[c,j] * xh[t-(K-1)+j, c],   y = z*sigmoid(z)
+ * (cross-correlation: w[c,K-1] multiplies the current token).  xh is x inside
+ * the token's own sequence; for local sequence 0 the last meta->n_halo rows of
+ * `halo` stand for the tokens just before it (halo row K-2 = the token right
+ * before); every other position is zero.
+ *
+ *   x     [T, C] activations, row-major (channels [Q heads|K heads|V heads]).
+ *   w     [C, K] activations.          bias [C] activations or NULL.
+ *   halo  [K-1, C] activations or NULL (then n_halo is taken as 0).
+ *   cu_seqlens int32 [N+1], cu[0] = 0, cu[N] = T (device).
+ *   meta  device gdn_cp_meta or NULL (n_halo = 0).
+ *   y     [T, C] output; must not overlap x.
+ * Errors: GDN_EINVAL for T < 0, N < 0, C < 1, K outside [1, 8], null
+ * required pointers or an unknown dtype.  T = 0 launches nothing.
+ */
+int gdn_conv1d_silu_halo(const void* x, const void* w, const void* bias, const void* halo,
+                         const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t C, int32_t K,
+                         const gdn_cp_meta* meta, void* y, gdn_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace gdn_conv1d_silu_halo_bwd needs for (T, C, K). */
+size_t gdn_conv_bwd_workspace_size(int64_t T, int32_t C, int32_t K);
+
+/*
+ * Reverse mode of gdn_conv1d_silu_halo.  Given dy = dL/dy [T, C]:
+ *   dx    [T, C] activations (overwritten): dL/dx;
+ *   dw    [C, K] float32 (overwritten): sum over tokens of dz * xh, reduced
+ *         in a fixed order (run-to-run deterministic);
+ *   dbias [C] float32 or NULL;
+ *   dhalo [K-1, C] activations or NULL: gradient of the halo rows, zero for
+ *         the rows beyond n_halo (what the page's differentiable halo
+ *         all-to-all hands back to the previous shard).
+ * Other arguments as in the forward.  ws/ws_bytes: workspace of at least
+ * gdn_conv_bwd_workspace_size(T, C, K) bytes, 256-byte aligned.
+ * Errors: as the forward, plus GDN_EWORKSPACE.
+ */
+int gdn_conv1d_silu_halo_bwd(const void* x, const void* w, const void* bias, const void* halo,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t C, int32_t K,
+                             const gdn_cp_meta* meta, const void* dy, void* dx, float* dw,
+                             float* dbias, void* dhalo, void* ws, size_t ws_bytes, gdn_dtype dt,
+                             hipStream_t stream);
+
+/* Bytes of workspace gdn_chunk_fwd (bwd = 0) or gdn_chunk_bwd (bwd = 1)
+ * needs for these sizes; 0 means none. */
+size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                                int32_t dv, gdn_dtype dt, int bwd);
+
+/*
+ * Chunked gated delta rule, forward.  [HP-CP] _l2norm_torch,
+ * _prepare_gdn_chunks_for_summary, _run_prepared_gdn_chunks, evaluated per
+ * sequence of cu_seqlens (sequences never mix; each is chunked in 64-token
+ * chunks from its own start).  Per value head h, with q/k head
+ * a = h / (Hv/Hk) (the page's repeat_interleave GQA expansion):
+ *   qh = scale * q / sqrt(|q|^2 + 1e-6), kh = k / sqrt(|k|^2 + 1e-6)
+ *        (plain scale*q, k when use_qk_l2norm = 0);
+ *   S <- exp(g_t) S;  S <- S + kh (beta_t (v_t - S^T kh))^T;  o_t = S^T qh
+ * with the state S laid out [dk, dv] as the page's recurrent_state, starting
+ * from h0[n] (zero if h0 is NULL) and ending as ht[n].
+ *
+ *   q, k     element (0, head 0, 0) of [T, Hk, dk] views; tokens are ld_qk
+ *            elements apart, heads dk apart (e.g. the Q and K channel blocks
+ *            of the conv output, ld_qk = C).
+ *   v        [T, Hv, dv] view with token stride ld_v.
+ *   g, beta  float32 [T, Hv] (g is the per-token log decay, before cumsum).
+ *   h0, ht   float32 [N, Hv, dk, dv] or NULL.
+ *   cu_seqlens int32 [N+1] (device), cu[0] = 0, cu[N] = T.
+ *   scale    multiplier of q (the page uses dk^-1/2).
+ *   o        [T, Hv, dv] activations, contiguous.
+ *   ws       workspace of gdn_chunk_workspace_size(..., 0) bytes (256-byte
+ *            aligned) or NULL when that size is 0.
+ * Errors: GDN_EINVAL for negative sizes, Hk < 1, Hv % Hk != 0, ld_qk smaller
+ * than Hk*dk, ld_v smaller than Hv*dv, null required pointers;
+ * GDN_EUNSUPPORTED unless dk, dv in {32, 64, 128} (bfloat16) or in {32, 64}
+ * (float32, whose chunk tiles would not fit in LDS at 128); GDN_EWORKSPACE.
+ */
+int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                  const float* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  int32_t N, int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                  int use_qk_l2norm, void* o, float* ht, void* ws, size_t ws_bytes, gdn_dtype dt,
+                  hipStream_t stream);
+
+/*
+ * Chunked gated delta rule, backward: reverse mode of gdn_chunk_fwd.  The
+ * gradient contract is the page's P2P autograd pair: dht (the final-state
+ * gradient coming back from the next shard) in, dh0 (sent to the previous
+ * shard) out.  Given d_o [T, Hv, dv] activations and dht [N, Hv, dk, dv]
+ * float32 (NULL = zero):
+ *   dq, dk_  gradients w.r.t. the raw q, k (before l2norm and scale), summed
+ *            over the value heads sharing a q/k head; written through views
+ *            with token stride ld_dqk (they may be the Q and K channel blocks
+ *            of one [T, C] conv-output gradient).
+ *   dv_      [T, Hv, dv] view with token stride ld_dv.
+ *   dg, dbeta float32 [T, Hv];  dh0 float32 [N, Hv, dk, dv] or NULL.
+ * Forward arguments as in gdn_chunk_fwd.  ws: gdn_chunk_workspace_size(...,1).
+ * Errors: as gdn_chunk_fwd.
+ */
+int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                  const float* g, const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  int32_t N, int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                  int use_qk_l2norm, const void* d_o, const float* dht, void* dq, void* dk_,
+                  int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta, float* dh0,
+                  void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

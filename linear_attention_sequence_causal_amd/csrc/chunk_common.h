@@ -1,0 +1,314 @@
+// chunk_common.h -- per-chunk machinery of the chunked gated delta rule,
+// shared by the forward and backward kernels.
+//
+// hyper-parallel "linear_attention_context_parallel.py",
+// _prepare_gdn_chunks_for_summary, evaluated for one (chunk, value head) in
+// one workgroup with every intermediate on chip:
+//   qh, kh    l2-normalised q (times scale) and k            (_l2norm_torch)
+//   G         in-chunk cumulative sum of g
+//   L         strict-lower( diag(beta) kh kh^T o exp(G_i - G_j) )
+//   P         lower-incl( qh kh^T o exp(G_i - G_j) )      (the output's attn)
+//   T         (I + L)^-1, unit lower triangular
+//   u         T diag(beta) v                              (chunk_value)
+//   w         T diag(beta exp(G)) kh                      (k_cumdecay)
+// The page forms T by a 63-step row recurrence; here the four 16x16
+// diagonal blocks are inverted by column-parallel forward substitution (one
+// wave, one lane per column) and the off-diagonal blocks follow from
+// T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj on fp32 MFMA, one block distance at
+// a time.  Products with token-sized contraction use bf16 MFMA with fp32
+// accumulation (fp32 MFMA for float32 activations); see gdn_common.h for
+// the fragment convention.
+//
+// LDS layout (one workgroup = one chunk of one head at a time):
+//   q  [64][DK+pad]  kh rows, k [64][DK+pad], kt [DK][64+pad] (kh transposed),
+//   vt [DV][64+pad] (v transposed), w [64][DK+pad], p [64][64+pad] (operand
+//   type), L and Tm [64][68] fp32, G / beta / beta*exp(G) [64] fp32.
+#pragma once
+
+#include "gdn_common.h"
+
+namespace gdn_chunk {
+
+constexpr int BT = 64;  // chunk length
+
+template <typename E> struct OpType { typedef E type; };  // bf16 -> bf16, float -> float
+
+template <typename O, int DK, int DV, bool HAS_Q, bool HAS_BWD = false>
+struct Smem {
+  static constexpr int PAD = 16 / (int)sizeof(O);
+  static constexpr int LDK = DK + PAD;  // row-major [BT][DK]
+  static constexpr int LDT = BT + PAD;  // [D][BT] and [BT][BT] operand arrays
+  static constexpr int LDF = BT + 4;    // fp32 [BT][BT]
+  alignas(16) O q[HAS_Q ? BT * LDK : 8];
+  alignas(16) O k[BT * LDK];
+  alignas(16) O kt[DK * LDT];
+  alignas(16) O vt[DV * LDT];
+  alignas(16) O w[BT * LDK];
+  alignas(16) O p[HAS_Q ? BT * LDT : 8];
+  alignas(16) float L[BT * LDF];
+  alignas(16) float Tm[BT * LDF];
+  alignas(16) float G[BT];
+  alignas(16) float beta[BT];
+  alignas(16) float bg[BT];  // beta * exp(G)
+};
+
+// Global -> register prefetch of one chunk (q, k rows of q/k head `qa`, v
+// rows of value head `h`, g and beta of head h).
+template <typename E, int DK, int DV, int NT, bool HAS_Q>
+struct Prefetch {
+  typedef typename Vec16<E>::type V16;
+  static constexpr int VE = Vec16<E>::N;
+  static constexpr int QPR = DK / VE;  // 16-byte vectors per q/k row
+  static constexpr int VPR = DV / VE;
+  static constexpr int QV = BT * QPR;
+  static constexpr int VV = BT * VPR;
+  static constexpr int PQ = (QV + NT - 1) / NT;
+  static constexpr int PV = (VV + NT - 1) / NT;
+  V16 q[HAS_Q ? PQ : 1];
+  V16 k[PQ];
+  V16 v[PV];
+  float g, beta;
+
+  GDN_DEV void load(const E* __restrict__ qp, const E* __restrict__ kp, int64_t ld_qk,
+                    const E* __restrict__ vp, int64_t ld_v, const float* __restrict__ gp,
+                    const float* __restrict__ bp, int Hv, int64_t tc, int64_t te, int tid) {
+#pragma unroll
+    for (int p = 0; p < PQ; p++) {
+      const int i = tid + NT * p;
+      const int row = i / QPR, vi = i % QPR;
+      const int64_t t = tc + row;
+      const bool ok = (i < QV) && (t < te);
+      if constexpr (HAS_Q)
+        q[p] = ok ? *reinterpret_cast<const V16*>(qp + t * ld_qk + vi * VE) : zero_vec16<E>();
+      k[p] = ok ? *reinterpret_cast<const V16*>(kp + t * ld_qk + vi * VE) : zero_vec16<E>();
+    }
+#pragma unroll
+    for (int p = 0; p < PV; p++) {
+      const int i = tid + NT * p;
+      const int row = i / VPR, vi = i % VPR;
+      const int64_t t = tc + row;
+      const bool ok = (i < VV) && (t < te);
+      v[p] = ok ? *reinterpret_cast<const V16*>(vp + t * ld_v + vi * VE) : zero_vec16<E>();
+    }
+    g = 0.f;
+    beta = 0.f;
+    if (tid < BT && tc + tid < te) {
+      g = gp[(tc + tid) * Hv];
+      beta = bp[(tc + tid) * Hv];
+    }
+  }
+};
+
+// Register prefetch -> LDS: l2norm (and q scale), plain and transposed
+// copies, in-chunk cumsum of g.  Rows past the sequence end are zero, which
+// leaves the state untouched (the page's zero padding).
+template <typename E, typename O, int DK, int DV, int NT, bool HAS_Q, class SM>
+GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale, int use_l2norm,
+                   int tid) {
+  typedef Prefetch<E, DK, DV, NT, HAS_Q> PF;
+  constexpr int VE = PF::VE;
+  constexpr int LDK = SM::LDK, LDT = SM::LDT;
+#pragma unroll
+  for (int p = 0; p < PF::PQ; p++) {
+    const int i = tid + NT * p;
+    const int row = i / PF::QPR, vi = i % PF::QPR;
+    float kf[VE], qf[VE];
+    float kss = 0.f, qss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; e++) {
+      kf[e] = to_f(pf.k[p][e]);
+      kss += kf[e] * kf[e];
+      if constexpr (HAS_Q) {
+        qf[e] = to_f(pf.q[p][e]);
+        qss += qf[e] * qf[e];
+      }
+    }
+    kss = group_sum<PF::QPR>(kss);
+    float kr = use_l2norm ? 1.f / sqrtf(kss + 1e-6f) : 1.f;
+    float qr = scale;
+    if constexpr (HAS_Q) {
+      qss = group_sum<PF::QPR>(qss);
+      if (use_l2norm) qr = scale / sqrtf(qss + 1e-6f);
+    }
+    if (i < PF::QV) {
+#pragma unroll
+      for (int e = 0; e < VE; e++) {
+        const O kv = from_f<O>(kf[e] * kr);
+        sm.k[row * LDK + vi * VE + e] = kv;
+        sm.kt[(vi * VE + e) * LDT + row] = kv;
+        if constexpr (HAS_Q) sm.q[row * LDK + vi * VE + e] = from_f<O>(qf[e] * qr);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF::PV; p++) {
+    const int i = tid + NT * p;
+    const int row = i / PF::VPR, vi = i % PF::VPR;
+    if (i < PF::VV) {
+#pragma unroll
+      for (int e = 0; e < VE; e++) sm.vt[(vi * VE + e) * LDT + row] = from_f<O>(to_f(pf.v[p][e]));
+    }
+  }
+  if (tid < BT) {  // wave 0: inclusive scan of g over the 64 rows
+    float G = pf.g;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(G, off, 64);
+      if (tid >= off) G += o;
+    }
+    sm.G[tid] = G;
+    sm.beta[tid] = pf.beta;
+    sm.bg[tid] = pf.beta * __expf(G);
+  }
+}
+
+// L (fp32) and, with HAS_Q, P (operand type) from kh kh^T and qh kh^T.
+// Only the 10 lower 16x16 tiles are computed; the upper tiles of L, P and
+// Tm are zeroed once per kernel by zero_upper().
+template <typename O, int DK, int NW, bool HAS_Q, class SM>
+GDN_DEV void gram(SM& sm, int wave, int lane) {
+  typedef Mfma<O> M;
+  constexpr int NTILE = HAS_Q ? 20 : 10;
+  for (int tt = wave; tt < NTILE; tt += NW) {
+    const bool isq = tt >= 10;
+    const int idx = isq ? tt - 10 : tt;
+    const int i = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+    const int j = idx - i * (i + 1) / 2;
+    floatx4 acc = zero4();
+    const O* A = isq ? sm.q : sm.k;
+#pragma unroll
+    for (int s = 0; s < DK / M::KSTEP; s++)
+      M::mma(acc, M::load(A, SM::LDK, 16 * i, s * M::KSTEP, lane),
+             M::load(sm.k, SM::LDK, 16 * j, s * M::KSTEP, lane));
+    const int col = 16 * j + (lane & 15);
+    const int rb = 16 * i + 4 * (lane >> 4);
+    const float Gc = sm.G[col];
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int row = rb + jj;
+      const float dec = row >= col ? __expf(sm.G[row] - Gc) : 0.f;
+      if (!isq) {
+        sm.L[row * SM::LDF + col] = row > col ? sm.beta[row] * acc[jj] * dec : 0.f;
+      } else {
+        sm.p[row * SM::LDT + col] = from_f<O>(acc[jj] * dec);
+      }
+    }
+  }
+}
+
+// Zero the strictly-upper 16x16 tiles of L, Tm and P (never written later).
+template <typename O, bool HAS_Q, int NT, class SM>
+GDN_DEV void zero_upper(SM& sm, int tid) {
+  for (int e = tid; e < BT * BT; e += NT) {
+    const int r = e / BT, c = e % BT;
+    if ((c >> 4) > (r >> 4)) {
+      sm.L[r * SM::LDF + c] = 0.f;
+      sm.Tm[r * SM::LDF + c] = 0.f;
+      if constexpr (HAS_Q) sm.p[r * SM::LDT + c] = from_f<O>(0.f);
+    }
+  }
+}
+
+// T = (I + L)^-1 into sm.Tm.  Needs a barrier before (L complete); ends with
+// a barrier.
+template <int NW, class SM>
+GDN_DEV void solve(SM& sm, int wave, int lane) {
+  constexpr int LDF = SM::LDF;
+  if (wave == 0) {
+    // diagonal blocks: lane (b, j) computes column j of (I + L_bb)^-1
+    const int b = lane >> 4, j = lane & 15;
+    const float* Lb = sm.L + (16 * b) * LDF + 16 * b;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      float s = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; m++) s -= Lb[i * LDF + m] * x[m];
+      x[i] = s;
+    }
+    float* Tb = sm.Tm + (16 * b) * LDF + 16 * b;
+#pragma unroll
+    for (int i = 0; i < 16; i++) Tb[i * LDF + j] = x[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks, by distance d = i - j
+  for (int d = 1; d < 4; d++) {
+    for (int blk = wave; blk < 4 - d; blk += NW) {
+      const int j = blk, i = blk + d;
+      floatx4 r = zero4();
+      for (int m = j; m < i; m++) {
+        // A = L_im (rows 16i, cols 16m), B = T_mj read as B[k][n] = Tm[16m+k][16j+n]
+        const floatx4 a = Mfma<float>::load(sm.L, LDF, 16 * i, 16 * m, lane);
+        const int kb = 16 * m + 4 * (lane >> 4), n = 16 * j + (lane & 15);
+        floatx4 bfr;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) bfr[jj] = sm.Tm[(kb + jj) * LDF + n];
+        Mfma<float>::mma(r, a, bfr);
+      }
+      // T_ij = -T_ii r  (r is already in B layout: its rows are k)
+      floatx4 o = zero4();
+      Mfma<float>::mma(o, Mfma<float>::load(sm.Tm, LDF, 16 * i, 16 * i, lane), r);
+      const int rb = 16 * i + 4 * (lane >> 4), c = 16 * j + (lane & 15);
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) sm.Tm[(rb + jj) * LDF + c] = -o[jj];
+    }
+    __syncthreads();
+  }
+}
+
+// u tiles for 32 value columns [vc0, vc0+32) into registers (C layout,
+// u[mt][nt]: token rows 16mt.., value cols vc0+16nt..).
+template <typename O, class SM>
+GDN_DEV void compute_u(const SM& sm, int vc0, int lane, floatx4 (&u)[4][2]) {
+  typedef Mfma<O> M;
+  constexpr int NS = BT / M::KSTEP;
+  typename M::frag a[4][NS];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int s = 0; s < NS; s++) a[mt][s] = M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.beta, lane);
+#pragma unroll
+  for (int nt = 0; nt < 2; nt++) {
+    typename M::frag b[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) b[s] = M::load(sm.vt, SM::LDT, vc0 + 16 * nt, s * M::KSTEP, lane);
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; s++) M::mma(acc, a[mt][s], b[s]);
+      u[mt][nt] = acc;
+    }
+  }
+}
+
+// w = T diag(beta exp(G)) kh into sm.w (operand type), tiles spread over waves.
+template <typename O, int DK, int NW, class SM>
+GDN_DEV void compute_w(SM& sm, int wave, int lane) {
+  typedef Mfma<O> M;
+  constexpr int NS = BT / M::KSTEP;
+  constexpr int NTILE = 4 * (DK / 16);
+  for (int tt = wave; tt < NTILE; tt += NW) {
+    const int mt = tt % 4, nt = tt / 4;
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+      M::mma(acc, M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.bg, lane),
+             M::load(sm.kt, SM::LDT, 16 * nt, s * M::KSTEP, lane));
+    const int rb = 16 * mt + 4 * (lane >> 4), c = 16 * nt + (lane & 15);
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) sm.w[(rb + jj) * SM::LDK + c] = from_f<O>(acc[jj]);
+  }
+}
+
+// B fragment for contraction step s from accumulator tiles X[kt][nt] whose
+// rows are the contraction index.
+template <typename O, int NKT, int NN>
+GDN_DEV typename Mfma<O>::frag acc_as_b(const floatx4 (&X)[NKT][NN], int s, int nt) {
+  if constexpr (Mfma<O>::KSTEP == 32)
+    return Mfma<O>::from_acc(X[2 * s][nt], X[2 * s + 1][nt]);
+  else
+    return Mfma<O>::from_acc(X[s][nt]);
+}
+
+}  // namespace gdn_chunk

@@ -1,0 +1,154 @@
+// gdn_common.h -- device helpers shared by the libgdn HIP sources (gfx950).
+//
+// MFMA fragment convention used by every contraction in this library
+// ---------------------------------------------------------------------
+// A 16x16 output tile C lives in one wave as floatx4 per lane: lane l holds
+// C[4*(l/16) + j][l%16] for j = 0..3 (the MFMA accumulator layout).
+// The contraction dimension is walked in "k-tiles" of 16.  Inside a k-tile,
+// lane group g = l/16 supplies the four k indices 4g..4g+3.  This is the
+// same order in which a C tile stores its rows, so an accumulator tile can
+// be fed back as the B operand of the next product (K = its row index)
+// without moving data between lanes -- the running state S [dk, dv] and the
+// corrected values v_new stay in registers between the products of a chunk.
+//
+//  * bf16 (v_mfma_f32_16x16x32_bf16, K = 32 = two k-tiles): a fragment is 8
+//    bf16, elements 0..3 from k-tile 2s, 4..7 from k-tile 2s+1.
+//  * fp32 (v_mfma_f32_16x16x4_f32, K = 4): a fragment is one k-tile (4
+//    floats); the four MFMAs of a k-tile take element j each.
+// A and B supply the same k for the same (lane group, element), so the
+// products are exact contractions regardless of the hardware's K order.
+// Operands read from LDS are stored [row][k] with k contiguous: A as
+// [M][K], B as [N][K] (i.e. B transposed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define GDN_DEV __device__ __forceinline__
+
+GDN_DEV float to_f(float x) { return x; }
+GDN_DEV float to_f(bf16 x) { return (float)x; }
+
+template <typename T> GDN_DEV T from_f(float x);
+template <> GDN_DEV float from_f<float>(float x) { return x; }
+template <> GDN_DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// 16-byte vector of activations.
+template <typename E> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  typedef floatx4 type;
+};
+template <> struct Vec16<bf16> {
+  static constexpr int N = 8;
+  typedef bf16x8 type;
+};
+
+template <typename E> GDN_DEV typename Vec16<E>::type zero_vec16() {
+  typename Vec16<E>::type z;
+#pragma unroll
+  for (int i = 0; i < Vec16<E>::N; i++) z[i] = from_f<E>(0.f);
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA policy: operand type O of the contractions.
+// ---------------------------------------------------------------------------
+template <typename O> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KSTEP = 32;  // k per fragment
+  typedef bf16x8 frag;
+
+  // rows row0 + l%16 of a [rows][ld] array, k indices k0 + (conv. order)
+  GDN_DEV static frag load(const bf16* base, int ld, int row0, int k0, int lane) {
+    const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+    frag f;
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    return f;
+  }
+  // same from an fp32 [rows][ld] array, element k scaled by sc[k]
+  GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
+                                  int lane) {
+    const int kk = k0 + 4 * (lane >> 4);
+    const float* p = base + (row0 + (lane & 15)) * ld + kk;
+    floatx4 lo = *reinterpret_cast<const floatx4*>(p);
+    floatx4 hi = *reinterpret_cast<const floatx4*>(p + 16);
+    floatx4 slo = *reinterpret_cast<const floatx4*>(sc + kk);
+    floatx4 shi = *reinterpret_cast<const floatx4*>(sc + kk + 16);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = (bf16)(lo[j] * slo[j]);
+      f[4 + j] = (bf16)(hi[j] * shi[j]);
+    }
+    return f;
+  }
+  // B fragment from accumulator tiles of k-tiles 2s and 2s+1
+  GDN_DEV static frag from_acc(const floatx4& c0, const floatx4& c1) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = (bf16)c0[j];
+      f[4 + j] = (bf16)c1[j];
+    }
+    return f;
+  }
+  GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 16;
+  typedef floatx4 frag;
+
+  GDN_DEV static frag load(const float* base, int ld, int row0, int k0, int lane) {
+    return *reinterpret_cast<const floatx4*>(base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+  }
+  GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
+                                  int lane) {
+    const int kk = k0 + 4 * (lane >> 4);
+    floatx4 a = *reinterpret_cast<const floatx4*>(base + (row0 + (lane & 15)) * ld + kk);
+    floatx4 s = *reinterpret_cast<const floatx4*>(sc + kk);
+    return a * s;
+  }
+  GDN_DEV static frag from_acc(const floatx4& c0) { return c0; }
+  GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+  }
+};
+
+// B fragment for k-step s taken from accumulator tiles indexed by k-tile
+// (tiles[kt] is the C tile whose rows are k-tile kt).
+template <typename O> struct AccToB;
+template <> struct AccToB<bf16> {
+  template <typename F>
+  GDN_DEV static Mfma<bf16>::frag get(F tile, int s) { return Mfma<bf16>::from_acc(tile(2 * s), tile(2 * s + 1)); }
+};
+template <> struct AccToB<float> {
+  template <typename F>
+  GDN_DEV static Mfma<float>::frag get(F tile, int s) { return Mfma<float>::from_acc(tile(s)); }
+};
+
+GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// Wave-level butterfly sum over groups of `width` consecutive lanes.
+template <int WIDTH> GDN_DEV float group_sum(float v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+GDN_DEV float fast_sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }

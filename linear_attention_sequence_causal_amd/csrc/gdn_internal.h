@@ -1,0 +1,30 @@
+// gdn_internal.h -- host-side helpers shared by the libgdn sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Records a formatted message as the thread's last error and returns code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+inline int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GDN_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace gdn

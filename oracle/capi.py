@@ -32,7 +32,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle shared library; returns its path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared",
+        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
                "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)

@@ -1,0 +1,122 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point declared in include/gdn.h, and rejects invalid host-visible arguments
+with the documented status codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_sequence_causal_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built; run `python -m linear_attention_sequence_causal_amd.build`")
+    return gdn.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("gdn_localize_cu_seqlens", "gdn_conv1d_silu_halo", "gdn_conv1d_silu_halo_bwd",
+              "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_chunk_workspace_size",
+              "gdn_conv_bwd_workspace_size", "gdn_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(gdn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(gdn.ENTRY_POINTS)
+
+
+def test_meta_struct_size():
+    # 3 int64 + 8 int32, no padding
+    assert gdn.META_BYTES == 56
+
+
+P = None
+
+
+def test_localize_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(0x1000)
+    bad = [
+        (fake, 0, 16, 1, 0, 4),     # num_seqs < 1
+        (fake, 2, 16, 0, 0, 4),     # world_size < 1
+        (fake, 2, 16, 2, 2, 4),     # rank out of range
+        (fake, 2, 16, 2, -1, 4),
+        (fake, 2, 16, 2, 0, 0),     # K < 1
+        (fake, 2, 0, 1, 0, 4),      # no tokens
+        (fake, 2, 17, 2, 0, 4),     # remainder
+    ]
+    for args in bad:
+        rc = lib.gdn_localize_cu_seqlens(*args, fake, fake, None)
+        assert rc == gdn.GDN_EINVAL, args
+        assert lib.gdn_last_error().decode()
+    assert lib.gdn_localize_cu_seqlens(None, 2, 16, 2, 0, 4, fake, fake, None) == gdn.GDN_EINVAL
+
+
+def test_conv_rejects_bad_arguments(lib):
+    f = ctypes.c_void_p(0x1000)
+    # K out of range, C < 1, negative T, null x with T > 0, unknown dtype
+    assert lib.gdn_conv1d_silu_halo(f, f, None, None, f, 1, 10, 8, 9, None, f, 1, None) == gdn.GDN_EINVAL
+    assert lib.gdn_conv1d_silu_halo(f, f, None, None, f, 1, 10, 0, 4, None, f, 1, None) == gdn.GDN_EINVAL
+    assert lib.gdn_conv1d_silu_halo(f, f, None, None, f, 1, -1, 8, 4, None, f, 1, None) == gdn.GDN_EINVAL
+    assert lib.gdn_conv1d_silu_halo(None, f, None, None, f, 1, 10, 8, 4, None, f, 1, None) == gdn.GDN_EINVAL
+    assert lib.gdn_conv1d_silu_halo(f, f, None, None, f, 1, 10, 8, 4, None, f, 7, None) == gdn.GDN_EINVAL
+    # T = 0 is a no-op
+    assert lib.gdn_conv1d_silu_halo(None, None, None, None, None, 0, 0, 8, 4, None, None, 1, None) == gdn.GDN_OK
+    # backward: workspace too small
+    need = lib.gdn_conv_bwd_workspace_size(100, 64, 4)
+    assert need > 0
+    rc = lib.gdn_conv1d_silu_halo_bwd(f, f, None, None, f, 1, 100, 64, 4, None, f, f, f, None, None,
+                                      f, need - 1, 1, None)
+    assert rc == gdn.GDN_EWORKSPACE
+
+
+def _chunk(lib, **kw):
+    f = ctypes.c_void_p(0x1000)
+    a = dict(q=f, k=f, ld_qk=6144, v=f, ld_v=6144, g=f, beta=f, h0=None, cu=f, N=1, T=64, Hk=16,
+             Hv=16, dk=128, dv=128, scale=0.1, l2=1, o=f, ht=None, ws=f, ws_bytes=1 << 40, dt=1)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["ld_qk"], a["v"], a["ld_v"], a["g"], a["beta"],
+                             a["h0"], a["cu"], a["N"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                             a["scale"], a["l2"], a["o"], a["ht"], a["ws"], a["ws_bytes"], a["dt"],
+                             None)
+
+
+def test_chunk_rejects_bad_arguments(lib):
+    assert _chunk(lib, Hv=24, Hk=16) == gdn.GDN_EINVAL          # Hv % Hk
+    assert _chunk(lib, Hk=0) == gdn.GDN_EINVAL
+    assert _chunk(lib, dk=48) == gdn.GDN_EUNSUPPORTED
+    assert _chunk(lib, dv=256) == gdn.GDN_EUNSUPPORTED
+    assert _chunk(lib, dt=0) == gdn.GDN_EUNSUPPORTED             # fp32 at d = 128
+    assert _chunk(lib, ld_qk=100) == gdn.GDN_EINVAL              # stride below the head block
+    assert _chunk(lib, ld_qk=2049 + 2048, ld_v=6144) == gdn.GDN_EINVAL  # not 16-byte multiple
+    assert _chunk(lib, q=None) == gdn.GDN_EINVAL
+    assert _chunk(lib, q=ctypes.c_void_p(0x1002)) == gdn.GDN_EINVAL     # misaligned
+    assert _chunk(lib, T=-1) == gdn.GDN_EINVAL
+    assert _chunk(lib, ws=None, ws_bytes=0) == gdn.GDN_EWORKSPACE
+    assert _chunk(lib, ws=ctypes.c_void_p(0x1010)) == gdn.GDN_EWORKSPACE  # not 256-aligned
+    assert _chunk(lib, ws_bytes=16) == gdn.GDN_EWORKSPACE
+    assert b"workspace" in lib.gdn_last_error()
+
+
+def test_workspace_sizes_are_host_only(lib):
+    # sizes are pure host arithmetic; segment summaries appear for long sequences
+    small = lib.gdn_chunk_workspace_size(256, 1, 2, 2, 32, 32, 0, 0)
+    big = lib.gdn_chunk_workspace_size(131072, 1, 16, 32, 128, 128, 1, 0)
+    assert 0 < small < big
+    assert lib.gdn_conv_bwd_workspace_size(0, 64, 4) == 0

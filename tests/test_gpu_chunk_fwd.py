@@ -1,0 +1,154 @@
+"""GPU chunked gated delta rule forward (gdn_chunk_fwd) against the oracle.
+
+Small cases: several chunks and ragged tails (lengths 1, 63, 64, 65, ...),
+empty sequences, GQA head sharing, random initial states, l2norm on/off,
+float32 and bfloat16, and forced segmentation (the affine-summary path with
+1-3 chunks per segment).  Workloads: each benchmark configuration at full
+size, the long one compared on a sample of value heads."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_sequence_causal_amd import gdn, workloads
+from tests.helpers import TOL, assert_close, cu_tensor, f64, oracle_chunk_fwd, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, lengths, Hk, Hv, dk, dv, dtype, h0=True):
+    gen = torch.Generator().manual_seed(seed)
+    T = sum(lengths)
+    C = 2 * Hk * dk + Hv * dv
+    # y plays the conv output: SiLU of normals, like the real path
+    y = torch.nn.functional.silu(torch.randn(T, C, generator=gen)).to(dtype)
+    beta = torch.sigmoid(torch.randn(T, Hv, generator=gen))
+    g = -torch.nn.functional.softplus(torch.randn(T, Hv, generator=gen))
+    h = torch.randn(len(lengths), Hv, dk, dv, generator=gen) * 0.05 if h0 else None
+    cu = [0] + list(np.cumsum(lengths))
+    return y, g, beta, h, cu
+
+
+def _run_and_check(y, g, beta, h0, cu, Hk, Hv, dk, dv, use_l2norm=True, seg=None):
+    dtype = y.dtype
+    if seg is not None:
+        os.environ["GDN_SEG_CHUNKS"] = str(seg)
+    try:
+        o, ht = gdn.gdn_chunk_fwd(y.cuda(), g.cuda(), beta.cuda(), cu_tensor(cu), Hk, Hv, dk, dv,
+                                  h0=None if h0 is None else h0.cuda(), use_qk_l2norm=use_l2norm)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("GDN_SEG_CHUNKS", None)
+    ro, rht = oracle_chunk_fwd(y, g, beta, h0, cu, Hk, Hv, dk, dv, dk ** -0.5,
+                               use_l2norm=use_l2norm)
+    assert_close("o", f64(o), ro, dtype)
+    assert_close("ht", f64(ht), rht, dtype)
+    return o, ht
+
+
+SMALL = [
+    # lengths, Hk, Hv, dk, dv, dtype
+    ([256], 2, 2, 32, 32, torch.float32),
+    ([1, 63, 64, 65, 0, 130], 1, 2, 32, 32, torch.float32),
+    ([200, 0, 77], 2, 2, 64, 64, torch.float32),
+    ([300], 2, 4, 128, 128, torch.bfloat16),
+    ([1, 63, 64, 65, 0, 129, 250], 2, 2, 128, 128, torch.bfloat16),
+    ([100, 333], 1, 2, 64, 128, torch.bfloat16),
+    ([190], 2, 2, 128, 64, torch.bfloat16),
+    ([70, 90], 4, 4, 32, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_small(ci):
+    lengths, Hk, Hv, dk, dv, dtype = SMALL[ci]
+    print("case", SMALL[ci], flush=True)
+    y, g, beta, h0, cu = _inputs(ci, lengths, Hk, Hv, dk, dv, dtype)
+    _run_and_check(y, g, beta, h0, cu, Hk, Hv, dk, dv)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_segmented(seg, dtype):
+    """Sequences cut into segments of `seg` chunks: summaries [M|E], the
+    scan over them and the per-segment outputs must equal the unsplit run."""
+    d = 32 if dtype == torch.float32 else 128
+    lengths = [1, 64, 130, 0, 400]
+    y, g, beta, h0, cu = _inputs(40 + seg, lengths, 2, 4, d, d, dtype)
+    g = g * 0.05  # slow decay: the carried state matters across segments
+    o1, h1 = _run_and_check(y, g, beta, h0, cu, 2, 4, d, d, seg=seg)
+    o2, h2 = _run_and_check(y, g, beta, h0, cu, 2, 4, d, d, seg=100000)
+    assert rel_err(f64(o1), f64(o2)) <= TOL[dtype]
+
+
+def test_no_l2norm_and_zero_state():
+    y, g, beta, _, cu = _inputs(9, [150, 40], 2, 2, 64, 64, torch.float32, h0=False)
+    y = y * 0.1  # unnormalised keys: keep |k| small so the recurrence stays contractive
+    _run_and_check(y, g, beta, None, cu, 2, 2, 64, 64, use_l2norm=False)
+
+
+def test_empty_sequences_return_initial_state():
+    y, g, beta, h0, cu = _inputs(11, [0, 5, 0], 1, 1, 32, 32, torch.float32)
+    o, ht = gdn.gdn_chunk_fwd(y.cuda(), g.cuda(), beta.cuda(), cu_tensor(cu), 1, 1, 32, 32,
+                              h0=h0.cuda())
+    assert torch.equal(ht[0].cpu(), h0[0]) and torch.equal(ht[2].cpu(), h0[2])
+    # T = 0
+    y0 = torch.empty(0, 128, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(y0, torch.empty(0, 1, device="cuda"), torch.empty(0, 1, device="cuda"),
+                              cu_tensor([0, 0]), 1, 1, 32, 32, h0=h0[:1].cuda())
+    assert o.shape == (0, 1, 32) and torch.equal(ht.cpu(), h0[:1])
+
+
+def _workload_inputs(spec):
+    inp = workloads.make(spec)
+    dtype = workloads.ACT_DTYPES[spec.act]
+    if spec.world_size > 1:
+        cu_glob = torch.tensor(inp["cu_global"], dtype=torch.int32, device="cuda")
+        cu, meta = gdn.gdn_localize_cu_seqlens(cu_glob, int(inp["cu_global"][-1]), spec.world_size,
+                                               spec.rank, spec.K)
+        m = gdn.read_meta(meta)
+        n_halo = m["n_halo"]
+    else:
+        cu = cu_tensor(inp["cu_global"])
+        n_halo = spec.n_halo if inp["halo"] is not None else 0
+        meta = gdn.make_meta("cuda", n_halo=n_halo) if n_halo else None
+    return inp, dtype, cu, meta, n_halo
+
+
+@pytest.mark.parametrize("name", ["single_t256_h2_d32_f32", "varlen8_h16_d128_bf16",
+                                  "shard3of8_32k_h16_d128_bf16", "fwdbwd_4x4096_h16_d128_bf16",
+                                  "long131k_hk16_hv32_d128_bf16"])
+def test_workload_forward(name):
+    """conv + chunk forward on the workload; per-stage check (the oracle's
+    chunk step fed the GPU conv output) and, where the oracle is cheap, the
+    end-to-end check from x in fp64 throughout."""
+    from oracle import capi
+    spec = workloads.config(name)
+    inp, dtype, cu, meta, n_halo = _workload_inputs(spec)
+    Hk, Hv, dk, dv = spec.Hk, spec.Hv, spec.dk, spec.dv
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    halo = None if inp["halo"] is None else inp["halo"].cuda()
+    y = gdn.gdn_conv1d_silu_halo(x, w, cu, halo=halo, meta=meta)
+    h0 = None if inp["h0"] is None else inp["h0"].cuda()
+    o, ht = gdn.gdn_chunk_fwd(y, inp["g"].cuda(), inp["beta"].cuda(), cu, Hk, Hv, dk, dv, h0=h0)
+    torch.cuda.synchronize()
+    cu_host = cu.cpu().numpy()
+    heads = None if inp["T"] * Hv <= 600000 else [0, 1, Hv - 1]
+    print("  T=%d heads=%s" % (inp["T"], heads), flush=True)
+    ro, rht = oracle_chunk_fwd(y.cpu(), inp["g"], inp["beta"], inp["h0"], cu_host, Hk, Hv, dk, dv,
+                               dk ** -0.5, heads=heads)
+    osel = o if heads is None else o[:, heads]
+    hsel = ht if heads is None else ht[:, heads]
+    assert_close("o", f64(osel), ro, dtype)
+    assert_close("ht", f64(hsel), rht, dtype)
+    if heads is None:
+        # end to end from x: oracle conv + chunk in fp64
+        yr = capi.conv1d_silu(f64(inp["x"]), f64(inp["w"]), None, f64(inp["halo"]), n_halo, cu_host)
+        q, k, v = (a for a in (yr[:, :Hk * dk].reshape(-1, Hk, dk),
+                               yr[:, Hk * dk:2 * Hk * dk].reshape(-1, Hk, dk),
+                               yr[:, 2 * Hk * dk:].reshape(-1, Hv, dv)))
+        eo, eht = capi.gdn_fwd(q, k, v, f64(inp["g"]), f64(inp["beta"]), f64(inp["h0"]), cu_host,
+                               dk ** -0.5)
+        assert_close("o(e2e)", f64(o), eo, dtype)
+        assert_close("ht(e2e)", f64(ht), eht, dtype)

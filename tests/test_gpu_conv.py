@@ -1,0 +1,126 @@
+"""GPU conv1d + SiLU with halo (forward and reverse mode) against the oracle.
+
+Small cases cover K in {1, 2, 4, 5}, packed batches with empty sequences,
+a halo with 1..K-1 valid rows, bias, float32 and bfloat16, and channel
+counts that do not fill a 16-byte vector (the scalar path).  The workload
+shapes run at full size."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_sequence_causal_amd import gdn, workloads
+from oracle import capi
+from tests.helpers import assert_close, cu_tensor, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, cu, C, K, dtype, bias=True, halo_rows=0):
+    g = torch.Generator().manual_seed(seed)
+    T = cu[-1]
+    x = torch.randn(T, C, generator=g).to(dtype)
+    w = (torch.randn(C, K, generator=g) / K ** 0.5).to(dtype)
+    b = torch.randn(C, generator=g).to(dtype) if bias else None
+    halo = torch.randn(K - 1, C, generator=g).to(dtype) if (K > 1 and halo_rows) else None
+    dy = torch.randn(T, C, generator=g).to(dtype)
+    return x, w, b, halo, dy
+
+
+CASES = [
+    # (cu, C, K, halo_rows)
+    ([0, 100], 64, 4, 0),
+    ([0, 0, 37, 37, 40, 300], 128, 4, 3),
+    ([0, 1, 2, 70], 48, 4, 2),
+    ([0, 513], 8, 1, 0),
+    ([0, 17, 90], 24, 2, 1),
+    ([0, 33, 200], 40, 5, 4),
+    ([0, 64, 65, 129], 20, 4, 3),     # C % 8 != 0: scalar path
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_conv_small(ci, dtype):
+    cu, C, K, hr = CASES[ci]
+    x, w, b, halo, dy = _case(ci, cu, C, K, dtype, bias=ci % 2 == 0, halo_rows=hr)
+    meta = gdn.make_meta("cuda", n_halo=hr) if hr else None
+    d = lambda t: None if t is None else t.cuda()
+    y = gdn.gdn_conv1d_silu_halo(d(x), d(w), cu_tensor(cu), bias=d(b), halo=d(halo), meta=meta)
+    ref = capi.conv1d_silu(f64(x), f64(w), f64(b), f64(halo), hr, cu)
+    assert_close("y", f64(y), ref, dtype)
+    dx, dw, db, dh = gdn.gdn_conv1d_silu_halo_bwd(d(x), d(w), cu_tensor(cu), d(dy), bias=d(b),
+                                                  halo=d(halo), meta=meta)
+    rdx, rdw, rdb, rdh = capi.conv1d_silu_bwd(f64(x), f64(w), f64(b), f64(halo), hr, cu, f64(dy))
+    assert_close("dx", f64(dx), rdx, dtype)
+    assert_close("dw", f64(dw), rdw, torch.float32 if dtype == torch.float32 else dtype)
+    if b is not None:
+        assert_close("dbias", f64(db), rdb, dtype)
+    if halo is not None:
+        assert_close("dhalo", f64(dh), rdh, dtype)
+        assert torch.all(dh[:K - 1 - hr].float() == 0)
+
+
+def test_conv_bwd_deterministic():
+    cu = [0, 300, 1000]
+    x, w, b, halo, dy = _case(5, cu, 256, 4, torch.bfloat16)
+    args = [t.cuda() for t in (x, w)]
+    r1 = gdn.gdn_conv1d_silu_halo_bwd(*args, cu_tensor(cu), dy.cuda())
+    r2 = gdn.gdn_conv1d_silu_halo_bwd(*args, cu_tensor(cu), dy.cuda())
+    assert torch.equal(r1[1], r2[1]) and torch.equal(r1[0], r2[0])
+
+
+def test_conv_empty_batch():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    w = torch.randn(64, 4, device="cuda").to(torch.bfloat16)
+    cu = cu_tensor([0, 0])
+    y = gdn.gdn_conv1d_silu_halo(x, w, cu)
+    assert y.shape == (0, 64)
+    halo = torch.randn(3, 64, device="cuda").to(torch.bfloat16)
+    dx, dw, _, dh = gdn.gdn_conv1d_silu_halo_bwd(x, w, cu, x, halo=halo,
+                                                 meta=gdn.make_meta("cuda", n_halo=3))
+    assert torch.all(dw == 0) and torch.all(dh.float() == 0)
+
+
+@pytest.mark.parametrize("name", ["varlen8_h16_d128_bf16", "shard3of8_32k_h16_d128_bf16",
+                                  "long131k_hk16_hv32_d128_bf16", "fwdbwd_4x4096_h16_d128_bf16",
+                                  "single_t256_h2_d32_f32"])
+def test_conv_workloads(name):
+    """Workload shapes at full size; the oracle runs on a sample of channels
+    for the long workload (every channel is independent)."""
+    spec = workloads.config(name)
+    inp = workloads.make(spec)
+    dtype = workloads.ACT_DTYPES[spec.act]
+    T = inp["T"]
+    if spec.world_size > 1:
+        cu_glob = torch.tensor(inp["cu_global"], dtype=torch.int32, device="cuda")
+        cu, meta = gdn.gdn_localize_cu_seqlens(cu_glob, int(inp["cu_global"][-1]), spec.world_size,
+                                               spec.rank, spec.K)
+        m = gdn.read_meta(meta)
+        cu_host = cu.cpu().numpy()[:m["num_local_seqs"] + 1]
+        n_halo = m["n_halo"]
+    else:
+        cu_host = inp["cu_global"]
+        cu = cu_tensor(cu_host)
+        n_halo = spec.n_halo if inp["halo"] is not None else 0
+        meta = gdn.make_meta("cuda", n_halo=n_halo) if n_halo else None
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    halo = None if inp["halo"] is None else inp["halo"].cuda()
+    y = gdn.gdn_conv1d_silu_halo(x, w, cu, halo=halo, meta=meta)
+    torch.cuda.synchronize()
+    C = spec.C
+    cols = np.arange(C) if T * C <= 64 * 2**20 else np.random.default_rng(0).choice(C, 96, replace=False)
+    xs = inp["x"][:, cols]
+    ref = capi.conv1d_silu(f64(xs), f64(inp["w"][cols]), None,
+                           None if inp["halo"] is None else f64(inp["halo"][:, cols]), n_halo,
+                           cu_host)
+    assert_close("y", f64(y[:, cols]), ref, dtype)
+    if spec.backward:
+        dy = torch.randn(T, C, generator=torch.Generator().manual_seed(1)).to(dtype)
+        dx, dw, _, dh = gdn.gdn_conv1d_silu_halo_bwd(x, w, cu, dy.cuda(), halo=halo, meta=meta)
+        rdx, rdw, _, rdh = capi.conv1d_silu_bwd(f64(xs), f64(inp["w"][cols]), None,
+                                                None if inp["halo"] is None else f64(inp["halo"][:, cols]),
+                                                n_halo, cu_host, f64(dy[:, cols]))
+        assert_close("dx", f64(dx[:, cols]), rdx, dtype)
+        assert_close("dw", f64(dw[cols]), rdw, dtype)
+        if dh is not None:
+            assert_close("dhalo", f64(dh[:, cols]), rdh, dtype)
