@@ -1,24 +1,753 @@
-// chunk_bwd.hip -- chunked gated delta rule, backward (reverse mode of
-// gdn_chunk_fwd).
+// chunk_bwd.hip -- gdn_chunk_bwd: reverse mode of the chunked gated delta
+// rule (gdn_chunk_fwd), l2norm and GQA head sharing included.
+//
+// Gradient contract: hyper-parallel "linear_attention_context_parallel.py",
+// _RecvInitialStateP2PFunction / _SendFinalStateP2PFunction -- the gradient
+// of the final state (dht) comes in, the gradient of the initial state (dh0)
+// goes out.  The math is the adjoint of the chunk algorithm of
+// _prepare_gdn_chunks_for_summary / _run_prepared_gdn_chunks.  Per chunk,
+// with S the state entering it, S' the state leaving it, gamma = e^G,
+// D = e^{G_C - G}, Vn = u - w S (v_new) and dS' = dL/dS':
+//   dVn  = P^T dO + D o (K dS')
+//   dS   = gamma_C dS' + Q^T (gamma o dO) - W^T dVn          (carried back)
+//   Y    = T^T dVn                   (gradient of u = T beta v, through T)
+//   dv   = beta o Y
+//   dQ   = gamma o (dO S^T) + dA K,        dA = (dO Vn^T) o Gamma, i >= j
+//   dK   = dA^T Q + D o (Vn dS'^T) - beta gamma o (Y S^T) + (M1 + M1^T) K
+//   M1   = diag(beta) (dL o Gamma) with dL = -Y Vn^T, strict lower
+// The last two use the identities  T^T dW = -Y S^T  (dW = -dVn S^T) and
+//   dL = -(Y u^T + T^T dW w^T) = -Y (u - w S)^T = -Y Vn^T,
+// so the w-path needs no extra [64, dk] intermediates.  dbeta and dG are row
+// sums of the same products; dg is the reverse in-chunk cumsum of dG.
+//
+// Kernels:
+//   1. the forward pipeline in "states" mode stores the state entering every
+//      chunk (fp32), with the segment summaries for parallelism;
+//   2. dstate: per (sequence, head), chunks in reverse, carries dS and stores
+//      dS' of every chunk (fp32); writes dh0;
+//   3. grad: per (chunk, head), all local gradients from S and dS' (fully
+//      parallel); dq-hat, dk-hat per value head go to an fp32 buffer;
+//   4. finalize: per (token, q/k head), sum over the value heads sharing it and
+//      back through l2norm and scale into the dq, dk views.
 #include <hip/hip_runtime.h>
 
-#include "chunk_common.h"
+#include "chunk_loop.h"
 #include "gdn_internal.h"
 
-size_t gdn_chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv);
+using namespace gdn_chunk;
 
 namespace gdn {
 int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, const void* v,
                    int64_t ld_v, const float* g, const float* beta, const int32_t* cu, int32_t N,
                    int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
+size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv);
+}  // namespace gdn
+
+namespace {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  int64_t ld_qk;
+  const void* v;
+  int64_t ld_v;
+  const float* g;
+  const float* beta;
+  int Hk, Hv;
+  float scale;
+  int use_l2norm;
+  const void* d_o;
+  const float* dht;
+  void* dq;
+  void* dk;
+  int64_t ld_dqk;
+  void* dv;
+  int64_t ld_dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  const int32_t* cu;
+  int64_t T;
+  const int32_t* counts;
+  const int4* chunk_tab;
+  const int32_t* seq_chunk_off;
+  const float* states;  // [chunk_cap][Hv][DK][DV]
+  float* dstates;       // [chunk_cap][Hv][DK][DV]
+  float* dqk;           // [T][Hv][2][DK]
+};
+
+template <typename E, int DK, int DV>
+struct BwdCfg {
+  typedef E O;
+  static constexpr int NW = DV / 32;
+  static constexpr int NT = NW * 64;
+  typedef Smem<O, DK, DV, true> SM;
+  typedef Prefetch<E, DK, DV, NT, true> PF;
+};
+
+// ---------------------------------------------------------------------------
+// 2. dS pass: reverse over the chunks of one sequence
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs a) {
+  typedef BwdCfg<E, DK, DV> CF;
+  typedef typename CF::O O;
+  typedef Mfma<O> M;
+  typedef typename CF::SM SM;
+  constexpr int NW = CF::NW, NT = CF::NT, KS = M::KSTEP;
+  constexpr int NSK = DK / KS, NSB = BT / KS, DKT = DK / 16;
+  __shared__ SM sm;  // sm.v holds the chunk of dO
+
+  const int n = blockIdx.x, h = blockIdx.y;
+  const int Hv = a.Hv, qa = h / (Hv / a.Hk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c0 = wave * 32;
+  int64_t s0 = a.cu[n], e0 = a.cu[n + 1];
+  s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
+  e0 = e0 < s0 ? s0 : (e0 > a.T ? a.T : e0);
+  const int nch = (int)((e0 - s0 + BT - 1) / BT);
+  const int chunk0 = a.seq_chunk_off[n];
+
+  zero_upper<O, true, NT>(sm, tid);
+  floatx4 dS[DKT][2];
+  {
+    const float* src = a.dht ? a.dht + ((int64_t)n * Hv + h) * DK * DV : nullptr;
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          dS[mt][nt][j] = src ? src[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] : 0.f;
+  }
+  const E* qp = (const E*)a.q + (int64_t)qa * DK;
+  const E* kp = (const E*)a.k + (int64_t)qa * DK;
+  const E* dop = (const E*)a.d_o + (int64_t)h * DV;
+  const float* gp = a.g + h;
+  const float* bp = a.beta + h;
+  typename CF::PF pf;
+  if (nch > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, s0 + (int64_t)(nch - 1) * BT, e0, tid);
+
+  for (int c = nch - 1; c >= 0; c--) {
+    const int64_t tc = s0 + (int64_t)c * BT;
+    __syncthreads();
+    stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
+    if (c > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, tc - BT, e0, tid);
+    {  // dS' of this chunk for the gradient kernel
+      float* dst = a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV;
+#pragma unroll
+      for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
+    }
+    __syncthreads();
+    gram_kk<O, DK, NW>(sm, wave, lane);
+    __syncthreads();
+    solve<O, DK, NW, true>(sm, wave, lane);
+    compute_w<O, DK, NW>(sm, wave, lane);
+    __syncthreads();
+
+    const float GC = sm.G[BT - 1];
+    // dVn = P^T dO + D o (K dS')
+    typename M::frag sb[NSK][2];
+#pragma unroll
+    for (int s = 0; s < NSK; s++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++) sb[s][nt] = acc_as_b<O>(dS, s, nt);
+    floatx4 dvn[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      floatx4 k0 = zero4(), k1 = zero4(), p0 = zero4(), p1 = zero4();
+#pragma unroll
+      for (int s = 0; s < NSK; s++) {
+        const typename M::frag kf = M::load(sm.k, SM::LDK, 16 * mt, s * KS, lane);
+        M::mma(k0, kf, sb[s][0]);
+        M::mma(k1, kf, sb[s][1]);
+      }
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
+        M::mma(p0, pt, M::load_col(sm.v, SM::LDV, c0, s * KS, lane));
+        M::mma(p1, pt, M::load_col(sm.v, SM::LDV, c0 + 16, s * KS, lane));
+      }
+      const int rb = 16 * mt + 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float d = __expf(GC - sm.G[rb + j]);
+        p0[j] += d * k0[j];
+        p1[j] += d * k1[j];
+      }
+      dvn[mt][0] = -p0;  // stored negated: the W^T term enters with a minus
+      dvn[mt][1] = -p1;
+    }
+    // dS <- gamma_C dS' + Q^T (gamma o dO) - W^T dVn
+    const float eC = __expf(GC);
+    typename M::frag db[NSB][2], gb[NSB][2];
+#pragma unroll
+    for (int s = 0; s < NSB; s++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++) {
+        db[s][nt] = acc_as_b<O>(dvn, s, nt);
+        gb[s][nt] = M::load_col_scaled(sm.v, SM::LDV, c0 + 16 * nt, s * KS, sm.eg, lane);
+      }
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++) {
+      floatx4 acc0 = dS[mt][0] * eC, acc1 = dS[mt][1] * eC;
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        const typename M::frag qt = M::load_col(sm.q, SM::LDK, 16 * mt, s * KS, lane);
+        const typename M::frag wt = M::load_col(sm.w, SM::LDK, 16 * mt, s * KS, lane);
+        M::mma(acc0, qt, gb[s][0]);
+        M::mma(acc1, qt, gb[s][1]);
+        M::mma(acc0, wt, db[s][0]);
+        M::mma(acc1, wt, db[s][1]);
+      }
+      dS[mt][0] = acc0;
+      dS[mt][1] = acc1;
+    }
+  }
+  if (a.dh0) {
+    float* dst = a.dh0 + ((int64_t)n * Hv + h) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
+  }
 }
+
+// ---------------------------------------------------------------------------
+// 3. local gradients of one (chunk, head)
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+struct GradSmem {
+  typedef Smem<E, DK, DV, true> SM;
+  static constexpr int LDA = BT + 4;  // dA, dA^T, M1 + M1^T: [64][68] operand type
+  static constexpr int NW = DV / 32;
+  static constexpr bool MS_IN_V = sizeof(E) * BT * SM::LDV >= sizeof(E) * BT * LDA;
+  SM b;
+  alignas(16) E dO[BT * SM::LDV];
+  alignas(16) E ms_own[MS_IN_V ? 8 : BT * LDA];
+  alignas(16) float part[4][NW][BT];  // row sums over each wave's columns
+  alignas(16) float tp[5][4][BT];     // row/column sums of the 64x64 tiles
+  alignas(16) float dot[NW];
+};
+
+// row-partials kinds
+enum { kRB = 0, kRYKS = 1, kRDOQS = 2, kRKDSVN = 3 };
+// tile partial kinds
+enum { kRowP = 0, kColP = 1, kRowKK = 2, kRowL = 3, kColL = 4 };
+
+// sum over the 16 lanes of each lane group (one C-tile row)
+GDN_DEV float row16_sum(float v) { return group_sum<16>(v); }
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a) {
+  static_assert(DK == DV, "the gradient kernel assumes dk == dv");
+  typedef BwdCfg<E, DK, DV> CF;
+  typedef typename CF::O O;
+  typedef Mfma<O> M;
+  typedef GradSmem<E, DK, DV> GS;
+  typedef typename GS::SM SM;
+  constexpr int NW = CF::NW, NT = CF::NT, KS = M::KSTEP;
+  constexpr int NSK = DK / KS, NSB = BT / KS;
+  constexpr int LDV = SM::LDV, LDA = GS::LDA;
+  __shared__ GS gs;
+  SM& sm = gs.b;
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= a.counts[1]) return;
+  const int4 ent = a.chunk_tab[c];
+  const int64_t tc = ent.x, te = ent.y;
+  const int Hv = a.Hv, qa = h / (Hv / a.Hk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, ln = lane & 15;
+  const int c0 = wave * 32;
+
+  zero_upper<O, true, NT>(sm, tid);
+  {
+    typename CF::PF pf;
+    pf.load((const E*)a.q + (int64_t)qa * DK, (const E*)a.k + (int64_t)qa * DK, a.ld_qk,
+            (const E*)a.v + (int64_t)h * DV, a.ld_v, a.g + h, a.beta + h, Hv, tc, te, tid);
+    typedef typename Vec16<E>::type V16;
+    constexpr int VE = Vec16<E>::N, VPR = DV / VE;
+    const E* dop = (const E*)a.d_o + (int64_t)h * DV;
+    for (int i = tid; i < BT * VPR; i += NT) {
+      const int row = i / VPR, vi = i % VPR;
+      const int64_t t = tc + row;
+      *reinterpret_cast<V16*>(gs.dO + row * LDV + vi * VE) =
+          t < te ? *reinterpret_cast<const V16*>(dop + (t * Hv) * DV + vi * VE) : zero_vec16<E>();
+    }
+    stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
+  }
+  __syncthreads();
+  gram_kk<O, DK, NW>(sm, wave, lane);
+  __syncthreads();
+  solve<O, DK, NW, true>(sm, wave, lane);
+  floatx4 vn[4][2];
+  compute_u<O>(sm, c0, lane, vn);  // u, turned into Vn below
+  compute_w<O, DK, NW>(sm, wave, lane);
+  __syncthreads();
+
+  const float GC = sm.G[BT - 1];
+  const float* Sg = a.states + ((int64_t)c * Hv + h) * DK * DV;
+  const float* dSg = a.dstates + ((int64_t)c * Hv + h) * DK * DV;
+
+  // S and dS' as B fragments (K = dk, N = this wave's value columns) and <dS', S>
+  typename M::frag sb[NSK][2], dsb[NSK][2];
+  float dot = 0.f;
+#pragma unroll
+  for (int s = 0; s < NSK; s++)
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++) {
+      constexpr int TPS = KS / 16;  // C-tiles per contraction step
+      floatx4 st[TPS], dt[TPS];
+#pragma unroll
+      for (int q = 0; q < TPS; q++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int idx = (16 * (TPS * s + q) + 4 * g4 + j) * DV + c0 + 16 * nt + ln;
+          st[q][j] = Sg[idx];
+          dt[q][j] = dSg[idx];
+          dot += st[q][j] * dt[q][j];
+        }
+      if constexpr (TPS == 2) {
+        sb[s][nt] = M::from_acc(st[0], st[1]);
+        dsb[s][nt] = M::from_acc(dt[0], dt[1]);
+      } else {
+        sb[s][nt] = M::from_acc(st[0]);
+        dsb[s][nt] = M::from_acc(dt[0]);
+      }
+    }
+
+  // Vn = u - W S; QS; KS; K dS'
+  floatx4 ks[4][2], kds[4][2];
+  float r_doqs[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    floatx4 w0 = zero4(), w1 = zero4(), q0 = zero4(), q1 = zero4(), k0 = zero4(), k1 = zero4(),
+            d0 = zero4(), d1 = zero4();
+#pragma unroll
+    for (int s = 0; s < NSK; s++) {
+      const typename M::frag wf = M::load(sm.w, SM::LDK, 16 * mt, s * KS, lane);
+      const typename M::frag qf = M::load(sm.q, SM::LDK, 16 * mt, s * KS, lane);
+      const typename M::frag kf = M::load(sm.k, SM::LDK, 16 * mt, s * KS, lane);
+      M::mma(w0, wf, sb[s][0]);
+      M::mma(w1, wf, sb[s][1]);
+      M::mma(q0, qf, sb[s][0]);
+      M::mma(q1, qf, sb[s][1]);
+      M::mma(k0, kf, sb[s][0]);
+      M::mma(k1, kf, sb[s][1]);
+      M::mma(d0, kf, dsb[s][0]);
+      M::mma(d1, kf, dsb[s][1]);
+    }
+    vn[mt][0] -= w0;
+    vn[mt][1] -= w1;
+    ks[mt][0] = k0;
+    ks[mt][1] = k1;
+    kds[mt][0] = d0;
+    kds[mt][1] = d1;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int row = 16 * mt + 4 * g4 + j;
+      r_doqs[mt][j] = to_f(gs.dO[row * LDV + c0 + ln]) * q0[j] + to_f(gs.dO[row * LDV + c0 + 16 + ln]) * q1[j];
+    }
+  }
+  // dVn = P^T dO + D o K dS'
+  floatx4 dvn[4][2];
+  float r_kdsvn[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    floatx4 p0 = zero4(), p1 = zero4();
+#pragma unroll
+    for (int s = 0; s < NSB; s++) {
+      const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
+      M::mma(p0, pt, M::load_col(gs.dO, LDV, c0, s * KS, lane));
+      M::mma(p1, pt, M::load_col(gs.dO, LDV, c0 + 16, s * KS, lane));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int row = 16 * mt + 4 * g4 + j;
+      const float d = __expf(GC - sm.G[row]);
+      r_kdsvn[mt][j] = kds[mt][0][j] * vn[mt][0][j] + kds[mt][1][j] * vn[mt][1][j];
+      p0[j] += d * kds[mt][0][j];
+      p1[j] += d * kds[mt][1][j];
+    }
+    dvn[mt][0] = p0;
+    dvn[mt][1] = p1;
+  }
+  // Y = T^T dVn; dv = beta o Y
+  floatx4 y[4][2];
+  float r_b[4][4], r_yks[4][4];
+  E* dvp = (E*)a.dv + (int64_t)h * DV + c0 + ln;
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    floatx4 y0 = zero4(), y1 = zero4();
+#pragma unroll
+    for (int s = 0; s < NSB; s++) {
+      const typename M::frag tt = M::load_col_f32(sm.Tm, SM::LDF, 16 * mt, s * KS, nullptr, lane);
+      M::mma(y0, tt, acc_as_b<O>(dvn, s, 0));
+      M::mma(y1, tt, acc_as_b<O>(dvn, s, 1));
+    }
+    y[mt][0] = y0;
+    y[mt][1] = y1;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int row = 16 * mt + 4 * g4 + j;
+      const float bt = sm.beta[row];
+      r_b[mt][j] = y0[j] * to_f(sm.v[row * LDV + c0 + ln]) + y1[j] * to_f(sm.v[row * LDV + c0 + 16 + ln]);
+      r_yks[mt][j] = y0[j] * ks[mt][0][j] + y1[j] * ks[mt][1][j];
+      const int64_t t = tc + row;
+      if (t < te) {
+        dvp[t * a.ld_dv] = from_f<E>(bt * y0[j]);
+        dvp[t * a.ld_dv + 16] = from_f<E>(bt * y1[j]);
+      }
+    }
+  }
+  // row sums over this wave's columns
+  dot = group_sum<64>(dot);
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float v0 = row16_sum(r_b[mt][j]), v1 = row16_sum(r_yks[mt][j]),
+                  v2 = row16_sum(r_doqs[mt][j]), v3 = row16_sum(r_kdsvn[mt][j]);
+      if (ln == 0) {
+        const int row = 16 * mt + 4 * g4 + j;
+        gs.part[kRB][wave][row] = v0;
+        gs.part[kRYKS][wave][row] = v1;
+        gs.part[kRDOQS][wave][row] = v2;
+        gs.part[kRKDSVN][wave][row] = v3;
+      }
+    }
+  if (lane == 0) gs.dot[wave] = dot;
+  __syncthreads();  // w, Tm, v, p-columns reads done
+  // Vn over w, Y over Tm (operand type, [64][LDV])
+  O* sVn = sm.w;
+  O* sY = reinterpret_cast<O*>(sm.Tm);
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int row = 16 * mt + 4 * g4 + j;
+      sVn[row * LDV + c0 + ln] = from_f<O>(vn[mt][0][j]);
+      sVn[row * LDV + c0 + 16 + ln] = from_f<O>(vn[mt][1][j]);
+      sY[row * LDV + c0 + ln] = from_f<O>(y[mt][0][j]);
+      sY[row * LDV + c0 + 16 + ln] = from_f<O>(y[mt][1][j]);
+    }
+  __syncthreads();
+
+  // dL = -Y Vn^T (strict lower): M1 + M1^T, dbeta and dG partials
+  O* sMs = GS::MS_IN_V ? sm.v : gs.ms_own;
+  for (int t = wave; t < 10; t += NW) {
+    int i, j;
+    lower_tile_ij(t, i, j);
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < DV / KS; s++)
+      M::mma(acc, M::load(sY, LDV, 16 * i, s * KS, lane), M::load(sVn, LDV, 16 * j, s * KS, lane));
+    const int col = 16 * j + ln;
+    float rk[4], rl[4], cl = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int row = 16 * i + 4 * g4 + jj;
+      const bool lo = row > col;
+      const float dl = lo ? -acc[jj] : 0.f;
+      const float kk = sm.L[row * SM::LDF + col];  // kh.kh o Gamma (strict lower, no beta)
+      const float gam = lo ? __expf(sm.G[row] - sm.G[col]) : 0.f;
+      const float m1 = sm.beta[row] * dl * gam;
+      rk[jj] = dl * kk;
+      rl[jj] = dl * sm.beta[row] * kk;
+      cl += rl[jj];
+      if (i > j || lo) {
+        sMs[row * LDA + col] = from_f<O>(m1);
+        sMs[col * LDA + row] = from_f<O>(m1);
+      } else if (row == col) {
+        sMs[row * LDA + col] = from_f<O>(0.f);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const float a1 = row16_sum(rk[jj]), a2 = row16_sum(rl[jj]);
+      if (ln == 0) {
+        gs.tp[kRowKK][j][16 * i + 4 * g4 + jj] = a1;
+        gs.tp[kRowL][j][16 * i + 4 * g4 + jj] = a2;
+      }
+    }
+    cl += __shfl_xor(cl, 16, 64);
+    cl += __shfl_xor(cl, 32, 64);
+    if (g4 == 0) gs.tp[kColL][i][col] = cl;
+  }
+  __syncthreads();
+
+  // dP = dO Vn^T (lower incl): dA = dP o Gamma into L's region; dG partials
+  O* sdA = reinterpret_cast<O*>(sm.L);
+  floatx4 dat[(10 + NW - 1) / NW];
+  int nmine = 0;
+  for (int t = wave; t < 10; t += NW, nmine++) {
+    int i, j;
+    lower_tile_ij(t, i, j);
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < DV / KS; s++)
+      M::mma(acc, M::load(gs.dO, LDV, 16 * i, s * KS, lane), M::load(sVn, LDV, 16 * j, s * KS, lane));
+    const int col = 16 * j + ln;
+    float rp[4], cp = 0.f;
+    floatx4 da;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int row = 16 * i + 4 * g4 + jj;
+      const bool lo = row >= col;
+      const float dp = lo ? acc[jj] : 0.f;
+      da[jj] = lo ? dp * __expf(sm.G[row] - sm.G[col]) : 0.f;
+      rp[jj] = dp * to_f(sm.p[row * SM::LDT + col]);
+      cp += rp[jj];
+      sdA[row * LDA + col] = from_f<O>(da[jj]);
+      if (i > j) sdA[(16 * j + 4 * g4 + jj) * LDA + 16 * i + ln] = from_f<O>(0.f);
+    }
+    dat[nmine] = da;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const float a1 = row16_sum(rp[jj]);
+      if (ln == 0) gs.tp[kRowP][j][16 * i + 4 * g4 + jj] = a1;
+    }
+    cp += __shfl_xor(cp, 16, 64);
+    cp += __shfl_xor(cp, 32, 64);
+    if (g4 == 0) gs.tp[kColP][i][col] = cp;
+  }
+  __syncthreads();  // P reads done: dA^T goes over p
+  O* sdAT = sm.p;
+  nmine = 0;
+  for (int t = wave; t < 10; t += NW, nmine++) {
+    int i, j;
+    lower_tile_ij(t, i, j);
+    const int col = 16 * j + ln;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int row = 16 * i + 4 * g4 + jj;
+      sdAT[col * LDA + row] = from_f<O>(dat[nmine][jj]);
+      if (i > j) sdAT[(16 * i + 4 * g4 + jj) * LDA + 16 * j + ln] = from_f<O>(0.f);
+    }
+  }
+  __syncthreads();
+
+  // dk-side: this wave's key columns [c0, c0+32)
+  float* dqk = a.dqk + (int64_t)h * 2 * DK;
+#pragma unroll
+  for (int nt = 0; nt < 2; nt++) {
+    const int dc = c0 + 16 * nt;
+    typename M::frag st[NSK], dst[NSK], kc[NSB], qc[NSB];
+#pragma unroll
+    for (int s = 0; s < NSK; s++) {
+      st[s] = M::load_f32(Sg, DV, dc, s * KS, lane);    // B[k = value idx][n = key idx] = S[n][k]
+      dst[s] = M::load_f32(dSg, DV, dc, s * KS, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < NSB; s++) {
+      kc[s] = M::load_col(sm.k, SM::LDK, dc, s * KS, lane);
+      qc[s] = M::load_col(sm.q, SM::LDK, dc, s * KS, lane);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      floatx4 a1 = zero4(), a2 = zero4(), b3 = zero4(), b4 = zero4(), b5 = zero4(), b6 = zero4();
+#pragma unroll
+      for (int s = 0; s < NSK; s++) {
+        M::mma(a1, M::load(gs.dO, LDV, 16 * mt, s * KS, lane), st[s]);
+        M::mma(b4, M::load(sVn, LDV, 16 * mt, s * KS, lane), dst[s]);
+        M::mma(b5, M::load(sY, LDV, 16 * mt, s * KS, lane), st[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        M::mma(a2, M::load(sdA, LDA, 16 * mt, s * KS, lane), kc[s]);
+        M::mma(b3, M::load(sdAT, LDA, 16 * mt, s * KS, lane), qc[s]);
+        M::mma(b6, M::load(sMs, LDA, 16 * mt, s * KS, lane), kc[s]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * mt + 4 * g4 + j;
+        const int64_t t = tc + row;
+        const float gm = sm.eg[row];
+        const float d = __expf(GC - sm.G[row]);
+        const float dqv = gm * a1[j] + a2[j];
+        const float dkv = b3[j] + d * b4[j] - sm.beta[row] * gm * b5[j] + b6[j];
+        if (t < te) {
+          dqk[t * Hv * 2 * DK + dc + ln] = dqv;
+          dqk[t * Hv * 2 * DK + DK + dc + ln] = dkv;
+        }
+      }
+    }
+  }
+
+  // dbeta, dG -> dg (wave 0, lane = row)
+  if (wave == 0) {
+    const int r = lane;
+    const int rb = r >> 4;
+    float rB = 0.f, rYKS = 0.f, rDOQS = 0.f, rKDSVN = 0.f, dotS = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      rB += gs.part[kRB][w][r];
+      rYKS += gs.part[kRYKS][w][r];
+      rDOQS += gs.part[kRDOQS][w][r];
+      rKDSVN += gs.part[kRKDSVN][w][r];
+      dotS += gs.dot[w];
+    }
+    float rowP = 0.f, colP = 0.f, rowKK = 0.f, rowL = 0.f, colL = 0.f;
+    for (int j = 0; j <= rb; j++) {
+      rowP += gs.tp[kRowP][j][r];
+      rowKK += gs.tp[kRowKK][j][r];
+      rowL += gs.tp[kRowL][j][r];
+    }
+    for (int i = rb; i < 4; i++) {
+      colP += gs.tp[kColP][i][r];
+      colL += gs.tp[kColL][i][r];
+    }
+    const float gm = sm.eg[r], bt = sm.beta[r];
+    const float d = __expf(GC - sm.G[r]);
+    const float dbeta = rB - gm * rYKS + rowKK;
+    float dG = gm * rDOQS - d * rKDSVN - bt * gm * rYKS + rowP - colP + rowL - colL;
+    const float tail = group_sum<64>(d * rKDSVN) + __expf(GC) * dotS;  // d/dG_C terms
+    if (r == BT - 1) dG += tail;
+    // dg_t = sum_{s >= t} dG_s within the chunk
+    float suf = dG;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(suf, off, 64);
+      if (r + off < 64) suf += o;
+    }
+    const int64_t t = tc + r;
+    if (t < te) {
+      a.dbeta[t * Hv + h] = dbeta;
+      a.dg[t * Hv + h] = suf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. sum over value heads and back through l2norm / scale
+// ---------------------------------------------------------------------------
+template <typename E, int DK>
+__global__ __launch_bounds__(256) void finalize_qk_kernel(BwdArgs a, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (u >= units) return;
+  const int64_t t = u / a.Hk;
+  const int qa = (int)(u % a.Hk);
+  const int grp = a.Hv / a.Hk;
+  constexpr int PER = (DK + 63) / 64;
+  float dq[PER], dk[PER], q[PER], k[PER];
+  float qs = 0.f, ks = 0.f, qd = 0.f, kd = 0.f;
+  const E* qp = (const E*)a.q + t * a.ld_qk + (int64_t)qa * DK;
+  const E* kp = (const E*)a.k + t * a.ld_qk + (int64_t)qa * DK;
+#pragma unroll
+  for (int e = 0; e < PER; e++) {
+    const int d = lane + 64 * e;
+    dq[e] = dk[e] = q[e] = k[e] = 0.f;
+    if (d < DK) {
+      for (int hh = qa * grp; hh < (qa + 1) * grp; hh++) {
+        const float* src = a.dqk + (t * a.Hv + hh) * 2 * DK;
+        dq[e] += src[d];
+        dk[e] += src[DK + d];
+      }
+      q[e] = to_f(qp[d]);
+      k[e] = to_f(kp[d]);
+    }
+    qs += q[e] * q[e];
+    ks += k[e] * k[e];
+    qd += q[e] * dq[e];
+    kd += k[e] * dk[e];
+  }
+  qs = group_sum<64>(qs);
+  ks = group_sum<64>(ks);
+  qd = group_sum<64>(qd);
+  kd = group_sum<64>(kd);
+  E* dqp = (E*)a.dq + t * a.ld_dqk + (int64_t)qa * DK;
+  E* dkp = (E*)a.dk + t * a.ld_dqk + (int64_t)qa * DK;
+  const float rq = a.use_l2norm ? 1.f / sqrtf(qs + 1e-6f) : 1.f;
+  const float rk = a.use_l2norm ? 1.f / sqrtf(ks + 1e-6f) : 1.f;
+#pragma unroll
+  for (int e = 0; e < PER; e++) {
+    const int d = lane + 64 * e;
+    if (d < DK) {
+      float gq = a.scale * dq[e], gk = dk[e];
+      if (a.use_l2norm) {
+        gq = a.scale * rq * (dq[e] - q[e] * rq * rq * qd);
+        gk = rk * (dk[e] - k[e] * rk * rk * kd);
+      }
+      dqp[d] = from_f<E>(gq);
+      dkp[d] = from_f<E>(gk);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+  Plan plan;
+  size_t off_states, off_dstates, off_dqk, end;
+};
+
+BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) {
+  BwdLayout L;
+  L.plan = make_plan(T, N, Hv, dk, dv);
+  size_t o = L.plan.end;
+  const size_t st = sizeof(float) * (size_t)L.plan.chunk_cap * Hv * dk * dv;
+  L.off_states = o;
+  o = gdn::round_up(o + st, 256);
+  L.off_dstates = o;
+  o = gdn::round_up(o + st, 256);
+  L.off_dqk = o;
+  o = gdn::round_up(o + sizeof(float) * (size_t)T * Hv * 2 * dk, 256);
+  L.end = o;
+  return L;
+}
+
+template <typename E, int DK, int DV>
+int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayout& L, char* ws,
+               hipStream_t stream) {
+  typedef BwdCfg<E, DK, DV> CF;
+  PlanPtrs pp = L.plan.ptrs(ws, true);
+  b.counts = pp.counts;
+  b.chunk_tab = pp.chunk_tab;
+  b.seq_chunk_off = pp.seq_chunk_off;
+  b.states = reinterpret_cast<const float*>(ws + L.off_states);
+  b.dstates = reinterpret_cast<float*>(ws + L.off_dstates);
+  b.dqk = reinterpret_cast<float*>(ws + L.off_dqk);
+  LoopArgs la = la_in;
+  la.states = reinterpret_cast<float*>(ws + L.off_states);
+  if (int rc = run_pipeline<E, DK, DV, kStates>(la, b.cu, N, T, L.plan, ws, true, stream)) return rc;
+  hipLaunchKernelGGL((dstate_kernel<E, DK, DV>), dim3(N, b.Hv), dim3(CF::NT), 0, stream, b);
+  if (int rc = gdn::check_launch("gdn_chunk_bwd(dstate)")) return rc;
+  hipLaunchKernelGGL((grad_kernel<E, DK, DV>), dim3((unsigned)L.plan.chunk_cap, b.Hv), dim3(CF::NT),
+                     0, stream, b);
+  if (int rc = gdn::check_launch("gdn_chunk_bwd(grad)")) return rc;
+  const int64_t units = T * b.Hk;
+  hipLaunchKernelGGL((finalize_qk_kernel<E, DK>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0,
+                     stream, b, units);
+  return gdn::check_launch("gdn_chunk_bwd(finalize)");
+}
+
+// dh0 = dht (or 0) for every sequence when there are no tokens at all
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(const float* __restrict__ src,
+                                                           float* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
 
 extern "C" size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv,
                                            int32_t dk, int32_t dv, gdn_dtype dt, int bwd) {
   (void)Hk;
   (void)dt;
-  if (bwd) return 0;
-  return gdn_chunk_fwd_workspace(T, N, Hv, dk, dv);
+  if (T < 0 || N < 0 || Hv < 1 || dk < 1 || dv < 1) return 0;
+  if (!bwd) return gdn::chunk_fwd_workspace(T, N, Hv, dk, dv);
+  return bwd_layout(T, N, Hv, dk, dv).end;
 }
 
 extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v,
@@ -29,11 +758,72 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const 
                              int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta,
                              float* dh0, void* ws, size_t ws_bytes, gdn_dtype dt,
                              hipStream_t stream) {
-  (void)h0; (void)scale; (void)use_qk_l2norm; (void)d_o; (void)dht; (void)dq; (void)dk_;
-  (void)ld_dqk; (void)dv_; (void)ld_dv; (void)dg; (void)dbeta; (void)dh0; (void)ws;
-  (void)ws_bytes; (void)stream;
   int rc = gdn::validate_chunk("gdn_chunk_bwd", q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk,
                                Hv, dk, dv, dt);
   if (rc != GDN_OK) return rc;
-  return gdn::fail(GDN_EUNSUPPORTED, "gdn_chunk_bwd: not built yet");
+  const bool have = (dt == GDN_BF16 && dk == dv && (dk == 128 || dk == 64)) ||
+                    (dt == GDN_F32 && dk == dv && (dk == 32 || dk == 64));
+  if (!have)
+    return gdn::fail(GDN_EUNSUPPORTED,
+                     "gdn_chunk_bwd: needs dk == dv (128 or 64 for bfloat16, 32 or 64 for float32)");
+  if (T > 0 && (!d_o || !dq || !dk_ || !dv_ || !dg || !dbeta))
+    return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: null gradient pointer");
+  if (ld_dqk < (int64_t)Hk * dk || ld_dv < (int64_t)Hv * dv)
+    return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: gradient row strides smaller than the head blocks");
+  const BwdLayout L = bwd_layout(T, N, Hv, dk, dv);
+  if (!ws || ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_bwd: workspace needs %zu bytes, 256-byte aligned",
+                     L.end);
+  if (T == 0 || N == 0) {
+    if (dh0 && N > 0) {
+      const int64_t n = (int64_t)N * Hv * dk * dv;
+      hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                         dht, dh0, n);
+      return gdn::check_launch("gdn_chunk_bwd(empty)");
+    }
+    return GDN_OK;
+  }
+  BwdArgs b{};
+  b.q = q;
+  b.k = k;
+  b.ld_qk = ld_qk;
+  b.v = v;
+  b.ld_v = ld_v;
+  b.g = g;
+  b.beta = beta;
+  b.Hk = Hk;
+  b.Hv = Hv;
+  b.scale = scale;
+  b.use_l2norm = use_qk_l2norm ? 1 : 0;
+  b.d_o = d_o;
+  b.dht = dht;
+  b.dq = dq;
+  b.dk = dk_;
+  b.ld_dqk = ld_dqk;
+  b.dv = dv_;
+  b.ld_dv = ld_dv;
+  b.dg = dg;
+  b.dbeta = dbeta;
+  b.dh0 = dh0;
+  b.cu = cu_seqlens;
+  b.T = T;
+  LoopArgs la{};
+  la.q = q;
+  la.k = k;
+  la.ld_qk = ld_qk;
+  la.v = v;
+  la.ld_v = ld_v;
+  la.g = g;
+  la.beta = beta;
+  la.h0 = h0;
+  la.Hk = Hk;
+  la.Hv = Hv;
+  la.scale = scale;
+  la.use_l2norm = b.use_l2norm;
+  if (dt == GDN_BF16) {
+    if (dk == 128) return launch_bwd<bf16, 128, 128>(b, la, N, T, L, (char*)ws, stream);
+    return launch_bwd<bf16, 64, 64>(b, la, N, T, L, (char*)ws, stream);
+  }
+  if (dk == 32) return launch_bwd<float, 32, 32>(b, la, N, T, L, (char*)ws, stream);
+  return launch_bwd<float, 64, 64>(b, la, N, T, L, (char*)ws, stream);
 }

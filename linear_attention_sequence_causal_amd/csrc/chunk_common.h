@@ -6,23 +6,25 @@
 // one workgroup with every intermediate on chip:
 //   qh, kh    l2-normalised q (times scale) and k            (_l2norm_torch)
 //   G         in-chunk cumulative sum of g
-//   L         strict-lower( diag(beta) kh kh^T o exp(G_i - G_j) )
+//   L         strict-lower( diag(beta) kh kh^T o exp(G_i - G_j) ); the LDS
+//             copy holds it without diag(beta), which the solve applies
 //   P         lower-incl( qh kh^T o exp(G_i - G_j) )      (the output's attn)
 //   T         (I + L)^-1, unit lower triangular
 //   u         T diag(beta) v                              (chunk_value)
 //   w         T diag(beta exp(G)) kh                      (k_cumdecay)
 // The page forms T by a 63-step row recurrence; here the four 16x16
-// diagonal blocks are inverted by column-parallel forward substitution (one
-// wave, one lane per column) and the off-diagonal blocks follow from
-// T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj on fp32 MFMA, one block distance at
-// a time.  Products with token-sized contraction use bf16 MFMA with fp32
-// accumulation (fp32 MFMA for float32 activations); see gdn_common.h for
-// the fragment convention.
+// diagonal blocks are inverted by column-oriented forward substitution (one
+// wave, one lane per column, while the other waves form P) and the
+// off-diagonal blocks follow from T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj on
+// fp32 MFMA, one block distance at a time.  Products with token-sized
+// contraction use bf16 MFMA with fp32 accumulation (fp32 MFMA for float32
+// activations); see gdn_common.h for the fragment convention.
 //
-// LDS layout (one workgroup = one chunk of one head at a time):
-//   q  [64][DK+pad]  kh rows, k [64][DK+pad], kt [DK][64+pad] (kh transposed),
-//   vt [DV][64+pad] (v transposed), w [64][DK+pad], p [64][64+pad] (operand
-//   type), L and Tm [64][68] fp32, G / beta / beta*exp(G) [64] fp32.
+// LDS (one workgroup = one chunk of one head at a time), rows padded by 16
+// bytes: q, k [64][DK], v [64][DV], w [64][DK] and p [64][64] in the operand
+// type; L and Tm [64][68] fp32; G, beta, beta*exp(G), exp(G) [64] fp32.  Operands
+// whose contraction index is the token (k in w and in the state update, v
+// in u) are read down columns of the row-major copies.
 #pragma once
 
 #include "gdn_common.h"
@@ -31,18 +33,16 @@ namespace gdn_chunk {
 
 constexpr int BT = 64;  // chunk length
 
-template <typename E> struct OpType { typedef E type; };  // bf16 -> bf16, float -> float
-
-template <typename O, int DK, int DV, bool HAS_Q, bool HAS_BWD = false>
+template <typename O, int DK, int DV, bool HAS_Q>
 struct Smem {
   static constexpr int PAD = 16 / (int)sizeof(O);
   static constexpr int LDK = DK + PAD;  // row-major [BT][DK]
-  static constexpr int LDT = BT + PAD;  // [D][BT] and [BT][BT] operand arrays
+  static constexpr int LDV = DV + PAD;  // row-major [BT][DV]
+  static constexpr int LDT = BT + PAD;  // [BT][BT] operand arrays
   static constexpr int LDF = BT + 4;    // fp32 [BT][BT]
   alignas(16) O q[HAS_Q ? BT * LDK : 8];
   alignas(16) O k[BT * LDK];
-  alignas(16) O kt[DK * LDT];
-  alignas(16) O vt[DV * LDT];
+  alignas(16) O v[BT * LDV];
   alignas(16) O w[BT * LDK];
   alignas(16) O p[HAS_Q ? BT * LDT : 8];
   alignas(16) float L[BT * LDF];
@@ -50,6 +50,7 @@ struct Smem {
   alignas(16) float G[BT];
   alignas(16) float beta[BT];
   alignas(16) float bg[BT];  // beta * exp(G)
+  alignas(16) float eg[BT];  // exp(G)
 };
 
 // Global -> register prefetch of one chunk (q, k rows of q/k head `qa`, v
@@ -99,15 +100,16 @@ struct Prefetch {
   }
 };
 
-// Register prefetch -> LDS: l2norm (and q scale), plain and transposed
-// copies, in-chunk cumsum of g.  Rows past the sequence end are zero, which
+// Register prefetch -> LDS: l2norm (and q scale), row-major copies (16-byte
+// stores), in-chunk cumsum of g.  Rows past the sequence end are zero, which
 // leaves the state untouched (the page's zero padding).
 template <typename E, typename O, int DK, int DV, int NT, bool HAS_Q, class SM>
 GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale, int use_l2norm,
                    int tid) {
   typedef Prefetch<E, DK, DV, NT, HAS_Q> PF;
+  typedef typename Vec16<O>::type OV;
   constexpr int VE = PF::VE;
-  constexpr int LDK = SM::LDK, LDT = SM::LDT;
+  static_assert(sizeof(E) == sizeof(O), "activation and operand types must match");
 #pragma unroll
   for (int p = 0; p < PF::PQ; p++) {
     const int i = tid + NT * p;
@@ -124,30 +126,28 @@ GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale
       }
     }
     kss = group_sum<PF::QPR>(kss);
-    float kr = use_l2norm ? 1.f / sqrtf(kss + 1e-6f) : 1.f;
+    const float kr = use_l2norm ? 1.f / sqrtf(kss + 1e-6f) : 1.f;
     float qr = scale;
     if constexpr (HAS_Q) {
       qss = group_sum<PF::QPR>(qss);
       if (use_l2norm) qr = scale / sqrtf(qss + 1e-6f);
     }
     if (i < PF::QV) {
+      OV kv, qv;
 #pragma unroll
       for (int e = 0; e < VE; e++) {
-        const O kv = from_f<O>(kf[e] * kr);
-        sm.k[row * LDK + vi * VE + e] = kv;
-        sm.kt[(vi * VE + e) * LDT + row] = kv;
-        if constexpr (HAS_Q) sm.q[row * LDK + vi * VE + e] = from_f<O>(qf[e] * qr);
+        kv[e] = from_f<O>(kf[e] * kr);
+        if constexpr (HAS_Q) qv[e] = from_f<O>(qf[e] * qr);
       }
+      *reinterpret_cast<OV*>(sm.k + row * SM::LDK + vi * VE) = kv;
+      if constexpr (HAS_Q) *reinterpret_cast<OV*>(sm.q + row * SM::LDK + vi * VE) = qv;
     }
   }
 #pragma unroll
   for (int p = 0; p < PF::PV; p++) {
     const int i = tid + NT * p;
     const int row = i / PF::VPR, vi = i % PF::VPR;
-    if (i < PF::VV) {
-#pragma unroll
-      for (int e = 0; e < VE; e++) sm.vt[(vi * VE + e) * LDT + row] = from_f<O>(to_f(pf.v[p][e]));
-    }
+    if (i < PF::VV) *reinterpret_cast<OV*>(sm.v + row * SM::LDV + vi * VE) = pf.v[p];
   }
   if (tid < BT) {  // wave 0: inclusive scan of g over the 64 rows
     float G = pf.g;
@@ -156,43 +156,53 @@ GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale
       const float o = __shfl_up(G, off, 64);
       if (tid >= off) G += o;
     }
+    const float eG = __expf(G);
     sm.G[tid] = G;
     sm.beta[tid] = pf.beta;
-    sm.bg[tid] = pf.beta * __expf(G);
+    sm.bg[tid] = pf.beta * eG;
+    sm.eg[tid] = eG;
   }
 }
 
-// L (fp32) and, with HAS_Q, P (operand type) from kh kh^T and qh kh^T.
-// Only the 10 lower 16x16 tiles are computed; the upper tiles of L, P and
-// Tm are zeroed once per kernel by zero_upper().
-template <typename O, int DK, int NW, bool HAS_Q, class SM>
-GDN_DEV void gram(SM& sm, int wave, int lane) {
+// One lower 16x16 tile (i, j), j <= i, of kh kh^T (-> strict-lower L
+// without beta, fp32) or qh kh^T (-> P, operand type), with the decay
+// exp(G_row - G_col) applied.
+template <typename O, int DK, class SM>
+GDN_DEV void gram_tile(SM& sm, bool isq, int i, int j, int lane) {
   typedef Mfma<O> M;
-  constexpr int NTILE = HAS_Q ? 20 : 10;
-  for (int tt = wave; tt < NTILE; tt += NW) {
-    const bool isq = tt >= 10;
-    const int idx = isq ? tt - 10 : tt;
-    const int i = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
-    const int j = idx - i * (i + 1) / 2;
-    floatx4 acc = zero4();
-    const O* A = isq ? sm.q : sm.k;
+  floatx4 acc = zero4();
+  const O* A = isq ? sm.q : sm.k;
 #pragma unroll
-    for (int s = 0; s < DK / M::KSTEP; s++)
-      M::mma(acc, M::load(A, SM::LDK, 16 * i, s * M::KSTEP, lane),
-             M::load(sm.k, SM::LDK, 16 * j, s * M::KSTEP, lane));
-    const int col = 16 * j + (lane & 15);
-    const int rb = 16 * i + 4 * (lane >> 4);
-    const float Gc = sm.G[col];
+  for (int s = 0; s < DK / M::KSTEP; s++)
+    M::mma(acc, M::load(A, SM::LDK, 16 * i, s * M::KSTEP, lane),
+           M::load(sm.k, SM::LDK, 16 * j, s * M::KSTEP, lane));
+  const int col = 16 * j + (lane & 15);
+  const int rb = 16 * i + 4 * (lane >> 4);
+  const float Gc = sm.G[col];
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      const int row = rb + jj;
-      const float dec = row >= col ? __expf(sm.G[row] - Gc) : 0.f;
-      if (!isq) {
-        sm.L[row * SM::LDF + col] = row > col ? sm.beta[row] * acc[jj] * dec : 0.f;
-      } else {
-        sm.p[row * SM::LDT + col] = from_f<O>(acc[jj] * dec);
-      }
+  for (int jj = 0; jj < 4; jj++) {
+    const int row = rb + jj;
+    const float dec = row >= col ? __expf(sm.G[row] - Gc) : 0.f;
+    if (!isq) {
+      sm.L[row * SM::LDF + col] = row > col ? acc[jj] * dec : 0.f;
+    } else {
+      sm.p[row * SM::LDT + col] = from_f<O>(acc[jj] * dec);
     }
+  }
+}
+
+GDN_DEV void lower_tile_ij(int idx, int& i, int& j) {
+  i = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+  j = idx - i * (i + 1) / 2;
+}
+
+// L tiles (all waves).
+template <typename O, int DK, int NW, class SM>
+GDN_DEV void gram_kk(SM& sm, int wave, int lane) {
+  for (int t = wave; t < 10; t += NW) {
+    int i, j;
+    lower_tile_ij(t, i, j);
+    gram_tile<O, DK>(sm, false, i, j, lane);
   }
 }
 
@@ -209,26 +219,39 @@ GDN_DEV void zero_upper(SM& sm, int tid) {
   }
 }
 
-// T = (I + L)^-1 into sm.Tm.  Needs a barrier before (L complete); ends with
-// a barrier.
-template <int NW, class SM>
+// T = (I + L)^-1 into sm.Tm; with HAS_Q the P tiles are formed by the waves
+// that do not invert.  Needs a barrier before (L complete); ends with one.
+template <typename O, int DK, int NW, bool HAS_Q, class SM>
 GDN_DEV void solve(SM& sm, int wave, int lane) {
   constexpr int LDF = SM::LDF;
   if (wave == 0) {
-    // diagonal blocks: lane (b, j) computes column j of (I + L_bb)^-1
+    // diagonal blocks: lane (b, j) computes column j of (I + L_bb)^-1 by
+    // column-oriented substitution (x_m final after step m)
     const int b = lane >> 4, j = lane & 15;
     const float* Lb = sm.L + (16 * b) * LDF + 16 * b;
+    const float* bb = sm.beta + 16 * b;
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      float s = (i == j) ? 1.f : 0.f;
+    for (int i = 0; i < 16; i++) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; m++) s -= Lb[i * LDF + m] * x[m];
-      x[i] = s;
+    for (int m = 0; m < 15; m++) {
+#pragma unroll
+      for (int i = m + 1; i < 16; i++) x[i] -= bb[i] * Lb[i * LDF + m] * x[m];
     }
     float* Tb = sm.Tm + (16 * b) * LDF + 16 * b;
 #pragma unroll
     for (int i = 0; i < 16; i++) Tb[i * LDF + j] = x[i];
+  }
+  if constexpr (HAS_Q) {
+    // P tiles on the other waves (or wave 0 alone when there is one wave)
+    constexpr int WP = NW > 1 ? NW - 1 : 1;
+    const int wp = NW > 1 ? wave - 1 : 0;
+    if (NW == 1 || wave > 0)
+      for (int t = wp; t < 10; t += WP) {
+        int i, j;
+        lower_tile_ij(t, i, j);
+        gram_tile<O, DK>(sm, true, i, j, lane);
+      }
   }
   __syncthreads();
   // off-diagonal blocks, by distance d = i - j
@@ -236,14 +259,11 @@ GDN_DEV void solve(SM& sm, int wave, int lane) {
     for (int blk = wave; blk < 4 - d; blk += NW) {
       const int j = blk, i = blk + d;
       floatx4 r = zero4();
+      const float brow = sm.beta[16 * i + (lane & 15)];  // L = diag(beta) (kh kh^T o Gamma)
       for (int m = j; m < i; m++) {
-        // A = L_im (rows 16i, cols 16m), B = T_mj read as B[k][n] = Tm[16m+k][16j+n]
-        const floatx4 a = Mfma<float>::load(sm.L, LDF, 16 * i, 16 * m, lane);
-        const int kb = 16 * m + 4 * (lane >> 4), n = 16 * j + (lane & 15);
-        floatx4 bfr;
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) bfr[jj] = sm.Tm[(kb + jj) * LDF + n];
-        Mfma<float>::mma(r, a, bfr);
+        // A = L_im (rows 16i, cols 16m); B[k][n] = Tm[16m+k][16j+n]
+        Mfma<float>::mma(r, Mfma<float>::load(sm.L, LDF, 16 * i, 16 * m, lane) * brow,
+                         Mfma<float>::load_col(sm.Tm + 16 * m * LDF, LDF, 16 * j, 0, lane));
       }
       // T_ij = -T_ii r  (r is already in B layout: its rows are k)
       floatx4 o = zero4();
@@ -262,23 +282,22 @@ template <typename O, class SM>
 GDN_DEV void compute_u(const SM& sm, int vc0, int lane, floatx4 (&u)[4][2]) {
   typedef Mfma<O> M;
   constexpr int NS = BT / M::KSTEP;
-  typename M::frag a[4][NS];
+  typename M::frag b[2][NS];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
+  for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-    for (int s = 0; s < NS; s++) a[mt][s] = M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.beta, lane);
+    for (int s = 0; s < NS; s++) b[nt][s] = M::load_col(sm.v, SM::LDV, vc0 + 16 * nt, s * M::KSTEP, lane);
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++) {
-    typename M::frag b[NS];
+  for (int mt = 0; mt < 4; mt++) {
+    floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-    for (int s = 0; s < NS; s++) b[s] = M::load(sm.vt, SM::LDT, vc0 + 16 * nt, s * M::KSTEP, lane);
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
-      floatx4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < NS; s++) M::mma(acc, a[mt][s], b[s]);
-      u[mt][nt] = acc;
+    for (int s = 0; s < NS; s++) {
+      const typename M::frag a = M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.beta, lane);
+      M::mma(acc0, a, b[0][s]);
+      M::mma(acc1, a, b[1][s]);
     }
+    u[mt][0] = acc0;
+    u[mt][1] = acc1;
   }
 }
 
@@ -294,7 +313,7 @@ GDN_DEV void compute_w(SM& sm, int wave, int lane) {
 #pragma unroll
     for (int s = 0; s < NS; s++)
       M::mma(acc, M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.bg, lane),
-             M::load(sm.kt, SM::LDT, 16 * nt, s * M::KSTEP, lane));
+             M::load_col(sm.k, SM::LDK, 16 * nt, s * M::KSTEP, lane));
     const int rb = 16 * mt + 4 * (lane >> 4), c = 16 * nt + (lane & 15);
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) sm.w[(rb + jj) * SM::LDK + c] = from_f<O>(acc[jj]);

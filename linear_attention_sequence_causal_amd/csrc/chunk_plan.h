@@ -1,0 +1,159 @@
+// chunk_plan.h -- device-side work lists of the chunk kernels (no host sync).
+//
+// From cu_seqlens one workgroup derives, for every sequence n (each chunked
+// in 64-token chunks from its own start):
+//   * its segments: runs of `seg_len` tokens handled by one workgroup each
+//     (table[s] = {n, token begin, token end, first/last flags}, seg_chunk0[s]
+//     = global index of the segment's first chunk);
+//   * seq_off[n] / seq_nseg[n]: its first segment and segment count;
+//   * seq_chunk_off[n]: the global index of its first chunk;
+//   * chunk_tab[c] = {chunk begin token, end token of its sequence, n}.
+// Counts go to counts[0] (segments) and counts[1] (chunks).  Capacities are
+// host-side upper bounds (T / seg_len + N segments, T / 64 + N chunks); the
+// kernels size their grids by them and exit past the counts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "gdn_internal.h"
+
+namespace gdn_chunk {
+
+constexpr int kFirst = 1, kLast = 2;
+
+struct PlanPtrs {
+  int32_t* counts;  // [2]
+  int4* table;      // [seg_cap]
+  int32_t* seg_chunk0;
+  int32_t* seq_off;
+  int32_t* seq_nseg;
+  int32_t* seq_chunk_off;
+  int4* chunk_tab;  // [chunk_cap] (may be null)
+};
+
+namespace {
+
+__device__ __forceinline__ int block_excl_scan256(int v, int* buf, int* total) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = t >= off ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const int incl = buf[t];
+  *total = buf[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int N, int64_t T,
+                                                   int seg_len, int seg_cap, int chunk_cap,
+                                                   PlanPtrs pp) {
+  __shared__ int buf[256];
+  const int t = threadIdx.x;
+  int run_seg = 0, run_chunk = 0;
+  for (int base = 0; base < N; base += 256) {
+    const int n = base + t;
+    int64_t s = 0, e = 0;
+    int ns = 0, nc = 0;
+    if (n < N) {
+      s = cu[n];
+      e = cu[n + 1];
+      s = s < 0 ? 0 : (s > T ? T : s);
+      e = e < s ? s : (e > T ? T : e);
+      ns = (int)((e - s + seg_len - 1) / seg_len);
+      nc = (int)((e - s + 63) / 64);
+    }
+    int tot_s = 0, tot_c = 0;
+    const int off_s = run_seg + block_excl_scan256(ns, buf, &tot_s);
+    const int off_c = run_chunk + block_excl_scan256(nc, buf, &tot_c);
+    if (n < N) {
+      pp.seq_off[n] = off_s;
+      pp.seq_nseg[n] = ns;
+      pp.seq_chunk_off[n] = off_c;
+      for (int p = 0; p < ns && off_s + p < seg_cap; p++) {
+        const int64_t a = s + (int64_t)p * seg_len;
+        const int64_t b = a + seg_len < e ? a + seg_len : e;
+        pp.table[off_s + p] =
+            make_int4(n, (int)a, (int)b, (p == 0 ? kFirst : 0) | (p == ns - 1 ? kLast : 0));
+        pp.seg_chunk0[off_s + p] = off_c + p * (seg_len / 64);
+      }
+      if (pp.chunk_tab)
+        for (int c = 0; c < nc && off_c + c < chunk_cap; c++)
+          pp.chunk_tab[off_c + c] = make_int4((int)(s + 64 * c), (int)e, n, 0);
+    }
+    run_seg += tot_s;
+    run_chunk += tot_c;
+  }
+  if (t == 0) {
+    pp.counts[0] = run_seg < seg_cap ? run_seg : seg_cap;
+    pp.counts[1] = run_chunk < chunk_cap ? run_chunk : chunk_cap;
+  }
+}
+
+}  // namespace
+
+// Host-side layout of the plan inside a workspace.
+struct Plan {
+  int64_t seg_len;
+  int64_t seg_cap, chunk_cap;
+  bool split;  // some sequence may have more than one segment
+  size_t off_counts, off_table, off_seg_chunk0, off_seq_off, off_seq_nseg, off_seq_chunk_off,
+      off_chunk_tab, off_state, off_init, end;
+
+  PlanPtrs ptrs(char* ws, bool with_chunks) const {
+    PlanPtrs p;
+    p.counts = reinterpret_cast<int32_t*>(ws + off_counts);
+    p.table = reinterpret_cast<int4*>(ws + off_table);
+    p.seg_chunk0 = reinterpret_cast<int32_t*>(ws + off_seg_chunk0);
+    p.seq_off = reinterpret_cast<int32_t*>(ws + off_seq_off);
+    p.seq_nseg = reinterpret_cast<int32_t*>(ws + off_seq_nseg);
+    p.seq_chunk_off = reinterpret_cast<int32_t*>(ws + off_seq_chunk_off);
+    p.chunk_tab = with_chunks ? reinterpret_cast<int4*>(ws + off_chunk_tab) : nullptr;
+    return p;
+  }
+};
+
+// seg_chunks: chunks per segment (0 = pick from the device size and the
+// number of (sequence, head) chains; GDN_SEG_CHUNKS overrides for tuning).
+inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) {
+  Plan p{};
+  const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
+  int64_t per = 1;
+  const char* env = getenv("GDN_SEG_CHUNKS");
+  if (env && atoi(env) > 0) {
+    per = atoi(env);
+  } else {
+    const int64_t cus = gdn::device_cu_count();
+    per = (chunks * Hv + cus - 1) / cus;  // chunks per workgroup for one wave of the GPU
+    if (per < 1) per = 1;
+  }
+  p.seg_len = per * 64;
+  p.split = p.seg_len < T;
+  p.seg_cap = T / p.seg_len + N + 1;
+  p.chunk_cap = chunks + 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = gdn::round_up(o + bytes, 256);
+    return at;
+  };
+  p.off_counts = take(8);
+  p.off_table = take(sizeof(int4) * (size_t)p.seg_cap);
+  p.off_seg_chunk0 = take(4 * (size_t)p.seg_cap);
+  p.off_seq_off = take(4 * (size_t)N);
+  p.off_seq_nseg = take(4 * (size_t)N);
+  p.off_seq_chunk_off = take(4 * (size_t)N);
+  p.off_chunk_tab = take(sizeof(int4) * (size_t)p.chunk_cap);
+  p.off_state = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * (dk + dv) : 0);
+  p.off_init = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * dv : 0);
+  p.end = o;
+  return p;
+}
+
+}  // namespace gdn_chunk

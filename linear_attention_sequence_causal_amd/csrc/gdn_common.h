@@ -92,6 +92,56 @@ template <> struct Mfma<bf16> {
     }
     return f;
   }
+  // same from an fp32 [rows][ld] array (e.g. a state in global memory)
+  GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, int lane) {
+    const float* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    floatx4 lo = *reinterpret_cast<const floatx4*>(p);
+    floatx4 hi = *reinterpret_cast<const floatx4*>(p + 16);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = (bf16)lo[j];
+      f[4 + j] = (bf16)hi[j];
+    }
+    return f;
+  }
+  // column access: element (k, c0 + l%16) of a [K][ld] array, k in the
+  // convention's order -- an operand whose contraction index runs down rows
+  GDN_DEV static frag load_col(const bf16* base, int ld, int c0, int k0, int lane) {
+    const bf16* p = base + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = p[j * ld];
+      f[4 + j] = p[(16 + j) * ld];
+    }
+    return f;
+  }
+  GDN_DEV static frag load_col_f32(const float* base, int ld, int c0, int k0, const float* sc,
+                                   int lane) {
+    const int kk = k0 + 4 * (lane >> 4);
+    const float* p = base + kk * ld + c0 + (lane & 15);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = (bf16)(sc ? p[j * ld] * sc[kk + j] : p[j * ld]);
+      f[4 + j] = (bf16)(sc ? p[(16 + j) * ld] * sc[kk + 16 + j] : p[(16 + j) * ld]);
+    }
+    return f;
+  }
+  // column access with element k scaled by sc[k]
+  GDN_DEV static frag load_col_scaled(const bf16* base, int ld, int c0, int k0, const float* sc,
+                                      int lane) {
+    const int kk = k0 + 4 * (lane >> 4);
+    const bf16* p = base + kk * ld + c0 + (lane & 15);
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f[j] = (bf16)((float)p[j * ld] * sc[kk + j]);
+      f[4 + j] = (bf16)((float)p[(16 + j) * ld] * sc[kk + 16 + j]);
+    }
+    return f;
+  }
   // B fragment from accumulator tiles of k-tiles 2s and 2s+1
   GDN_DEV static frag from_acc(const floatx4& c0, const floatx4& c1) {
     frag f;
@@ -121,6 +171,25 @@ template <> struct Mfma<float> {
     floatx4 s = *reinterpret_cast<const floatx4*>(sc + kk);
     return a * s;
   }
+  GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, int lane) {
+    return load(base, ld, row0, k0, lane);
+  }
+  GDN_DEV static frag load_col(const float* base, int ld, int c0, int k0, int lane) {
+    const float* p = base + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+    return frag{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
+  GDN_DEV static frag load_col_scaled(const float* base, int ld, int c0, int k0, const float* sc,
+                                      int lane) {
+    return load_col_f32(base, ld, c0, k0, sc, lane);
+  }
+  GDN_DEV static frag load_col_f32(const float* base, int ld, int c0, int k0, const float* sc,
+                                   int lane) {
+    const int kk = k0 + 4 * (lane >> 4);
+    const float* p = base + kk * ld + c0 + (lane & 15);
+    frag f{p[0], p[ld], p[2 * ld], p[3 * ld]};
+    if (sc) f *= *reinterpret_cast<const floatx4*>(sc + kk);
+    return f;
+  }
   GDN_DEV static frag from_acc(const floatx4& c0) { return c0; }
   GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
@@ -128,18 +197,6 @@ template <> struct Mfma<float> {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
   }
-};
-
-// B fragment for k-step s taken from accumulator tiles indexed by k-tile
-// (tiles[kt] is the C tile whose rows are k-tile kt).
-template <typename O> struct AccToB;
-template <> struct AccToB<bf16> {
-  template <typename F>
-  GDN_DEV static Mfma<bf16>::frag get(F tile, int s) { return Mfma<bf16>::from_acc(tile(2 * s), tile(2 * s + 1)); }
-};
-template <> struct AccToB<float> {
-  template <typename F>
-  GDN_DEV static Mfma<float>::frag get(F tile, int s) { return Mfma<float>::from_acc(tile(s)); }
 };
 
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }

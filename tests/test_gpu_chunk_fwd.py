@@ -94,7 +94,7 @@ def test_empty_sequences_return_initial_state():
                               h0=h0.cuda())
     assert torch.equal(ht[0].cpu(), h0[0]) and torch.equal(ht[2].cpu(), h0[2])
     # T = 0
-    y0 = torch.empty(0, 128, device="cuda")
+    y0 = torch.empty(0, 96, device="cuda")
     o, ht = gdn.gdn_chunk_fwd(y0, torch.empty(0, 1, device="cuda"), torch.empty(0, 1, device="cuda"),
                               cu_tensor([0, 0]), 1, 1, 32, 32, h0=h0[:1].cuda())
     assert o.shape == (0, 1, 32) and torch.equal(ht.cpu(), h0[:1])
