@@ -4,12 +4,22 @@
 // hyper-parallel "linear_attention_context_parallel.py":
 // _run_prepared_gdn_chunks (per chunk: v_new = u - w S;
 // o = (qh o e^G) S + P v_new; S <- e^{G_C} S + (kh o e^{G_C - G})^T v_new),
-// with the chunk preparation of chunk_common.h, per sequence of cu_seqlens.
+// per sequence of cu_seqlens.
 //
 // A workgroup owns one (segment, value head): a run of whole 64-token chunks
 // of one sequence, processed in order with the [dk, dv] fp32 state resident
 // in registers (each wave holds 32 state columns as MFMA accumulator tiles,
-// which feed the next products directly).  When there are too few
+// which feed the next products directly).
+//
+// Per chunk the page forms u = T diag(beta) v and w = T diag(beta e^G) kh
+// (T = (I + L)^-1) and then v_new = u - w S.  By linearity
+//   v_new = T diag(beta) (v - diag(e^G) kh S),
+// so each wave solves for its own state columns directly: kh S is one
+// product, and T is applied by blocked forward substitution over the four
+// 16-token block rows, x_i <- D_i (x_i - diag(beta_i) sum_{m<i} L_im x_m),
+// with the inverted diagonal blocks D_i -- no T, u or w is ever formed and
+// nothing of it passes through LDS.  q and k are staged raw; the l2norm and
+// the q scale enter as per-row factors of the products.  When there are too few
 // (sequence, head) chains to fill the GPU, sequences are cut into segments
 // and the page's affine state summaries make the segments independent
 // (_compute_gdn_state_summary_from_prepared,
@@ -59,6 +69,32 @@ struct LoopArgs {
   float* states;     // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk
 };
 
+// LDS of the chunk loop (one chunk of one head at a time; rows padded by
+// 16 bytes).  q, k are the raw rows (l2norm enters as per-row factors), v the
+// raw values (later the staged output), p the decayed q k^T, L the strict
+// lower kh kh^T o Gamma in fp32 whose diagonal 16x16 blocks are replaced by
+// D_b = (I + diag(beta) L_bb)^-1.
+template <typename O, int DK, int DV, bool HAS_Q>
+struct LoopSmem {
+  static constexpr int PAD = 16 / (int)sizeof(O);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDV = DV + PAD;
+  static constexpr int LDP = BT + PAD;
+  static constexpr int LDF = BT + 4;
+  // small per-row arrays first: ds_read/ds_write immediate offsets reach
+  // 64 KiB, so everything addressed per row stays within reach of one base
+  alignas(16) float G[BT];
+  alignas(16) float beta[BT];
+  alignas(16) float eg[BT];  // exp(G)
+  alignas(16) float rq[BT];  // scale / |q| (scale without l2norm)
+  alignas(16) float rk[BT];  // 1 / |k| (1 without l2norm)
+  alignas(16) float L[BT * LDF];
+  alignas(16) O p[HAS_Q ? BT * LDP : 8];
+  alignas(16) O k[BT * LDK];
+  alignas(16) O q[HAS_Q ? BT * LDK : 8];
+  alignas(16) O v[BT * LDV];
+};
+
 template <typename E, int DK, int DV, int MODE>
 struct LoopCfg {
   typedef E O;  // operand type equals the activation type (bf16 or fp32)
@@ -66,15 +102,120 @@ struct LoopCfg {
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
   static constexpr int NW = NSC / 32;
   static constexpr int NT = NW * 64;
-  typedef Smem<O, DK, DV, HAS_Q> SM;
+  typedef LoopSmem<O, DK, DV, HAS_Q> SM;
   typedef Prefetch<E, DK, DV, NT, HAS_Q> PF;
 };
 
+// Register prefetch -> LDS as raw rows, plus the per-row l2norm factors and
+// the in-chunk cumsum of g.  Rows past the sequence end are zero.
+template <typename E, int DK, int DV, int NT, bool HAS_Q, class SM>
+GDN_DEV void stage_raw(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale, int use_l2norm,
+                       int tid) {
+  typedef Prefetch<E, DK, DV, NT, HAS_Q> PF;
+  typedef typename Vec16<E>::type V16;
+  constexpr int VE = PF::VE;
+#pragma unroll
+  for (int p = 0; p < PF::PQ; p++) {
+    const int i = tid + NT * p;
+    const int row = i / PF::QPR, vi = i % PF::QPR;
+    float kss = 0.f, qss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; e++) {
+      const float kf = to_f(pf.k[p][e]);
+      kss += kf * kf;
+      if constexpr (HAS_Q) {
+        const float qf = to_f(pf.q[p][e]);
+        qss += qf * qf;
+      }
+    }
+    kss = group_sum<PF::QPR>(kss);
+    if constexpr (HAS_Q) qss = group_sum<PF::QPR>(qss);
+    if (i < PF::QV) {
+      *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vi * VE) = pf.k[p];
+      if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vi * VE) = pf.q[p];
+      if (vi == 0) {
+        sm.rk[row] = use_l2norm ? __builtin_amdgcn_rsqf(kss + 1e-6f) : 1.f;
+        if constexpr (HAS_Q) sm.rq[row] = use_l2norm ? scale * __builtin_amdgcn_rsqf(qss + 1e-6f) : scale;
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF::PV; p++) {
+    const int i = tid + NT * p;
+    const int row = i / PF::VPR, vi = i % PF::VPR;
+    if (i < PF::VV) *reinterpret_cast<V16*>(sm.v + row * SM::LDV + vi * VE) = pf.v[p];
+  }
+  if (tid < BT) {  // wave 0: inclusive scan of g over the 64 rows
+    float G = pf.g;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(G, off, 64);
+      if (tid >= off) G += o;
+    }
+    sm.G[tid] = G;
+    sm.beta[tid] = pf.beta;
+    sm.eg[tid] = __expf(G);
+  }
+}
+
+// Lower 16x16 tile (i, j) of k k^T (-> L) or q k^T (-> P) from raw rows, with
+// the l2norm factors and the decay exp(G_r - G_c).
+template <typename O, int DK, class SM>
+GDN_DEV void gram_tile_raw(SM& sm, bool isq, int i, int j, int lane) {
+  typedef Mfma<O> M;
+  floatx4 acc = zero4();
+  const O* A = isq ? sm.q : sm.k;
+#pragma unroll
+  for (int s = 0; s < DK / M::KSTEP; s++)
+    M::mma(acc, M::load(A, SM::LDK, 16 * i, s * M::KSTEP, lane),
+           M::load(sm.k, SM::LDK, 16 * j, s * M::KSTEP, lane));
+  const int col = 16 * j + (lane & 15);
+  const int rb = 16 * i + 4 * (lane >> 4);
+  const float Gc = sm.G[col], rc = sm.rk[col];
+#pragma unroll
+  for (int jj = 0; jj < 4; jj++) {
+    const int row = rb + jj;
+    const float dec = row >= col ? __expf(sm.G[row] - Gc) : 0.f;
+    if (!isq) {
+      sm.L[row * SM::LDF + col] = row > col ? acc[jj] * sm.rk[row] * rc * dec : 0.f;
+    } else {
+      sm.p[row * SM::LDP + col] = from_f<O>(acc[jj] * sm.rq[row] * rc * dec);
+    }
+  }
+}
+
+// Column j of D_b = (I + diag(beta_b) L_bb)^-1 by column-oriented forward
+// substitution, written over L_bb.
+template <class SM>
+GDN_DEV void invert_diag_block(SM& sm, int b, int j) {
+  constexpr int LDF = SM::LDF;
+  float* Lb = sm.L + (16 * b) * LDF + 16 * b;
+  const float* bb = sm.beta + 16 * b;
+  // keep the unit vector's construction inside the chunk loop (hoisted, it
+  // would pin 16 registers for the whole kernel)
+  int jj;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(jj) : "v"(j));
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) x[i] = (i == jj) ? 1.f : 0.f;
+#pragma unroll
+  for (int m = 0; m < 15; m++) {
+#pragma unroll
+    for (int i = m + 1; i < 16; i++) x[i] -= bb[i] * Lb[i * LDF + m] * x[m];
+  }
+#pragma unroll
+  // Lanes of one wave run in lockstep: every read of the block above is
+  // issued before these writes.
+  for (int i = 0; i < 16; i++) Lb[i * LDF + j] = x[i];
+}
+
 template <typename E, int DK, int DV, int MODE>
-__global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_kernel(LoopArgs a) {
+__global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+void chunk_loop_kernel(LoopArgs a) {
   typedef LoopCfg<E, DK, DV, MODE> CF;
   typedef typename CF::O O;
   typedef Mfma<O> M;
+  typedef Tile16<O> T16;
   constexpr int NW = CF::NW, NT = CF::NT;
   constexpr int KS = M::KSTEP;
   constexpr int NSK = DK / KS;  // contraction steps over dk
@@ -92,12 +233,12 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
   const int64_t tb = ent.y, te = ent.z;
   const int Hv = a.Hv;
   const int qa = h / (Hv / a.Hk);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int g4 = lane >> 4, ln = lane & 15;
   const int c0 = wave * 32;                        // first state column of this wave
-  const bool mcol = MODE == kSummary && c0 < DK;   // wave holds columns of M (u = 0)
+  const bool mcol = MODE == kSummary && c0 < DK;   // wave holds columns of M (v = 0)
   const int vc0 = MODE == kSummary ? c0 - DK : c0; // value column of the wave's first column
-
-  zero_upper<O, CF::HAS_Q, NT>(sm, tid);
 
   // state tiles S[mt][nt]: rows 16mt + 4(lane/16) + j, cols c0 + 16nt + lane%16
   floatx4 S[DKT][2];
@@ -113,13 +254,19 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
       for (int nt = 0; nt < 2; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int row = 16 * mt + 4 * (lane >> 4) + j, col = c0 + 16 * nt + (lane & 15);
+          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
           float v = 0.f;
           if (mcol) v = (row == col) ? 1.f : 0.f;
           else if (src) v = src[row * DV + col];
           S[mt][nt][j] = v;
         }
   }
+  // upper tiles of P stay zero
+  if constexpr (OUT)
+    for (int e = tid; e < BT * BT; e += NT) {
+      const int r = e / BT, c = e % BT;
+      if ((c >> 4) > (r >> 4)) sm.p[r * SM::LDP + c] = from_f<O>(0.f);
+    }
 
   const E* qp = (const E*)a.q + (int64_t)qa * DK;
   const E* kp = (const E*)a.k + (int64_t)qa * DK;
@@ -132,9 +279,14 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
 
   for (int c = 0; c < nchunks; c++) {
     const int64_t tc = tb + (int64_t)c * BT;
+    // Lane-dependent addresses are rebuilt every chunk from an opaque copy of
+    // the thread index: hoisted out of the loop they would pin dozens of
+    // registers for its whole length.
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
     __syncthreads();  // the previous chunk's LDS readers are done
-    stage<E, O, DK, DV, NT, CF::HAS_Q>(sm, pf, a.scale, a.use_l2norm, tid);
-    if (c + 1 < nchunks) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tc + BT, te, tid);
+    stage_raw<E, DK, DV, NT, CF::HAS_Q>(sm, pf, a.scale, a.use_l2norm, tid_c);
     if constexpr (MODE == kStates) {
       // the state entering this chunk, for the backward
       float* dst = a.states + ((int64_t)(a.seg_chunk0[seg] + c) * Hv + h) * DK * DV;
@@ -144,82 +296,123 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
         for (int nt = 0; nt < 2; nt++)
 #pragma unroll
           for (int j = 0; j < 4; j++)
-            dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] = S[mt][nt][j];
+            dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
     }
     __syncthreads();
-    gram_kk<O, DK, NW>(sm, wave, lane);
+    // L (and P) tiles
+    {
+      constexpr int NTILE = OUT ? 20 : 10;
+#pragma unroll 1
+      for (int t = wave; t < NTILE; t += NW) {
+        int i, j;
+        lower_tile_ij(t % 10, i, j);
+        gram_tile_raw<O, DK>(sm, t >= 10, i, j, lane);
+      }
+    }
     __syncthreads();
-    solve<O, DK, NW, CF::HAS_Q>(sm, wave, lane);  // P tiles too; ends with a barrier
+    // D_b = (I + diag(beta) L_bb)^-1, one 16-lane group per block
+    if (NW >= 4) {
+      if (wave < 4 && lane < 16) invert_diag_block(sm, wave, lane);
+    } else if (wave == 0) {
+      invert_diag_block(sm, g4, ln);
+    }
 
-    floatx4 u[4][2];
-    if (!mcol) compute_u<O>(sm, vc0, lane, u);
-    compute_w<O, DK, NW>(sm, wave, lane);
-    __syncthreads();
-
-    // v_new = u - w S
-    typename M::frag sb[NSK][2];
-#pragma unroll
-    for (int s = 0; s < NSK; s++)
-#pragma unroll
-      for (int nt = 0; nt < 2; nt++) sb[s][nt] = acc_as_b<O>(S, s, nt);
-    floatx4 vn[4][2];
+    // (k S) for this wave's columns
+    floatx4 x[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
-      floatx4 acc0 = zero4(), acc1 = zero4();
+      floatx4 k0 = zero4(), k1 = zero4();
 #pragma unroll
       for (int s = 0; s < NSK; s++) {
-        const typename M::frag wf = M::load(sm.w, SM::LDK, 16 * mt, s * KS, lane);
-        M::mma(acc0, wf, sb[s][0]);
-        M::mma(acc1, wf, sb[s][1]);
+        const typename M::frag kf = M::load(sm.k, SM::LDK, 16 * mt, s * KS, lane);
+        M::mma(k0, kf, acc_as_b<O>(S, s, 0));
+        M::mma(k1, kf, acc_as_b<O>(S, s, 1));
       }
-      vn[mt][0] = mcol ? -acc0 : u[mt][0] - acc0;
-      vn[mt][1] = mcol ? -acc1 : u[mt][1] - acc1;
+      // right-hand side beta o (v - exp(G) o (kh S))
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * mt + 4 * g4 + j;
+        const float bt = sm.beta[row], gk = sm.eg[row] * sm.rk[row];
+        const float v0 = mcol ? 0.f : to_f(sm.v[row * SM::LDV + vc0 + ln]);
+        const float v1 = mcol ? 0.f : to_f(sm.v[row * SM::LDV + vc0 + 16 + ln]);
+        x[mt][0][j] = bt * (v0 - gk * k0[j]);
+        x[mt][1][j] = bt * (v1 - gk * k1[j]);
+      }
+    }
+    __syncthreads();  // D blocks written; v reads done
+    // S's operand copy is rebuilt from the accumulators for (q S) below; kept
+    // live through the solve it would cost 32 registers
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++) asm volatile("" : "+v"(S[mt][nt]));
+
+    // v_new = (I + diag(beta) L)^-1 rhs, block rows in order:
+    // x_i <- D_i (x_i - diag(beta_i) sum_{m<i} L_im x_m)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int m = 0; m < i; m++) {
+        const float nb = -sm.beta[16 * i + ln];
+        const typename T16::frag lf = T16::load_f32(sm.L, SM::LDF, 16 * i, 16 * m, nb, lane);
+        T16::mma(x[i][0], lf, T16::from_acc(x[m][0]));
+        T16::mma(x[i][1], lf, T16::from_acc(x[m][1]));
+      }
+      const typename T16::frag df = T16::load_f32(sm.L, SM::LDF, 16 * i, 16 * i, 1.f, lane);
+      floatx4 y0 = zero4(), y1 = zero4();
+      T16::mma(y0, df, T16::from_acc(x[i][0]));
+      T16::mma(y1, df, T16::from_acc(x[i][1]));
+      x[i][0] = y0;
+      x[i][1] = y1;
     }
 
     const float GC = sm.G[BT - 1];
     if constexpr (OUT) {
-      // o = e^G o (qh S) + P v_new, staged in LDS over v (free after the
-      // barrier above) and written below as whole 16-byte row pieces
+      // o = (rq e^G) o (q S) + P v_new, staged over v, written below as whole
+      // 16-byte row pieces
       O* so = sm.v;
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
+        const int rb = 16 * mt + 4 * g4;
         floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
         for (int s = 0; s < NSK; s++) {
           const typename M::frag qf = M::load(sm.q, SM::LDK, 16 * mt, s * KS, lane);
-          M::mma(acc0, qf, sb[s][0]);
-          M::mma(acc1, qf, sb[s][1]);
+          M::mma(acc0, qf, acc_as_b<O>(S, s, 0));
+          M::mma(acc1, qf, acc_as_b<O>(S, s, 1));
         }
-        const int rb = 16 * mt + 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const float eg = sm.eg[rb + j];
-          acc0[j] *= eg;
-          acc1[j] *= eg;
+          const float f = sm.eg[rb + j] * sm.rq[rb + j];
+          acc0[j] *= f;
+          acc1[j] *= f;
         }
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
-          const typename M::frag pfrag = M::load(sm.p, SM::LDT, 16 * mt, s * KS, lane);
-          M::mma(acc0, pfrag, acc_as_b<O>(vn, s, 0));
-          M::mma(acc1, pfrag, acc_as_b<O>(vn, s, 1));
+          const typename M::frag pfrag = M::load(sm.p, SM::LDP, 16 * mt, s * KS, lane);
+          M::mma(acc0, pfrag, acc_as_b<O>(x, s, 0));
+          M::mma(acc1, pfrag, acc_as_b<O>(x, s, 1));
         }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          so[(rb + j) * SM::LDV + c0 + (lane & 15)] = from_f<O>(acc0[j]);
-          so[(rb + j) * SM::LDV + c0 + 16 + (lane & 15)] = from_f<O>(acc1[j]);
+          so[(rb + j) * SM::LDV + c0 + ln] = from_f<O>(acc0[j]);
+          so[(rb + j) * SM::LDV + c0 + 16 + ln] = from_f<O>(acc1[j]);
         }
       }
     }
 
-    // S <- e^{G_C} S + kh^T (e^{G_C - G} o v_new)
+    // the next chunk's rows, in flight during the state update
+    if (c + 1 < nchunks) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tc + BT, te, tid_c);
+
+    // S <- e^{G_C} S + k^T (rk e^{G_C - G} o v_new)
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
-      const int rb = 16 * mt + 4 * (lane >> 4);
+      const int rb = 16 * mt + 4 * g4;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const float d = __expf(GC - sm.G[rb + j]);
-        vn[mt][0][j] *= d;
-        vn[mt][1][j] *= d;
+        const float d = sm.rk[rb + j] * __expf(GC - sm.G[rb + j]);
+        x[mt][0][j] *= d;
+        x[mt][1][j] *= d;
       }
     }
     const float eC = __expf(GC);
@@ -227,7 +420,7 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
 #pragma unroll
     for (int s = 0; s < NSB; s++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++) vb[s][nt] = acc_as_b<O>(vn, s, nt);
+      for (int nt = 0; nt < 2; nt++) vb[s][nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++) {
       floatx4 acc0 = S[mt][0] * eC, acc1 = S[mt][1] * eC;
@@ -247,7 +440,7 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
       constexpr int VE = Vec16<E>::N;
       constexpr int OPR = DV / VE;
       E* op = (E*)a.o + (int64_t)h * DV;
-      for (int i = tid; i < BT * OPR; i += NT) {
+      for (int i = tid_c; i < BT * OPR; i += NT) {
         const int row = i / OPR, vi = i % OPR;
         const int64_t t = tc + row;
         if (t < te)
@@ -273,7 +466,7 @@ __global__ __launch_bounds__((LoopCfg<E, DK, DV, MODE>::NT)) void chunk_loop_ker
       for (int nt = 0; nt < 2; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int row = 16 * mt + 4 * (lane >> 4) + j, col = c0 + 16 * nt + (lane & 15);
+          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
           dst[row * ld + col] = S[mt][nt][j];
         }
   }

@@ -23,23 +23,27 @@ namespace {
 
 constexpr int kRunsPerBlock = 4;   // blockDim.y
 constexpr int kLanes = 64;         // blockDim.x: channel vectors per block
-constexpr int kFwdRows = 16;       // tokens per thread run, forward
+constexpr int kFwdRows = 8;        // tokens per thread run, forward
 constexpr int kBwdRows = 16;       // tokens per thread run, backward
 constexpr int kBwdMaxSplits = 64;  // token splits of the backward grid (dw partial rows)
 
-// V channels of one row as an aligned vector (V*sizeof(E) == 16) or scalars.
-template <typename E, int V> struct Row {
+// V channels of one row: a packed 16-byte vector when V*sizeof(E) == 16
+// (bf16 stays two to a register), else V scalars.
+template <typename E, int V, bool VEC = (V * sizeof(E) == 16)> struct Row;
+template <typename E, int V> struct Row<E, V, true> {
+  typename Vec16<E>::type v;
+  GDN_DEV float at(int i) const { return to_f(v[i]); }
+};
+template <typename E, int V> struct Row<E, V, false> {
   E v[V];
+  GDN_DEV float at(int i) const { return to_f(v[i]); }
 };
 
 template <typename E, int V>
 __device__ __forceinline__ Row<E, V> load_row(const E* p) {
   Row<E, V> r;
   if constexpr (V * sizeof(E) == 16) {
-    typedef typename Vec16<E>::type VT;
-    VT t = *reinterpret_cast<const VT*>(p);
-#pragma unroll
-    for (int i = 0; i < V; i++) r.v[i] = t[i];
+    r.v = *reinterpret_cast<const typename Vec16<E>::type*>(p);
   } else {
 #pragma unroll
     for (int i = 0; i < V; i++) r.v[i] = p[i];
@@ -64,8 +68,12 @@ __device__ __forceinline__ void store_row(E* p, const float* f) {
 template <typename E, int V>
 __device__ __forceinline__ Row<E, V> zero_row() {
   Row<E, V> r;
+  if constexpr (V * sizeof(E) == 16) {
+    r.v = zero_vec16<E>();
+  } else {
 #pragma unroll
-  for (int i = 0; i < V; i++) r.v[i] = from_f<E>(0.f);
+    for (int i = 0; i < V; i++) r.v[i] = from_f<E>(0.f);
+  }
   return r;
 }
 
@@ -87,20 +95,17 @@ template <typename E, int K, int V>
 __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
     const E* __restrict__ x, const E* __restrict__ w, const E* __restrict__ bias,
     const E* __restrict__ halo, const int32_t* __restrict__ cu, int N, int64_t T, int C,
-    const gdn_cp_meta* __restrict__ meta, E* __restrict__ y) {
+    int cgroups, const gdn_cp_meta* __restrict__ meta, E* __restrict__ y) {
   constexpr int R = kFwdRows;
-  const int c0 = (blockIdx.y * kLanes + threadIdx.x) * V;
-  const int64_t t0 = ((int64_t)blockIdx.x * kRunsPerBlock + threadIdx.y) * R;
+  // channel groups vary fastest so that concurrent blocks cover whole rows
+  const int64_t b = blockIdx.x;
+  const int cg = (int)(b % cgroups);
+  const int64_t tile = b / cgroups;
+  const int c0 = (cg * kLanes + threadIdx.x) * V;
+  const int64_t t0 = (tile * kRunsPerBlock + threadIdx.y) * R;
   if (c0 >= C || t0 >= T) return;
   const int n_halo = (halo && meta) ? meta->n_halo : 0;
 
-  // rows t0-(K-1) .. t0+R-1, loaded up front
-  Row<E, V> xr[R + K - 1];
-#pragma unroll
-  for (int i = 0; i < R + K - 1; i++) {
-    const int64_t tau = t0 - (K - 1) + i;
-    xr[i] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
-  }
   float wv[K][V], bv[V];
 #pragma unroll
   for (int i = 0; i < V; i++) {
@@ -108,15 +113,38 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < K; j++) wv[j][i] = to_f(w[(c0 + i) * K + j]);
   }
+  int n = find_seq(cu, N, t0);
+  int64_t s = cu[n], e = cu[n + 1];
+
+  if (t0 - (K - 1) >= s && t0 + R <= e && t0 + R <= T) {
+    // the run and its K-1 predecessors lie inside one sequence: no masking;
+    // rows t0-(K-1) .. t0+R-1 are loaded up front
+    Row<E, V> xr[R + K - 1];
+#pragma unroll
+    for (int i = 0; i < R + K - 1; i++) xr[i] = load_row<E, V>(x + (t0 - (K - 1) + i) * C + c0);
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      float out[V];
+#pragma unroll
+      for (int i = 0; i < V; i++) {
+        float z = bv[i];
+#pragma unroll
+        for (int j = 0; j < K; j++) z += wv[j][i] * xr[r + j].at(i);
+        out[i] = z * fast_sigmoid(z);
+      }
+      store_row<E, V>(y + (t0 + r) * C + c0, out);
+    }
+    return;
+  }
+
+  // runs that touch a sequence start or the batch end: every tap is loaded
+  // on its own (L1/L2 hits) with the sequence and halo masks
   Row<E, V> hr[K > 1 ? K - 1 : 1];
   const int64_t cu0 = cu[0];
   const bool use_halo = n_halo > 0 && t0 - (K - 1) < cu0;
 #pragma unroll
   for (int i = 0; i < K - 1; i++)
     hr[i] = use_halo ? load_row<E, V>(halo + (int64_t)i * C + c0) : zero_row<E, V>();
-
-  int n = find_seq(cu, N, t0);
-  int64_t s = cu[n], e = cu[n + 1];
 #pragma unroll
   for (int r = 0; r < R; r++) {
     const int64_t t = t0 + r;
@@ -133,15 +161,16 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
       for (int j = 0; j < K; j++) {
         const int64_t tau = t - (K - 1) + j;
         if (tau >= s) {
+          const Row<E, V> xv = load_row<E, V>(x + tau * C + c0);
 #pragma unroll
-          for (int i = 0; i < V; i++) z[i] += wv[j][i] * to_f(xr[r + j].v[i]);
+          for (int i = 0; i < V; i++) z[i] += wv[j][i] * xv.at(i);
         } else if (n == 0 && s - tau <= n_halo) {
           const int hrow = (int)(K - 1 - (s - tau));
 #pragma unroll
           for (int hi = 0; hi < K - 1; hi++)
             if (hi == hrow) {
 #pragma unroll
-              for (int i = 0; i < V; i++) z[i] += wv[j][i] * to_f(hr[hi].v[i]);
+              for (int i = 0; i < V; i++) z[i] += wv[j][i] * hr[hi].at(i);
             }
         }
       }
@@ -239,14 +268,14 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
           for (int i = 0; i < V; i++) xt[j][i] = 0.f;
           if (tau >= s) {
 #pragma unroll
-            for (int i = 0; i < V; i++) xt[j][i] = to_f(xr[r + j].v[i]);
+            for (int i = 0; i < V; i++) xt[j][i] = xr[r + j].at(i);
           } else if (n == 0 && s - tau <= n_halo) {
             const int hrow = (int)(K - 1 - (s - tau));
 #pragma unroll
             for (int hi = 0; hi < K - 1; hi++)
               if (hi == hrow) {
 #pragma unroll
-                for (int i = 0; i < V; i++) xt[j][i] = to_f(hr[hi].v[i]);
+                for (int i = 0; i < V; i++) xt[j][i] = hr[hi].at(i);
               }
           }
         }
@@ -256,7 +285,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
 #pragma unroll
           for (int j = 0; j < K; j++) z += wv[j][i] * xt[j][i];
           const float sg = fast_sigmoid(z);
-          const float d = to_f(gr[r].v[i]) * sg * (1.f + z * (1.f - sg));
+          const float d = gr[r].at(i) * sg * (1.f + z * (1.f - sg));
           dz[r][i] = d;
           if (r < R) {
             dbacc[i] += d;
@@ -387,16 +416,16 @@ int launch_fwd_k(const ConvArgs& a, void* y, hipStream_t stream) {
   const int64_t runs = (a.T + kFwdRows - 1) / kFwdRows;
   const int64_t tiles = (runs + kRunsPerBlock - 1) / kRunsPerBlock;
   const int cgroups = (cvec + kLanes - 1) / kLanes;
-  if (tiles > INT32_MAX || cgroups > 65535) return gdn::fail(GDN_EINVAL, "conv: T or C too large");
-  dim3 grid((unsigned)tiles, (unsigned)cgroups);
+  if (tiles * cgroups > INT32_MAX) return gdn::fail(GDN_EINVAL, "conv: T * C too large");
+  dim3 grid((unsigned)(tiles * cgroups));
   if (vec)
     hipLaunchKernelGGL((conv_fwd_kernel<E, K, VE>), grid, block, 0, stream, (const E*)a.x,
                        (const E*)a.w, (const E*)a.bias, (const E*)a.halo, a.cu, a.N, a.T, a.C,
-                       a.meta, (E*)y);
+                       cgroups, a.meta, (E*)y);
   else
     hipLaunchKernelGGL((conv_fwd_kernel<E, K, 1>), grid, block, 0, stream, (const E*)a.x,
                        (const E*)a.w, (const E*)a.bias, (const E*)a.halo, a.cu, a.N, a.T, a.C,
-                       a.meta, (E*)y);
+                       cgroups, a.meta, (E*)y);
   return gdn::check_launch("gdn_conv1d_silu_halo");
 }
 

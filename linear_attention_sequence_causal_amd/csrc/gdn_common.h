@@ -67,7 +67,7 @@ template <> struct Mfma<bf16> {
 
   // rows row0 + l%16 of a [rows][ld] array, k indices k0 + (conv. order)
   GDN_DEV static frag load(const bf16* base, int ld, int row0, int k0, int lane) {
-    const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    const bf16* p = base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0);
     bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
     bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
     frag f;
@@ -78,12 +78,12 @@ template <> struct Mfma<bf16> {
   // same from an fp32 [rows][ld] array, element k scaled by sc[k]
   GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
                                   int lane) {
-    const int kk = k0 + 4 * (lane >> 4);
-    const float* p = base + (row0 + (lane & 15)) * ld + kk;
+    const int kl = 4 * (lane >> 4);
+    const float* p = base + ((lane & 15) * ld + kl) + (row0 * ld + k0);
     floatx4 lo = *reinterpret_cast<const floatx4*>(p);
     floatx4 hi = *reinterpret_cast<const floatx4*>(p + 16);
-    floatx4 slo = *reinterpret_cast<const floatx4*>(sc + kk);
-    floatx4 shi = *reinterpret_cast<const floatx4*>(sc + kk + 16);
+    floatx4 slo = *reinterpret_cast<const floatx4*>(sc + kl + k0);
+    floatx4 shi = *reinterpret_cast<const floatx4*>(sc + kl + k0 + 16);
     frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -94,7 +94,7 @@ template <> struct Mfma<bf16> {
   }
   // same from an fp32 [rows][ld] array (e.g. a state in global memory)
   GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, int lane) {
-    const float* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    const float* p = base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0);
     floatx4 lo = *reinterpret_cast<const floatx4*>(p);
     floatx4 hi = *reinterpret_cast<const floatx4*>(p + 16);
     frag f;
@@ -108,7 +108,7 @@ template <> struct Mfma<bf16> {
   // column access: element (k, c0 + l%16) of a [K][ld] array, k in the
   // convention's order -- an operand whose contraction index runs down rows
   GDN_DEV static frag load_col(const bf16* base, int ld, int c0, int k0, int lane) {
-    const bf16* p = base + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+    const bf16* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
     frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -120,7 +120,7 @@ template <> struct Mfma<bf16> {
   GDN_DEV static frag load_col_f32(const float* base, int ld, int c0, int k0, const float* sc,
                                    int lane) {
     const int kk = k0 + 4 * (lane >> 4);
-    const float* p = base + kk * ld + c0 + (lane & 15);
+    const float* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
     frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -133,7 +133,7 @@ template <> struct Mfma<bf16> {
   GDN_DEV static frag load_col_scaled(const bf16* base, int ld, int c0, int k0, const float* sc,
                                       int lane) {
     const int kk = k0 + 4 * (lane >> 4);
-    const bf16* p = base + kk * ld + c0 + (lane & 15);
+    const bf16* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
     frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -162,12 +162,12 @@ template <> struct Mfma<float> {
   typedef floatx4 frag;
 
   GDN_DEV static frag load(const float* base, int ld, int row0, int k0, int lane) {
-    return *reinterpret_cast<const floatx4*>(base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+    return *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
   }
   GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
                                   int lane) {
     const int kk = k0 + 4 * (lane >> 4);
-    floatx4 a = *reinterpret_cast<const floatx4*>(base + (row0 + (lane & 15)) * ld + kk);
+    floatx4 a = *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
     floatx4 s = *reinterpret_cast<const floatx4*>(sc + kk);
     return a * s;
   }
@@ -175,7 +175,7 @@ template <> struct Mfma<float> {
     return load(base, ld, row0, k0, lane);
   }
   GDN_DEV static frag load_col(const float* base, int ld, int c0, int k0, int lane) {
-    const float* p = base + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+    const float* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
     return frag{p[0], p[ld], p[2 * ld], p[3 * ld]};
   }
   GDN_DEV static frag load_col_scaled(const float* base, int ld, int c0, int k0, const float* sc,
@@ -185,7 +185,7 @@ template <> struct Mfma<float> {
   GDN_DEV static frag load_col_f32(const float* base, int ld, int c0, int k0, const float* sc,
                                    int lane) {
     const int kk = k0 + 4 * (lane >> 4);
-    const float* p = base + kk * ld + c0 + (lane & 15);
+    const float* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
     frag f{p[0], p[ld], p[2 * ld], p[3 * ld]};
     if (sc) f *= *reinterpret_cast<const floatx4*>(sc + kk);
     return f;
@@ -199,6 +199,38 @@ template <> struct Mfma<float> {
   }
 };
 
+// Products over one k-tile (K = 16): bf16 via v_mfma_f32_16x16x16_bf16,
+// fp32 via four v_mfma_f32_16x16x4_f32.  Same fragment convention.
+template <typename O> struct Tile16;
+template <> struct Tile16<bf16> {
+  typedef bf16x4 frag;
+  // A[row0 + l%16][k0 + 4g .. +3] of an fp32 array, times s
+  GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, float s, int lane) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) f[j] = (bf16)(a[j] * s);
+    return f;
+  }
+  GDN_DEV static frag from_acc(const floatx4& c) {
+    frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) f[j] = (bf16)c[j];
+    return f;
+  }
+  GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+  }
+};
+template <> struct Tile16<float> {
+  typedef floatx4 frag;
+  GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, float s, int lane) {
+    return *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0)) * s;
+  }
+  GDN_DEV static frag from_acc(const floatx4& c) { return c; }
+  GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) { Mfma<float>::mma(acc, a, b); }
+};
+
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 // Wave-level butterfly sum over groups of `width` consecutive lanes.
@@ -208,4 +240,5 @@ template <int WIDTH> GDN_DEV float group_sum(float v) {
   return v;
 }
 
-GDN_DEV float fast_sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
+// sigmoid with the hardware exp2 and reciprocal (about 1 ulp each)
+GDN_DEV float fast_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
