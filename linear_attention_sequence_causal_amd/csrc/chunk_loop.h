@@ -38,6 +38,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "chunk_common.h"
 #include "chunk_plan.h"
 #include "gdn_internal.h"
@@ -285,7 +287,7 @@ void chunk_loop_kernel(LoopArgs a) {
     int tid_c = tid;
     asm volatile("" : "+v"(tid_c));
     const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
-    __syncthreads();  // the previous chunk's LDS readers are done
+    lds_barrier();  // the previous chunk's LDS readers are done
     stage_raw<E, DK, DV, NT, CF::HAS_Q>(sm, pf, a.scale, a.use_l2norm, tid_c);
     if constexpr (MODE == kStates) {
       // the state entering this chunk, for the backward
@@ -298,7 +300,7 @@ void chunk_loop_kernel(LoopArgs a) {
           for (int j = 0; j < 4; j++)
             dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
     }
-    __syncthreads();
+    lds_barrier();
     // L (and P) tiles
     {
       constexpr int NTILE = OUT ? 20 : 10;
@@ -309,7 +311,7 @@ void chunk_loop_kernel(LoopArgs a) {
         gram_tile_raw<O, DK>(sm, t >= 10, i, j, lane);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // D_b = (I + diag(beta) L_bb)^-1, one 16-lane group per block
     if (NW >= 4) {
       if (wave < 4 && lane < 16) invert_diag_block(sm, wave, lane);
@@ -339,7 +341,7 @@ void chunk_loop_kernel(LoopArgs a) {
         x[mt][1][j] = bt * (v1 - gk * k1[j]);
       }
     }
-    __syncthreads();  // D blocks written; v reads done
+    lds_barrier();  // D blocks written; v reads done
     // S's operand copy is rebuilt from the accumulators for (q S) below; kept
     // live through the solve it would cost 32 registers
 #pragma unroll
@@ -435,7 +437,7 @@ void chunk_loop_kernel(LoopArgs a) {
     }
 
     if constexpr (OUT) {
-      __syncthreads();  // staged o complete
+      lds_barrier();  // staged o complete
       typedef typename Vec16<E>::type V16;
       constexpr int VE = Vec16<E>::N;
       constexpr int OPR = DV / VE;
@@ -460,6 +462,381 @@ void chunk_loop_kernel(LoopArgs a) {
     dst = a.ht + ((int64_t)n * Hv + h) * DK * DV;
   }
   if (dst) {
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
+          dst[row * ld + col] = S[mt][nt][j];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Producer/consumer form of the chunk loop (bf16 activations).
+//
+// The per-chunk work splits into a state-independent part (stage the rows,
+// the l2norm factors and the cumsum of g, the gram tiles L and P, the
+// inverted diagonal blocks D) and the chain through the state (k S, the
+// substitution, q S + P v_new, the state update).  A workgroup holds NC
+// consumer waves, each owning 32 state columns, and four producer waves that
+// prepare chunk c + 1 into one of two LDS buffers while the consumers run
+// chunk c from the other, so every SIMD interleaves a producer and a consumer
+// wave.  Each iteration has two phases separated by workgroup barriers:
+//   phase 1  producers: prefetched rows -> LDS (raw q, k, v), row factors,
+//            G, beta, e^G; then the global loads of the chunk after next;
+//            consumers: (k S), right-hand side, blocked substitution;
+//   phase 2  producers: L tiles of row block pw and P tiles of row block
+//            3 - pw (five tiles per wave), then D_pw from their own L_pw,pw;
+//            consumers: o = (rq e^G) o (q S) + P v_new stored from LDS
+//            staging of their own columns, S <- e^{G_C} S + k^T (d o v_new).
+// A buffer written by producers in iteration i is read by consumers in
+// iteration i + 1 and rewritten in iteration i + 2, after two barriers.
+// Make this wave's LDS writes visible to its own later reads from other lanes.
+GDN_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// D_b = (I + N)^-1 with N = diag(beta_b) L_bb strictly lower 16x16, so
+// N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8): six fp32
+// products on the matrix cores by one whole wave.  The C layout of a product
+// is the B operand of the next; A operands are read back through the
+// scratch tile `sc` (an upper tile of L, never read as L).  D is written over
+// L_bb.
+template <class SM>
+GDN_DEV void invert_diag_mfma(SM& sm, int b, float* sc, int lane) {
+  typedef Tile16<float> F;
+  constexpr int LDF = SM::LDF;
+  const int g4 = lane >> 4, ln = lane & 15;
+  float* Lb = sm.L + 16 * b * LDF + 16 * b;
+  const float* bb = sm.beta + 16 * b;
+  const floatx4 NA = F::load_f32(Lb, LDF, 0, 0, bb[ln], lane);  // A[r][k] = beta_r L[r][k]
+  floatx4 NC;                                                      // C[4g+j][ln]
+#pragma unroll
+  for (int j = 0; j < 4; j++) NC[j] = bb[4 * g4 + j] * Lb[(4 * g4 + j) * LDF + ln];
+  floatx4 N2 = zero4();
+  F::mma(N2, NA, NC);
+#pragma unroll
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * LDF + ln] = N2[j];
+  wave_lds_sync();
+  const floatx4 N2A = F::load_f32(sc, LDF, 0, 0, 1.f, lane);
+  floatx4 N4 = zero4();
+  F::mma(N4, N2A, N2);
+#pragma unroll
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * LDF + ln] = N4[j];
+  wave_lds_sync();
+  const floatx4 N4A = F::load_f32(sc, LDF, 0, 0, 1.f, lane);
+  floatx4 N8 = zero4();
+  F::mma(N8, N4A, N4);
+  // R1 = (I + N^4)(I + N^8), R2 = (I + N^2) R1, D = (I - N) R2
+  floatx4 R1 = N4 + N8;
+#pragma unroll
+  for (int j = 0; j < 4; j++) R1[j] += (4 * g4 + j == ln) ? 1.f : 0.f;
+  F::mma(R1, N4A, N8);
+  floatx4 R2 = R1;
+  F::mma(R2, N2A, R1);
+  floatx4 t = zero4();
+  F::mma(t, NA, R2);
+#pragma unroll
+  for (int j = 0; j < 4; j++) Lb[(4 * g4 + j) * LDF + ln] = R2[j] - t[j];
+}
+
+template <typename E, int DK, int DV, int MODE>
+struct WsCfg {
+  static constexpr bool OUT = MODE == kOut;
+  static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
+  static constexpr int NC = NSC / 32;                          // consumer waves
+  static constexpr int NP = 4;                                 // producer waves
+  static constexpr int NT = (NC + NP) * 64;
+  typedef LoopSmem<E, DK, DV, OUT> SM;
+  typedef Prefetch<E, DK, DV, NP * 64, OUT> PF;
+  // both buffers within the 160 KiB of LDS of a CU
+  static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
+};
+
+template <typename E, int DK, int DV, int MODE>
+__global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
+  typedef WsCfg<E, DK, DV, MODE> CF;
+  typedef E O;
+  typedef Mfma<O> M;
+  typedef Tile16<O> T16;
+  constexpr int NC = CF::NC;
+  constexpr int KS = M::KSTEP;
+  constexpr int NSK = DK / KS;  // contraction steps over dk
+  constexpr int NSB = BT / KS;  // contraction steps over the chunk
+  constexpr int DKT = DK / 16;  // state row tiles
+  constexpr bool OUT = CF::OUT;
+  typedef typename CF::SM SM;
+  __shared__ SM buf[2];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= a.counts[0]) return;
+  const int4 ent = a.seg_table[seg];
+  if (MODE == kSummary && (ent.w & kLast)) return;
+  const int n = ent.x;
+  const int64_t tb = ent.y, te = ent.z;
+  const int Hv = a.Hv;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int nchunks = (int)((te - tb + BT - 1) / BT);
+
+  // upper tiles of P stay zero in both buffers
+  if constexpr (OUT)
+    for (int e = tid; e < 2 * BT * BT; e += CF::NT) {
+      const int b = e / (BT * BT), r = (e / BT) % BT, c = e % BT;
+      if ((c >> 4) > (r >> 4)) buf[b].p[r * SM::LDP + c] = from_f<O>(0.f);
+    }
+
+  // The two roles run separate loops with the same barrier sequence (two per
+  // iteration, iterations -1 .. nchunks-1), so each keeps only its own
+  // registers live.
+  if (wave >= NC) {
+    // ======================= producers =======================
+    const int pw = wave - NC;  // its 16-row block
+    const int qa = h / (Hv / a.Hk);
+    const E* qp = (const E*)a.q + (int64_t)qa * DK;
+    const E* kp = (const E*)a.k + (int64_t)qa * DK;
+    const E* vp = (const E*)a.v + (int64_t)h * DV;
+    const float* gp = a.g + h;
+    const float* bp = a.beta + h;
+    typename CF::PF pf;
+    if (nchunks > 0) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb, te, tid - NC * 64);
+    for (int it = -1; it < nchunks; it++) {
+      // lane-dependent addresses are rebuilt every iteration from an opaque
+      // copy of the thread index: hoisted they would pin registers
+      int tid_c = tid;
+      asm volatile("" : "+v"(tid_c));
+      const int lane = tid_c & 63;
+      const int pc = it + 1;  // the chunk prepared
+      SM& P = buf[pc & 1];
+      if (pc < nchunks) {
+        stage_raw<E, DK, DV, CF::NP * 64, OUT>(P, pf, a.scale, a.use_l2norm, tid_c - NC * 64);
+        if (pc + 1 < nchunks)
+          pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb + (int64_t)(pc + 1) * BT, te,
+                  tid_c - NC * 64);
+      }
+      lds_barrier();
+      if (pc < nchunks) {
+        // L tiles of row block pw, P tiles of row block 3 - pw
+#pragma unroll 1
+        for (int j = 0; j <= pw; j++) gram_tile_raw<O, DK>(P, false, pw, j, lane);
+        if constexpr (OUT) {
+#pragma unroll 1
+          for (int j = 0; j <= 3 - pw; j++) gram_tile_raw<O, DK>(P, true, 3 - pw, j, lane);
+        }
+        // D_pw = (I + diag(beta) L_pw,pw)^-1 from the tile this wave just
+        // wrote; scratch in an upper tile of L: (0,1), (1,2), (2,3), (0,2)
+        wave_lds_sync();
+        const int si = pw == 3 ? 0 : pw, sj = pw == 3 ? 2 : pw + 1;
+        invert_diag_mfma(P, pw, P.L + 16 * si * SM::LDF + 16 * sj, lane);
+      }
+      lds_barrier();
+    }
+    return;
+  }
+
+  // ======================= consumers =======================
+  const int lane0 = tid & 63;
+  const int c0 = wave * 32;                         // first state column of this wave
+  const bool mcol = MODE == kSummary && c0 < DK;    // wave holds columns of M (v = 0)
+  const int vc0 = MODE == kSummary ? c0 - DK : c0;  // value column of the first column
+  // state tiles S[mt][nt]: rows 16mt + 4(lane/16) + j, cols c0 + 16nt + lane%16
+  floatx4 S[DKT][2];
+  {
+    const int g4 = lane0 >> 4, ln = lane0 & 15;
+    const float* src = nullptr;
+    if (MODE != kSummary) {
+      if (!(ent.w & kFirst)) src = a.seg_init + ((int64_t)seg * Hv + h) * DK * DV;
+      else if (a.h0) src = a.h0 + ((int64_t)n * Hv + h) * DK * DV;
+    }
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
+          float v = 0.f;
+          if (mcol) v = (row == col) ? 1.f : 0.f;
+          else if (src) v = src[row * DV + col];
+          S[mt][nt][j] = v;
+        }
+  }
+  floatx4 x[4][2];
+  for (int it = -1; it < nchunks; it++) {
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
+    SM& C = buf[it & 1];
+
+    // ---------------- phase 1: k S, right-hand side, substitution
+    if (it >= 0) {
+      if constexpr (MODE == kStates) {
+        // the state entering this chunk, for the backward
+        float* dst = a.states + ((int64_t)(a.seg_chunk0[seg] + it) * Hv + h) * DK * DV;
+#pragma unroll
+        for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+          for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
+      }
+      // right-hand side beta o (v - e^G o rk o (k S)) for this wave's columns;
+      // k S accumulates in x, one contraction step of S's operand at a time
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) x[mt][0] = x[mt][1] = zero4();
+#pragma unroll
+      for (int s = 0; s < NSK; s++) {
+        const typename M::frag b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const typename M::frag kf = M::load(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          M::mma(x[mt][0], kf, b0);
+          M::mma(x[mt][1], kf, b1);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int row = 16 * mt + 4 * g4 + j;
+          const float bt = C.beta[row], gk = C.eg[row] * C.rk[row];
+          const float v0 = mcol ? 0.f : to_f(C.v[row * SM::LDV + vc0 + ln]);
+          const float v1 = mcol ? 0.f : to_f(C.v[row * SM::LDV + vc0 + 16 + ln]);
+          x[mt][0][j] = bt * (v0 - gk * x[mt][0][j]);
+          x[mt][1][j] = bt * (v1 - gk * x[mt][1][j]);
+        }
+      }
+      // v_new = (I + diag(beta) L)^-1 rhs by block rows:
+      // x_i <- D_i (x_i - diag(beta_i) sum_{m<i} L_im x_m)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int m = 0; m < i; m++) {
+          const float nb = -C.beta[16 * i + ln];
+          const typename T16::frag lf = T16::load_f32(C.L, SM::LDF, 16 * i, 16 * m, nb, lane);
+          T16::mma(x[i][0], lf, T16::from_acc(x[m][0]));
+          T16::mma(x[i][1], lf, T16::from_acc(x[m][1]));
+        }
+        const typename T16::frag df = T16::load_f32(C.L, SM::LDF, 16 * i, 16 * i, 1.f, lane);
+        floatx4 y0 = zero4(), y1 = zero4();
+        T16::mma(y0, df, T16::from_acc(x[i][0]));
+        T16::mma(y1, df, T16::from_acc(x[i][1]));
+        x[i][0] = y0;
+        x[i][1] = y1;
+      }
+    }
+    lds_barrier();
+
+    // ---------------- phase 2: output, state update
+    if (it >= 0) {
+      const float GC = C.G[BT - 1];
+      if constexpr (OUT) {
+        // o = (rq e^G) o (q S) + P v_new, staged over this wave's columns of v
+        floatx4 o[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) o[mt][0] = o[mt][1] = zero4();
+#pragma unroll
+        for (int s = 0; s < NSK; s++) {
+          const typename M::frag b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
+#pragma unroll
+          for (int mt = 0; mt < 4; mt++) {
+            const typename M::frag qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
+            M::mma(o[mt][0], qf, b0);
+            M::mma(o[mt][1], qf, b1);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const int rb = 16 * mt + 4 * g4;
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float f = C.eg[rb + j] * C.rq[rb + j];
+            o[mt][0][j] *= f;
+            o[mt][1][j] *= f;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NSB; s++) {
+          const typename M::frag x0 = acc_as_b<O>(x, s, 0), x1 = acc_as_b<O>(x, s, 1);
+#pragma unroll
+          for (int mt = 0; mt < 4; mt++) {
+            const typename M::frag pfrag = M::load(C.p, SM::LDP, 16 * mt, s * KS, lane);
+            M::mma(o[mt][0], pfrag, x0);
+            M::mma(o[mt][1], pfrag, x1);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const int rb = 16 * mt + 4 * g4;
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            C.v[(rb + j) * SM::LDV + c0 + ln] = from_f<O>(o[mt][0][j]);
+            C.v[(rb + j) * SM::LDV + c0 + 16 + ln] = from_f<O>(o[mt][1][j]);
+          }
+        }
+        // this wave's 32 columns of the 64 rows, as 16-byte pieces
+        wave_lds_sync();
+        typedef typename Vec16<E>::type V16;
+        constexpr int VE = Vec16<E>::N;
+        constexpr int PPR = 32 / VE;  // pieces per row
+        const int64_t tc = tb + (int64_t)it * BT;
+        E* op = (E*)a.o + (int64_t)h * DV + c0;
+#pragma unroll
+        for (int p = 0; p < BT * PPR / 64; p++) {
+          const int i = lane + 64 * p;
+          const int row = i / PPR, vi = i % PPR;
+          const int64_t t = tc + row;
+          if (t < te)
+            *reinterpret_cast<V16*>(op + t * (int64_t)Hv * DV + vi * VE) =
+                *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
+        }
+      }
+      // S <- e^{G_C} S + k^T (rk e^{G_C - G} o v_new)
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const int rb = 16 * mt + 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float d = C.rk[rb + j] * __expf(GC - C.G[rb + j]);
+          x[mt][0][j] *= d;
+          x[mt][1][j] *= d;
+        }
+      }
+      const float eC = __expf(GC);
+#pragma unroll
+      for (int mt = 0; mt < DKT; mt++) {
+        floatx4 acc0 = S[mt][0] * eC, acc1 = S[mt][1] * eC;
+#pragma unroll
+        for (int s = 0; s < NSB; s++) {
+          const typename M::frag kf = M::load_col(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          M::mma(acc0, kf, acc_as_b<O>(x, s, 0));
+          M::mma(acc1, kf, acc_as_b<O>(x, s, 1));
+        }
+        S[mt][0] = acc0;
+        S[mt][1] = acc1;
+      }
+    }
+    lds_barrier();
+  }
+
+  // final state: ht (output) or the summary X = [M | E]
+  float* dst = nullptr;
+  int ld = DV;
+  if (MODE == kSummary) {
+    dst = a.seg_state + ((int64_t)seg * Hv + h) * DK * (DK + DV);
+    ld = DK + DV;
+  } else if ((ent.w & kLast) && a.ht) {
+    dst = a.ht + ((int64_t)n * Hv + h) * DK * DV;
+  }
+  if (dst) {
+    const int g4 = lane0 >> 4, ln = lane0 & 15;
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
@@ -521,6 +898,20 @@ __global__ __launch_bounds__(256) void empty_seq_state_kernel(const int32_t* __r
   for (int i = threadIdx.x; i < dd; i += 256) ht[base + i] = h0 ? h0[base + i] : 0.f;
 }
 
+// One pass of the chunk loop over every segment: the producer/consumer form
+// for bfloat16 when its two buffers fit in LDS, else the single-buffer form.
+template <typename E, int DK, int DV, int MODE>
+void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
+  const dim3 grid((unsigned)pl.seg_cap, a.Hv);
+  if constexpr (std::is_same<E, bf16>::value && WsCfg<E, DK, DV, MODE>::FITS) {
+    hipLaunchKernelGGL((chunk_ws_kernel<E, DK, DV, MODE>), grid, dim3(WsCfg<E, DK, DV, MODE>::NT), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((chunk_loop_kernel<E, DK, DV, MODE>), grid, dim3(LoopCfg<E, DK, DV, MODE>::NT),
+                       0, stream, a);
+  }
+}
+
 // Plan, summaries + scan when segments split a sequence, then the final pass
 // in `FINAL` mode (kOut or kStates).  `a` carries the caller's tensors.
 template <typename E, int DK, int DV, int FINAL>
@@ -536,17 +927,13 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
                      (int)pl.seg_cap, (int)pl.chunk_cap, pp);
   if (int rc = gdn::check_launch("chunk plan")) return rc;
   if (pl.split) {
-    typedef LoopCfg<E, DK, DV, kSummary> CS;
-    hipLaunchKernelGGL((chunk_loop_kernel<E, DK, DV, kSummary>), dim3((unsigned)pl.seg_cap, a.Hv),
-                       dim3(CS::NT), 0, stream, a);
+    launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;
     hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(256), 0, stream,
                        a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv);
     if (int rc = gdn::check_launch("chunk scan")) return rc;
   }
-  typedef LoopCfg<E, DK, DV, FINAL> CO;
-  hipLaunchKernelGGL((chunk_loop_kernel<E, DK, DV, FINAL>), dim3((unsigned)pl.seg_cap, a.Hv),
-                     dim3(CO::NT), 0, stream, a);
+  launch_loop<E, DK, DV, FINAL>(a, pl, stream);
   return gdn::check_launch("chunk loop");
 }
 

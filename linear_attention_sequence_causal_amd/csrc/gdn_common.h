@@ -233,6 +233,12 @@ template <> struct Tile16<float> {
 
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier for hand-offs through LDS only: waits for this wave's LDS
+// operations, not for its global loads and stores in flight (the release
+// fence of __syncthreads() would drain those too).  The memory clobber keeps
+// the compiler from moving memory operations across it.
+GDN_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Wave-level butterfly sum over groups of `width` consecutive lanes.
 template <int WIDTH> GDN_DEV float group_sum(float v) {
 #pragma unroll
