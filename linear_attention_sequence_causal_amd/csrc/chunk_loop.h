@@ -120,18 +120,15 @@ GDN_DEV void stage_raw(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float s
   for (int p = 0; p < PF::PQ; p++) {
     const int i = tid + NT * p;
     const int row = i / PF::QPR, vi = i % PF::QPR;
-    float kss = 0.f, qss = 0.f;
-#pragma unroll
-    for (int e = 0; e < VE; e++) {
-      const float kf = to_f(pf.k[p][e]);
-      kss += kf * kf;
-      if constexpr (HAS_Q) {
-        const float qf = to_f(pf.q[p][e]);
-        qss += qf * qf;
-      }
+    float kss = sum_sq(pf.k[p]), qss = 0.f;
+    if constexpr (HAS_Q) qss = sum_sq(pf.q[p]);
+    if constexpr (PF::QPR <= 16) {
+      kss = row_group_sum<PF::QPR>(kss);
+      if constexpr (HAS_Q) qss = row_group_sum<PF::QPR>(qss);
+    } else {
+      kss = group_sum<PF::QPR>(kss);
+      if constexpr (HAS_Q) qss = group_sum<PF::QPR>(qss);
     }
-    kss = group_sum<PF::QPR>(kss);
-    if constexpr (HAS_Q) qss = group_sum<PF::QPR>(qss);
     if (i < PF::QV) {
       *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vi * VE) = pf.k[p];
       if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vi * VE) = pf.q[p];
@@ -494,6 +491,52 @@ void chunk_loop_kernel(LoopArgs a) {
 //            staging of their own columns, S <- e^{G_C} S + k^T (d o v_new).
 // A buffer written by producers in iteration i is read by consumers in
 // iteration i + 1 and rewritten in iteration i + 2, after two barriers.
+//
+// The substitution operands are stored ready for the matrix cores: N =
+// -diag(beta) L off the diagonal and D on it, both bf16 (the rounding the
+// bf16 products apply anyway).  Operands whose contraction index runs down
+// the stored rows (k^T in the state update, v in C layout) are read with the
+// transposing LDS load.
+
+// LDS of one buffer.  Per-row arrays first: ds immediate offsets reach 64 KiB.
+template <typename O, int DK, int DV, bool HAS_Q>
+struct WsSmem {
+  static constexpr int PAD = 16 / (int)sizeof(O);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDV = DV + PAD;
+  static constexpr int LDP = BT + PAD;
+  alignas(16) float G[BT];
+  alignas(16) float beta[BT];
+  alignas(16) float eg[BT];  // exp(G)
+  alignas(16) float rq[BT];  // scale / |q| (scale without l2norm)
+  alignas(16) float rk[BT];  // 1 / |k| (1 without l2norm)
+  alignas(16) O n[BT * LDP];  // -beta_r L[r][c] below the diagonal blocks, D_b on them
+  alignas(16) O p[HAS_Q ? BT * LDP : 8];
+  alignas(16) O k[BT * LDK];
+  alignas(16) O q[HAS_Q ? BT * LDK : 8];
+  alignas(16) O v[BT * LDV];
+};
+
+// Producer scratch for the diagonal inversion (one set per producer wave,
+// used within one phase): the fp32 L_bb tile and a work tile.
+constexpr int kScLd = 20;  // 16 + 4 floats: 16-byte aligned rows
+struct WsScratch {
+  alignas(16) float t[4][2][16 * kScLd];
+};
+
+template <typename E, int DK, int DV, int MODE>
+struct WsCfg {
+  static constexpr bool OUT = MODE == kOut;
+  static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
+  static constexpr int NC = NSC / 32;                          // consumer waves
+  static constexpr int NP = 4;                                 // producer waves
+  static constexpr int NT = (NC + NP) * 64;
+  typedef WsSmem<E, DK, DV, OUT> SM;
+  typedef Prefetch<E, DK, DV, NP * 64, OUT> PF;
+  // both buffers and the scratch within the 160 KiB of LDS of a CU
+  static constexpr bool FITS = 2 * sizeof(SM) + sizeof(WsScratch) <= 160 * 1024;
+};
+
 // Make this wave's LDS writes visible to its own later reads from other lanes.
 GDN_DEV void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -502,35 +545,30 @@ GDN_DEV void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// D_b = (I + N)^-1 with N = diag(beta_b) L_bb strictly lower 16x16, so
-// N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8): six fp32
-// products on the matrix cores by one whole wave.  The C layout of a product
-// is the B operand of the next; A operands are read back through the
-// scratch tile `sc` (an upper tile of L, never read as L).  D is written over
-// L_bb.
-template <class SM>
-GDN_DEV void invert_diag_mfma(SM& sm, int b, float* sc, int lane) {
+// D = (I + N)^-1 for N = diag(bb) L, L strictly lower 16x16, so N^16 = 0 and
+// (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8): six fp32 products on the
+// matrix cores by one whole wave.  Lt: L in fp32 [16][kScLd] (A operands are
+// read from it), NC: N in C layout (N[4(lane/16)+j][lane%16]), sc: a work
+// tile.  The C layout of a product is the B operand of the next.  Returns D
+// in C layout.
+GDN_DEV floatx4 invert_unit_lower16(const float* Lt, const float* bb, const floatx4& NC, float* sc,
+                                    int lane) {
   typedef Tile16<float> F;
-  constexpr int LDF = SM::LDF;
   const int g4 = lane >> 4, ln = lane & 15;
-  float* Lb = sm.L + 16 * b * LDF + 16 * b;
-  const float* bb = sm.beta + 16 * b;
-  const floatx4 NA = F::load_f32(Lb, LDF, 0, 0, bb[ln], lane);  // A[r][k] = beta_r L[r][k]
-  floatx4 NC;                                                      // C[4g+j][ln]
-#pragma unroll
-  for (int j = 0; j < 4; j++) NC[j] = bb[4 * g4 + j] * Lb[(4 * g4 + j) * LDF + ln];
+  const floatx4 NA = F::load_f32(Lt, kScLd, 0, 0, bb[ln], lane);  // A[r][k] = beta_r L[r][k]
   floatx4 N2 = zero4();
   F::mma(N2, NA, NC);
 #pragma unroll
-  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * LDF + ln] = N2[j];
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kScLd + ln] = N2[j];
   wave_lds_sync();
-  const floatx4 N2A = F::load_f32(sc, LDF, 0, 0, 1.f, lane);
+  const floatx4 N2A = F::load(sc, kScLd, 0, 0, lane);
   floatx4 N4 = zero4();
   F::mma(N4, N2A, N2);
+  wave_lds_sync();  // every lane has read N^2 before it is overwritten
 #pragma unroll
-  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * LDF + ln] = N4[j];
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kScLd + ln] = N4[j];
   wave_lds_sync();
-  const floatx4 N4A = F::load_f32(sc, LDF, 0, 0, 1.f, lane);
+  const floatx4 N4A = F::load(sc, kScLd, 0, 0, lane);
   floatx4 N8 = zero4();
   F::mma(N8, N4A, N4);
   // R1 = (I + N^4)(I + N^8), R2 = (I + N^2) R1, D = (I - N) R2
@@ -542,22 +580,8 @@ GDN_DEV void invert_diag_mfma(SM& sm, int b, float* sc, int lane) {
   F::mma(R2, N2A, R1);
   floatx4 t = zero4();
   F::mma(t, NA, R2);
-#pragma unroll
-  for (int j = 0; j < 4; j++) Lb[(4 * g4 + j) * LDF + ln] = R2[j] - t[j];
+  return R2 - t;
 }
-
-template <typename E, int DK, int DV, int MODE>
-struct WsCfg {
-  static constexpr bool OUT = MODE == kOut;
-  static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
-  static constexpr int NC = NSC / 32;                          // consumer waves
-  static constexpr int NP = 4;                                 // producer waves
-  static constexpr int NT = (NC + NP) * 64;
-  typedef LoopSmem<E, DK, DV, OUT> SM;
-  typedef Prefetch<E, DK, DV, NP * 64, OUT> PF;
-  // both buffers within the 160 KiB of LDS of a CU
-  static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
-};
 
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
@@ -565,6 +589,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef E O;
   typedef Mfma<O> M;
   typedef Tile16<O> T16;
+  typedef typename M::frag Fr;
   constexpr int NC = CF::NC;
   constexpr int KS = M::KSTEP;
   constexpr int NSK = DK / KS;  // contraction steps over dk
@@ -573,6 +598,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   constexpr bool OUT = CF::OUT;
   typedef typename CF::SM SM;
   __shared__ SM buf[2];
+  __shared__ WsScratch scr;
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= a.counts[0]) return;
@@ -581,8 +607,9 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   const int n = ent.x;
   const int64_t tb = ent.y, te = ent.z;
   const int Hv = a.Hv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int g4 = lane >> 4, ln = lane & 15;
   const int nchunks = (int)((te - tb + BT - 1) / BT);
 
   // upper tiles of P stay zero in both buffers
@@ -597,43 +624,115 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   // registers live.
   if (wave >= NC) {
     // ======================= producers =======================
-    const int pw = wave - NC;  // its 16-row block
+    const int pw = wave - NC;  // L row block; P row block 3 - pw
+    const int iq = 3 - pw;
+    const int ptid = tid - NC * 64;
     const int qa = h / (Hv / a.Hk);
     const E* qp = (const E*)a.q + (int64_t)qa * DK;
     const E* kp = (const E*)a.k + (int64_t)qa * DK;
     const E* vp = (const E*)a.v + (int64_t)h * DV;
     const float* gp = a.g + h;
     const float* bp = a.beta + h;
+    float* Lt = scr.t[pw][0];
+    float* sc = scr.t[pw][1];
     typename CF::PF pf;
-    if (nchunks > 0) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb, te, tid - NC * 64);
+    if (nchunks > 0) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb, te, ptid);
     for (int it = -1; it < nchunks; it++) {
-      // lane-dependent addresses are rebuilt every iteration from an opaque
-      // copy of the thread index: hoisted they would pin registers
-      int tid_c = tid;
-      asm volatile("" : "+v"(tid_c));
-      const int lane = tid_c & 63;
       const int pc = it + 1;  // the chunk prepared
       SM& P = buf[pc & 1];
       if (pc < nchunks) {
-        stage_raw<E, DK, DV, CF::NP * 64, OUT>(P, pf, a.scale, a.use_l2norm, tid_c - NC * 64);
+        stage_raw<E, DK, DV, CF::NP * 64, OUT>(P, pf, a.scale, a.use_l2norm, ptid);
         if (pc + 1 < nchunks)
-          pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb + (int64_t)(pc + 1) * BT, te,
-                  tid_c - NC * 64);
+          pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb + (int64_t)(pc + 1) * BT, te, ptid);
       }
       lds_barrier();
       if (pc < nchunks) {
-        // L tiles of row block pw, P tiles of row block 3 - pw
-#pragma unroll 1
-        for (int j = 0; j <= pw; j++) gram_tile_raw<O, DK>(P, false, pw, j, lane);
-        if constexpr (OUT) {
-#pragma unroll 1
-          for (int j = 0; j <= 3 - pw; j++) gram_tile_raw<O, DK>(P, true, 3 - pw, j, lane);
+        // A operands read once per row block
+        Fr ak[NSK], aq[OUT ? NSK : 1];
+#pragma unroll
+        for (int s = 0; s < NSK; s++) {
+          ak[s] = M::load(P.k, SM::LDK, 16 * pw, s * KS, lane);
+          if constexpr (OUT) aq[s] = M::load(P.q, SM::LDK, 16 * iq, s * KS, lane);
         }
-        // D_pw = (I + diag(beta) L_pw,pw)^-1 from the tile this wave just
-        // wrote; scratch in an upper tile of L: (0,1), (1,2), (2,3), (0,2)
+        // Five independent tiles a wave: the diagonal L(pw,pw) and P(iq,iq),
+        // and the three off-diagonal ones, L(pw, j < pw) then P(iq, j < iq).
+        // Off the diagonal the decay factors as e^{G_r - G_0} e^{G_0 - G_c}
+        // with G_0 = G at the row block's first row: both factors <= 1.
+        const int rL = 16 * pw + 4 * g4, rP = 16 * iq + 4 * g4;  // this lane's first rows
+        floatx4 GL, fL, bL, GP, fP;
+        GL = *reinterpret_cast<const floatx4*>(P.G + rL);
+        fL = *reinterpret_cast<const floatx4*>(P.rk + rL);
+        bL = *reinterpret_cast<const floatx4*>(P.beta + rL);
+        if constexpr (OUT) {
+          GP = *reinterpret_cast<const floatx4*>(P.G + rP);
+          fP = *reinterpret_cast<const floatx4*>(P.rq + rP);
+        }
+        floatx4 accD = zero4(), accDP = zero4(), accO[3];
+#pragma unroll
+        for (int t = 0; t < 3; t++) accO[t] = zero4();
+#pragma unroll
+        for (int s = 0; s < NSK; s++) {
+          M::mma(accD, ak[s], M::load(P.k, SM::LDK, 16 * pw, s * KS, lane));
+          if constexpr (OUT) M::mma(accDP, aq[s], M::load(P.k, SM::LDK, 16 * iq, s * KS, lane));
+#pragma unroll
+          for (int t = 0; t < 3; t++) {
+            if (!OUT && t >= pw) break;
+            const int j = t < pw ? t : t - pw;
+            M::mma(accO[t], t < pw ? ak[s] : aq[OUT ? s : 0], M::load(P.k, SM::LDK, 16 * j, s * KS, lane));
+          }
+        }
+        // diagonal L tile: fp32 to the scratch (inversion), N off its blocks
+        floatx4 NCd;
+        {
+          const int col = 16 * pw + ln;
+          const float Gc = P.G[col], fc = P.rk[col];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            const int row = rL + jj;
+            const float e = __expf(fminf(GL[jj] - Gc, 0.f));  // clamped: masked entries stay finite
+            const float val = row > col ? accD[jj] * fL[jj] * fc * e : 0.f;
+            Lt[(4 * g4 + jj) * kScLd + ln] = val;
+            NCd[jj] = bL[jj] * val;
+          }
+        }
+        if constexpr (OUT) {
+          const int col = 16 * iq + ln;
+          const float Gc = P.G[col], fc = P.rk[col];
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            const int row = rP + jj;
+            const float e = __expf(fminf(GP[jj] - Gc, 0.f));
+            P.p[row * SM::LDP + col] = from_f<O>(row >= col ? accDP[jj] * fP[jj] * fc * e : 0.f);
+          }
+        }
+        {
+          const float G0L = P.G[16 * pw], G0P = OUT ? P.G[16 * iq] : 0.f;
+          floatx4 aL, aP;
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            aL[jj] = -bL[jj] * fL[jj] * __expf(GL[jj] - G0L);
+            if constexpr (OUT) aP[jj] = fP[jj] * __expf(GP[jj] - G0P);
+          }
+#pragma unroll
+          for (int t = 0; t < 3; t++) {
+            if (!OUT && t >= pw) break;
+            const bool isL = t < pw;
+            const int j = isL ? t : t - pw;
+            const int col = 16 * j + ln;
+            const float bc = P.rk[col] * __expf((isL ? G0L : G0P) - P.G[col]);
+            O* dst = isL ? P.n : P.p;
+            const int r0 = isL ? rL : rP;
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++)
+              dst[(r0 + jj) * SM::LDP + col] = from_f<O>(accO[t][jj] * (isL ? aL[jj] : aP[jj]) * bc);
+          }
+        }
+        // D_pw = (I + diag(beta) L_pw,pw)^-1, written as bf16 on the diagonal
         wave_lds_sync();
-        const int si = pw == 3 ? 0 : pw, sj = pw == 3 ? 2 : pw + 1;
-        invert_diag_mfma(P, pw, P.L + 16 * si * SM::LDF + 16 * sj, lane);
+        const floatx4 D = invert_unit_lower16(Lt, P.beta + 16 * pw, NCd, sc, lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          P.n[(16 * pw + 4 * g4 + jj) * SM::LDP + 16 * pw + ln] = from_f<O>(D[jj]);
       }
       lds_barrier();
     }
@@ -641,14 +740,12 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   }
 
   // ======================= consumers =======================
-  const int lane0 = tid & 63;
   const int c0 = wave * 32;                         // first state column of this wave
   const bool mcol = MODE == kSummary && c0 < DK;    // wave holds columns of M (v = 0)
   const int vc0 = MODE == kSummary ? c0 - DK : c0;  // value column of the first column
   // state tiles S[mt][nt]: rows 16mt + 4(lane/16) + j, cols c0 + 16nt + lane%16
   floatx4 S[DKT][2];
   {
-    const int g4 = lane0 >> 4, ln = lane0 & 15;
     const float* src = nullptr;
     if (MODE != kSummary) {
       if (!(ent.w & kFirst)) src = a.seg_init + ((int64_t)seg * Hv + h) * DK * DV;
@@ -667,11 +764,9 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           S[mt][nt][j] = v;
         }
   }
+  const int64_t o_ld = (int64_t)Hv * DV;
   floatx4 x[4][2];
   for (int it = -1; it < nchunks; it++) {
-    int tid_c = tid;
-    asm volatile("" : "+v"(tid_c));
-    const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
     SM& C = buf[it & 1];
 
     // ---------------- phase 1: k S, right-hand side, substitution
@@ -693,38 +788,41 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       for (int mt = 0; mt < 4; mt++) x[mt][0] = x[mt][1] = zero4();
 #pragma unroll
       for (int s = 0; s < NSK; s++) {
-        const typename M::frag b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
+        const Fr b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const typename M::frag kf = M::load(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          const Fr kf = M::load(C.k, SM::LDK, 16 * mt, s * KS, lane);
           M::mma(x[mt][0], kf, b0);
           M::mma(x[mt][1], kf, b1);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
+        const floatx4 bt = *reinterpret_cast<const floatx4*>(C.beta + 16 * mt + 4 * g4);
+        const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
+        const floatx4 rk = *reinterpret_cast<const floatx4*>(C.rk + 16 * mt + 4 * g4);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int row = 16 * mt + 4 * g4 + j;
-          const float bt = C.beta[row], gk = C.eg[row] * C.rk[row];
-          const float v0 = mcol ? 0.f : to_f(C.v[row * SM::LDV + vc0 + ln]);
-          const float v1 = mcol ? 0.f : to_f(C.v[row * SM::LDV + vc0 + 16 + ln]);
-          x[mt][0][j] = bt * (v0 - gk * x[mt][0][j]);
-          x[mt][1][j] = bt * (v1 - gk * x[mt][1][j]);
+        for (int nt = 0; nt < 2; nt++) {
+          bf16x4 vv;
+          if (!mcol) vv = lds_rows4_tr(C.v, SM::LDV, 16 * mt, vc0 + 16 * nt, lane);
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float v = mcol ? 0.f : (float)vv[j];
+            x[mt][nt][j] = bt[j] * (v - eg[j] * rk[j] * x[mt][nt][j]);
+          }
         }
       }
       // v_new = (I + diag(beta) L)^-1 rhs by block rows:
-      // x_i <- D_i (x_i - diag(beta_i) sum_{m<i} L_im x_m)
+      // x_i <- D_i (x_i + sum_{m<i} N_im x_m),  N = -diag(beta) L
 #pragma unroll
       for (int i = 0; i < 4; i++) {
 #pragma unroll
         for (int m = 0; m < i; m++) {
-          const float nb = -C.beta[16 * i + ln];
-          const typename T16::frag lf = T16::load_f32(C.L, SM::LDF, 16 * i, 16 * m, nb, lane);
-          T16::mma(x[i][0], lf, T16::from_acc(x[m][0]));
-          T16::mma(x[i][1], lf, T16::from_acc(x[m][1]));
+          const typename T16::frag nf = T16::load(C.n, SM::LDP, 16 * i, 16 * m, lane);
+          T16::mma(x[i][0], nf, T16::from_acc(x[m][0]));
+          T16::mma(x[i][1], nf, T16::from_acc(x[m][1]));
         }
-        const typename T16::frag df = T16::load_f32(C.L, SM::LDF, 16 * i, 16 * i, 1.f, lane);
+        const typename T16::frag df = T16::load(C.n, SM::LDP, 16 * i, 16 * i, lane);
         floatx4 y0 = zero4(), y1 = zero4();
         T16::mma(y0, df, T16::from_acc(x[i][0]));
         T16::mma(y1, df, T16::from_acc(x[i][1]));
@@ -744,41 +842,38 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         for (int mt = 0; mt < 4; mt++) o[mt][0] = o[mt][1] = zero4();
 #pragma unroll
         for (int s = 0; s < NSK; s++) {
-          const typename M::frag b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
+          const Fr b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
 #pragma unroll
           for (int mt = 0; mt < 4; mt++) {
-            const typename M::frag qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
+            const Fr qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
             M::mma(o[mt][0], qf, b0);
             M::mma(o[mt][1], qf, b1);
           }
         }
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const int rb = 16 * mt + 4 * g4;
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const float f = C.eg[rb + j] * C.rq[rb + j];
-            o[mt][0][j] *= f;
-            o[mt][1][j] *= f;
-          }
+          const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
+          const floatx4 rq = *reinterpret_cast<const floatx4*>(C.rq + 16 * mt + 4 * g4);
+          o[mt][0] *= eg * rq;
+          o[mt][1] *= eg * rq;
         }
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
-          const typename M::frag x0 = acc_as_b<O>(x, s, 0), x1 = acc_as_b<O>(x, s, 1);
+          const Fr x0 = acc_as_b<O>(x, s, 0), x1 = acc_as_b<O>(x, s, 1);
 #pragma unroll
           for (int mt = 0; mt < 4; mt++) {
-            const typename M::frag pfrag = M::load(C.p, SM::LDP, 16 * mt, s * KS, lane);
+            const Fr pfrag = M::load(C.p, SM::LDP, 16 * mt, s * KS, lane);
             M::mma(o[mt][0], pfrag, x0);
             M::mma(o[mt][1], pfrag, x1);
           }
         }
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const int rb = 16 * mt + 4 * g4;
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            C.v[(rb + j) * SM::LDV + c0 + ln] = from_f<O>(o[mt][0][j]);
-            C.v[(rb + j) * SM::LDV + c0 + 16 + ln] = from_f<O>(o[mt][1][j]);
+            const int r = 16 * mt + 4 * g4 + j;
+            C.v[r * SM::LDV + c0 + ln] = from_f<O>(o[mt][0][j]);
+            C.v[r * SM::LDV + c0 + 16 + ln] = from_f<O>(o[mt][1][j]);
           }
         }
         // this wave's 32 columns of the 64 rows, as 16-byte pieces
@@ -787,37 +882,51 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         constexpr int VE = Vec16<E>::N;
         constexpr int PPR = 32 / VE;  // pieces per row
         const int64_t tc = tb + (int64_t)it * BT;
-        E* op = (E*)a.o + (int64_t)h * DV + c0;
+        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0);
 #pragma unroll
         for (int p = 0; p < BT * PPR / 64; p++) {
           const int i = lane + 64 * p;
           const int row = i / PPR, vi = i % PPR;
-          const int64_t t = tc + row;
-          if (t < te)
-            *reinterpret_cast<V16*>(op + t * (int64_t)Hv * DV + vi * VE) =
+          if (tc + row < te)
+            *reinterpret_cast<V16*>(op + row * o_ld + vi * VE) =
                 *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
         }
       }
       // S <- e^{G_C} S + k^T (rk e^{G_C - G} o v_new)
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
-        const int rb = 16 * mt + 4 * g4;
+        const floatx4 G = *reinterpret_cast<const floatx4*>(C.G + 16 * mt + 4 * g4);
+        const floatx4 rk = *reinterpret_cast<const floatx4*>(C.rk + 16 * mt + 4 * g4);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const float d = C.rk[rb + j] * __expf(GC - C.G[rb + j]);
+          const float d = rk[j] * __expf(GC - G[j]);
           x[mt][0][j] *= d;
           x[mt][1][j] *= d;
         }
       }
       const float eC = __expf(GC);
+      Fr xb[NSB][2];
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        xb[s][0] = acc_as_b<O>(x, s, 0);
+        xb[s][1] = acc_as_b<O>(x, s, 1);
+      }
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++) {
         floatx4 acc0 = S[mt][0] * eC, acc1 = S[mt][1] * eC;
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
-          const typename M::frag kf = M::load_col(C.k, SM::LDK, 16 * mt, s * KS, lane);
-          M::mma(acc0, kf, acc_as_b<O>(x, s, 0));
-          M::mma(acc1, kf, acc_as_b<O>(x, s, 1));
+          // A = k^T: dk rows 16 mt.., tokens s KS.. down the stored rows
+          Fr kf;
+          if constexpr (KS == 32) {
+            const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, 16 * mt, lane);
+            const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, 16 * mt, lane);
+            kf = Fr{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            kf = M::load_col(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          }
+          M::mma(acc0, kf, xb[s][0]);
+          M::mma(acc1, kf, xb[s][1]);
         }
         S[mt][0] = acc0;
         S[mt][1] = acc1;
@@ -836,7 +945,6 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
     dst = a.ht + ((int64_t)n * Hv + h) * DK * DV;
   }
   if (dst) {
-    const int g4 = lane0 >> 4, ln = lane0 & 15;
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll

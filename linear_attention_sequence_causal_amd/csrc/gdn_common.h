@@ -204,6 +204,10 @@ template <> struct Mfma<float> {
 template <typename O> struct Tile16;
 template <> struct Tile16<bf16> {
   typedef bf16x4 frag;
+  // A[row0 + l%16][k0 + 4g .. +3] of a bf16 array
+  GDN_DEV static frag load(const bf16* base, int ld, int row0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
+  }
   // A[row0 + l%16][k0 + 4g .. +3] of an fp32 array, times s
   GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, float s, int lane) {
     const floatx4 a = *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
@@ -224,12 +228,31 @@ template <> struct Tile16<bf16> {
 };
 template <> struct Tile16<float> {
   typedef floatx4 frag;
+  GDN_DEV static frag load(const float* base, int ld, int row0, int k0, int lane) {
+    return *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0));
+  }
   GDN_DEV static frag load_f32(const float* base, int ld, int row0, int k0, float s, int lane) {
     return *reinterpret_cast<const floatx4*>(base + ((lane & 15) * ld + 4 * (lane >> 4)) + (row0 * ld + k0)) * s;
   }
   GDN_DEV static frag from_acc(const floatx4& c) { return c; }
   GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) { Mfma<float>::mma(acc, a, b); }
 };
+
+// Transposed LDS read (ds_read_b64_tr_b16): from a row-major [rows][ld] bf16
+// array, lane l (group g = l/16, index i = l%16) receives the four elements
+// of column c0 + i in rows r0 + 4g + j, j = 0..3 -- a C-layout tile, or
+// half of an A fragment whose contraction index runs down the rows.  Within
+// each 16-lane group the instruction returns to lane i element i%4 of the
+// 8-byte vector read by lane 4j + i/4, so lane i points at row r0 + 4g +
+// i/4, columns c0 + 4(i%4) .. +3.  Addresses must be 8-byte aligned.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const bf16* p = base + ((4 * g + (i >> 2)) * ld + 4 * (i & 3)) + (r0 * ld + c0);
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -244,6 +267,34 @@ template <int WIDTH> GDN_DEV float group_sum(float v) {
 #pragma unroll
   for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
+}
+
+// Sum over aligned groups of W <= 16 consecutive lanes with DPP lane moves
+// (quad swaps, then the half-row and row mirrors), no LDS round trip.
+template <int CTRL> GDN_DEV float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int W> GDN_DEV float row_group_sum(float v) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16, "group of 1..16 lanes");
+  if constexpr (W >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (W >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  return v;
+}
+
+// Sum of squares of a 16-byte activation vector (bf16: pairwise dot
+// products accumulated in fp32).
+GDN_DEV float sum_sq(const floatx4& v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
+GDN_DEV float sum_sq(const bf16x8& v) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 pr{v[e], v[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+  }
+  return acc;
 }
 
 // sigmoid with the hardware exp2 and reciprocal (about 1 ulp each)
