@@ -154,8 +154,9 @@ def main():
     conv_b = conv_bytes_per_token(C, s_bytes) * T + C * K * s_bytes
     t_conv = per_call["conv_fwd"] * 1e-3
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                "kernel": "gdn_chunk_fwd (all launches of the call)"}
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": measured_traffic("chunk_fwd", spec.name),
+                "kernel": "gdn_chunk_fwd call: plan, segment summaries, scan, output pass"}
     chunk_hbm = chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
     extra = {
         "chunk_fwd_hbm": {"achieved": chunk_hbm / t_chunk / 1e9, "peak": HBM_PEAK / 1e9,
@@ -182,6 +183,21 @@ def main():
         "rooflines_other": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(call, workload):
+    """HBM bytes per call from the FETCH_SIZE / WRITE_SIZE counters stored
+    under profiles/, if they were taken on the kernels built from the current
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (call, workload))
+    if not os.path.exists(path):
+        return None
+    from linear_attention_sequence_causal_amd import profiling
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != profiling.source_digest():
+        return None
+    return rec["bytes_per_call"]
 
 
 def cpu_baseline(spec, inp, sample_tokens):

@@ -54,8 +54,8 @@ struct Smem {
 };
 
 // Global -> register prefetch of one chunk (q, k rows of q/k head `qa`, v
-// rows of value head `h`, g and beta of head h).
-template <typename E, int DK, int DV, int NT, bool HAS_Q>
+// rows of value head `h` unless HAS_V is false, g and beta of head h).
+template <typename E, int DK, int DV, int NT, bool HAS_Q, bool HAS_V = true>
 struct Prefetch {
   typedef typename Vec16<E>::type V16;
   static constexpr int VE = Vec16<E>::N;
@@ -64,10 +64,10 @@ struct Prefetch {
   static constexpr int QV = BT * QPR;
   static constexpr int VV = BT * VPR;
   static constexpr int PQ = (QV + NT - 1) / NT;
-  static constexpr int PV = (VV + NT - 1) / NT;
+  static constexpr int PV = HAS_V ? (VV + NT - 1) / NT : 0;
   V16 q[HAS_Q ? PQ : 1];
   V16 k[PQ];
-  V16 v[PV];
+  V16 v[PV > 0 ? PV : 1];
   float g, beta;
 
   GDN_DEV void load(const E* __restrict__ qp, const E* __restrict__ kp, int64_t ld_qk,

@@ -110,10 +110,10 @@ struct LoopCfg {
 
 // Register prefetch -> LDS as raw rows, plus the per-row l2norm factors and
 // the in-chunk cumsum of g.  Rows past the sequence end are zero.
-template <typename E, int DK, int DV, int NT, bool HAS_Q, class SM>
-GDN_DEV void stage_raw(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale, int use_l2norm,
-                       int tid) {
-  typedef Prefetch<E, DK, DV, NT, HAS_Q> PF;
+template <typename E, int DK, int DV, int NT, bool HAS_Q, bool HAS_V, class SM>
+GDN_DEV void stage_raw(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q, HAS_V>& pf, float scale,
+                       int use_l2norm, int tid) {
+  typedef Prefetch<E, DK, DV, NT, HAS_Q, HAS_V> PF;
   typedef typename Vec16<E>::type V16;
   constexpr int VE = PF::VE;
 #pragma unroll
@@ -285,7 +285,7 @@ void chunk_loop_kernel(LoopArgs a) {
     asm volatile("" : "+v"(tid_c));
     const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
     lds_barrier();  // the previous chunk's LDS readers are done
-    stage_raw<E, DK, DV, NT, CF::HAS_Q>(sm, pf, a.scale, a.use_l2norm, tid_c);
+    stage_raw(sm, pf, a.scale, a.use_l2norm, tid_c);
     if constexpr (MODE == kStates) {
       // the state entering this chunk, for the backward
       float* dst = a.states + ((int64_t)(a.seg_chunk0[seg] + c) * Hv + h) * DK * DV;
@@ -528,7 +528,8 @@ template <typename E, int DK, int DV, int MODE>
 struct WsCfg {
   static constexpr bool OUT = MODE == kOut;
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
-  static constexpr int NC = NSC / 32;                          // consumer waves
+  static constexpr int CW = 32;                                // columns per consumer wave
+  static constexpr int NC = NSC / CW;                          // consumer waves
   static constexpr int NP = 4;                                 // producer waves
   static constexpr int NT = (NC + NP) * 64;
   typedef WsSmem<E, DK, DV, OUT> SM;
@@ -591,6 +592,8 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef Tile16<O> T16;
   typedef typename M::frag Fr;
   constexpr int NC = CF::NC;
+  constexpr int CW = CF::CW;
+  constexpr int NN = CW / 16;  // 16-column tiles per consumer wave
   constexpr int KS = M::KSTEP;
   constexpr int NSK = DK / KS;  // contraction steps over dk
   constexpr int NSB = BT / KS;  // contraction steps over the chunk
@@ -641,19 +644,12 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       const int pc = it + 1;  // the chunk prepared
       SM& P = buf[pc & 1];
       if (pc < nchunks) {
-        stage_raw<E, DK, DV, CF::NP * 64, OUT>(P, pf, a.scale, a.use_l2norm, ptid);
+        stage_raw(P, pf, a.scale, a.use_l2norm, ptid);
         if (pc + 1 < nchunks)
           pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb + (int64_t)(pc + 1) * BT, te, ptid);
       }
       lds_barrier();
       if (pc < nchunks) {
-        // A operands read once per row block
-        Fr ak[NSK], aq[OUT ? NSK : 1];
-#pragma unroll
-        for (int s = 0; s < NSK; s++) {
-          ak[s] = M::load(P.k, SM::LDK, 16 * pw, s * KS, lane);
-          if constexpr (OUT) aq[s] = M::load(P.q, SM::LDK, 16 * iq, s * KS, lane);
-        }
         // Five independent tiles a wave: the diagonal L(pw,pw) and P(iq,iq),
         // and the three off-diagonal ones, L(pw, j < pw) then P(iq, j < iq).
         // Off the diagonal the decay factors as e^{G_r - G_0} e^{G_0 - G_c}
@@ -670,15 +666,21 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         floatx4 accD = zero4(), accDP = zero4(), accO[3];
 #pragma unroll
         for (int t = 0; t < 3; t++) accO[t] = zero4();
-#pragma unroll
+        // one contraction step at a time (kept rolled: the producer holds the
+        // next chunk's rows in registers meanwhile); each A operand serves
+        // every tile of its row block
+#pragma unroll 1
         for (int s = 0; s < NSK; s++) {
-          M::mma(accD, ak[s], M::load(P.k, SM::LDK, 16 * pw, s * KS, lane));
-          if constexpr (OUT) M::mma(accDP, aq[s], M::load(P.k, SM::LDK, 16 * iq, s * KS, lane));
+          const Fr ak = M::load(P.k, SM::LDK, 16 * pw, s * KS, lane);
+          Fr aq;
+          if constexpr (OUT) aq = M::load(P.q, SM::LDK, 16 * iq, s * KS, lane);
+          M::mma(accD, ak, M::load(P.k, SM::LDK, 16 * pw, s * KS, lane));
+          if constexpr (OUT) M::mma(accDP, aq, M::load(P.k, SM::LDK, 16 * iq, s * KS, lane));
 #pragma unroll
           for (int t = 0; t < 3; t++) {
             if (!OUT && t >= pw) break;
             const int j = t < pw ? t : t - pw;
-            M::mma(accO[t], t < pw ? ak[s] : aq[OUT ? s : 0], M::load(P.k, SM::LDK, 16 * j, s * KS, lane));
+            M::mma(accO[t], t < pw ? ak : aq, M::load(P.k, SM::LDK, 16 * j, s * KS, lane));
           }
         }
         // diagonal L tile: fp32 to the scratch (inversion), N off its blocks
@@ -740,11 +742,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   }
 
   // ======================= consumers =======================
-  const int c0 = wave * 32;                         // first state column of this wave
+  const int c0 = wave * CW;                         // first state column of this wave
   const bool mcol = MODE == kSummary && c0 < DK;    // wave holds columns of M (v = 0)
   const int vc0 = MODE == kSummary ? c0 - DK : c0;  // value column of the first column
   // state tiles S[mt][nt]: rows 16mt + 4(lane/16) + j, cols c0 + 16nt + lane%16
-  floatx4 S[DKT][2];
+  floatx4 S[DKT][NN];
   {
     const float* src = nullptr;
     if (MODE != kSummary) {
@@ -754,7 +756,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++)
+      for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
@@ -765,7 +767,9 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         }
   }
   const int64_t o_ld = (int64_t)Hv * DV;
-  floatx4 x[4][2];
+  typedef typename Vec16<E>::type V16;
+  constexpr int VE = Vec16<E>::N;
+  floatx4 x[4][NN], o[OUT ? 4 : 1][NN];
   for (int it = -1; it < nchunks; it++) {
     SM& C = buf[it & 1];
 
@@ -777,32 +781,45 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
         for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-          for (int nt = 0; nt < 2; nt++)
+          for (int nt = 0; nt < NN; nt++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
               dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
       }
-      // right-hand side beta o (v - e^G o rk o (k S)) for this wave's columns;
-      // k S accumulates in x, one contraction step of S's operand at a time
+      // k S (into x) and q S (into o), one contraction step of S's operand
+      // at a time
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) x[mt][0] = x[mt][1] = zero4();
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          x[mt][nt] = zero4();
+          if constexpr (OUT) o[mt][nt] = zero4();
+        }
 #pragma unroll
       for (int s = 0; s < NSK; s++) {
-        const Fr b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
+        Fr b[NN];
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) b[nt] = acc_as_b<O>(S, s, nt);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
           const Fr kf = M::load(C.k, SM::LDK, 16 * mt, s * KS, lane);
-          M::mma(x[mt][0], kf, b0);
-          M::mma(x[mt][1], kf, b1);
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
+          if constexpr (OUT) {
+            const Fr qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
+#pragma unroll
+            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], qf, b[nt]);
+          }
         }
       }
+      // right-hand side beta o (v - e^G o rk o (k S)) for this wave's columns
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
         const floatx4 bt = *reinterpret_cast<const floatx4*>(C.beta + 16 * mt + 4 * g4);
         const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
         const floatx4 rk = *reinterpret_cast<const floatx4*>(C.rk + 16 * mt + 4 * g4);
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
+        for (int nt = 0; nt < NN; nt++) {
           bf16x4 vv;
           if (!mcol) vv = lds_rows4_tr(C.v, SM::LDV, 16 * mt, vc0 + 16 * nt, lane);
 #pragma unroll
@@ -819,15 +836,16 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
         for (int m = 0; m < i; m++) {
           const typename T16::frag nf = T16::load(C.n, SM::LDP, 16 * i, 16 * m, lane);
-          T16::mma(x[i][0], nf, T16::from_acc(x[m][0]));
-          T16::mma(x[i][1], nf, T16::from_acc(x[m][1]));
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) T16::mma(x[i][nt], nf, T16::from_acc(x[m][nt]));
         }
         const typename T16::frag df = T16::load(C.n, SM::LDP, 16 * i, 16 * i, lane);
-        floatx4 y0 = zero4(), y1 = zero4();
-        T16::mma(y0, df, T16::from_acc(x[i][0]));
-        T16::mma(y1, df, T16::from_acc(x[i][1]));
-        x[i][0] = y0;
-        x[i][1] = y1;
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          floatx4 y = zero4();
+          T16::mma(y, df, T16::from_acc(x[i][nt]));
+          x[i][nt] = y;
+        }
       }
     }
     lds_barrier();
@@ -837,50 +855,35 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       const float GC = C.G[BT - 1];
       if constexpr (OUT) {
         // o = (rq e^G) o (q S) + P v_new, staged over this wave's columns of v
-        floatx4 o[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) o[mt][0] = o[mt][1] = zero4();
-#pragma unroll
-        for (int s = 0; s < NSK; s++) {
-          const Fr b0 = acc_as_b<O>(S, s, 0), b1 = acc_as_b<O>(S, s, 1);
-#pragma unroll
-          for (int mt = 0; mt < 4; mt++) {
-            const Fr qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
-            M::mma(o[mt][0], qf, b0);
-            M::mma(o[mt][1], qf, b1);
-          }
-        }
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
           const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
           const floatx4 rq = *reinterpret_cast<const floatx4*>(C.rq + 16 * mt + 4 * g4);
-          o[mt][0] *= eg * rq;
-          o[mt][1] *= eg * rq;
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) o[mt][nt] *= eg * rq;
         }
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
-          const Fr x0 = acc_as_b<O>(x, s, 0), x1 = acc_as_b<O>(x, s, 1);
+          Fr xs[NN];
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) xs[nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
           for (int mt = 0; mt < 4; mt++) {
             const Fr pfrag = M::load(C.p, SM::LDP, 16 * mt, s * KS, lane);
-            M::mma(o[mt][0], pfrag, x0);
-            M::mma(o[mt][1], pfrag, x1);
+#pragma unroll
+            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], pfrag, xs[nt]);
           }
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
+        for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int r = 16 * mt + 4 * g4 + j;
-            C.v[r * SM::LDV + c0 + ln] = from_f<O>(o[mt][0][j]);
-            C.v[r * SM::LDV + c0 + 16 + ln] = from_f<O>(o[mt][1][j]);
-          }
-        }
-        // this wave's 32 columns of the 64 rows, as 16-byte pieces
+          for (int nt = 0; nt < NN; nt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              C.v[(16 * mt + 4 * g4 + j) * SM::LDV + c0 + 16 * nt + ln] = from_f<O>(o[mt][nt][j]);
+        // this wave's columns of the 64 rows, as 16-byte pieces
         wave_lds_sync();
-        typedef typename Vec16<E>::type V16;
-        constexpr int VE = Vec16<E>::N;
-        constexpr int PPR = 32 / VE;  // pieces per row
+        constexpr int PPR = CW / VE;  // pieces per row
         const int64_t tc = tb + (int64_t)it * BT;
         E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0);
 #pragma unroll
@@ -900,20 +903,21 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const float d = rk[j] * __expf(GC - G[j]);
-          x[mt][0][j] *= d;
-          x[mt][1][j] *= d;
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) x[mt][nt][j] *= d;
         }
       }
       const float eC = __expf(GC);
-      Fr xb[NSB][2];
+      Fr xb[NSB][NN];
 #pragma unroll
-      for (int s = 0; s < NSB; s++) {
-        xb[s][0] = acc_as_b<O>(x, s, 0);
-        xb[s][1] = acc_as_b<O>(x, s, 1);
-      }
+      for (int s = 0; s < NSB; s++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) xb[s][nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++) {
-        floatx4 acc0 = S[mt][0] * eC, acc1 = S[mt][1] * eC;
+        floatx4 acc[NN];
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) acc[nt] = S[mt][nt] * eC;
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
           // A = k^T: dk rows 16 mt.., tokens s KS.. down the stored rows
@@ -925,11 +929,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           } else {
             kf = M::load_col(C.k, SM::LDK, 16 * mt, s * KS, lane);
           }
-          M::mma(acc0, kf, xb[s][0]);
-          M::mma(acc1, kf, xb[s][1]);
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xb[s][nt]);
         }
-        S[mt][0] = acc0;
-        S[mt][1] = acc1;
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
       }
     }
     lds_barrier();
@@ -948,7 +952,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++)
+      for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
