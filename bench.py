@@ -207,10 +207,10 @@ def cpu_baseline(spec, inp, sample_tokens):
     from oracle import capi
     T = inp["T"]
     if sample_tokens <= 0:
-        # ~7*dk*dv fp64 FLOP per token and head; aim for ~15 s at ~1 GFLOP/s/thread
+        # ~7*dk*dv fp64 FLOP per token and head; aim for ~15 s at ~2.5 GFLOP/s/thread
         thr = capi.max_threads()
         per_tok = 7.0 * spec.dk * spec.dv * spec.Hv
-        sample_tokens = int(min(T, max(256, 15 * 1e9 * min(thr, spec.Hv) / per_tok)))
+        sample_tokens = int(min(T, max(256, 15 * 2.5e9 * min(thr, spec.Hv) / per_tok)))
     n = min(sample_tokens, T)
     x = inp["x"][:n].double().numpy()
     w = inp["w"].double().numpy()
