@@ -129,8 +129,14 @@ inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) 
   if (env && atoi(env) > 0) {
     per = atoi(env);
   } else {
-    const int64_t cus = gdn::device_cu_count();
-    per = (chunks * Hv + cus - 1) / cus;  // chunks per workgroup for one wave of the GPU
+    // One workgroup per CU (the chunk loop holds most of a CU's LDS), and a
+    // few CUs may be held back from a queue: plan for 15/16 of them, so every
+    // segment of a pass is resident at once.  Segments per head: with N
+    // sequences of C chunks in all, at most ceil(C / per) + N - 1.
+    const int64_t slots = gdn::device_cu_count() * 15 / 16;
+    const int64_t budget = slots / Hv > 1 ? slots / Hv : 1;
+    const int64_t C = (T + 63) / 64 + N - 1;
+    per = budget > N ? (C + (budget - N + 1) - 1) / (budget - N + 1) : C + 1;
     if (per < 1) per = 1;
   }
   p.seg_len = per * 64;
