@@ -40,7 +40,8 @@ namespace gdn {
 int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, const void* v,
                    int64_t ld_v, const float* g, const float* beta, const int32_t* cu, int32_t N,
                    int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
-size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv);
+size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
+size_t chunk_rec_bytes(gdn_dtype dt);
 }  // namespace gdn
 
 namespace {
@@ -692,9 +693,9 @@ struct BwdLayout {
   size_t off_states, off_dstates, off_dqk, end;
 };
 
-BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) {
+BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
   BwdLayout L;
-  L.plan = make_plan(T, N, Hv, dk, dv);
+  L.plan = make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt));
   size_t o = L.plan.end;
   const size_t st = sizeof(float) * (size_t)L.plan.chunk_cap * Hv * dk * dv;
   L.off_states = o;
@@ -744,10 +745,9 @@ __global__ __launch_bounds__(256) void copy_or_zero_kernel(const float* __restri
 extern "C" size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv,
                                            int32_t dk, int32_t dv, gdn_dtype dt, int bwd) {
   (void)Hk;
-  (void)dt;
   if (T < 0 || N < 0 || Hv < 1 || dk < 1 || dv < 1) return 0;
-  if (!bwd) return gdn::chunk_fwd_workspace(T, N, Hv, dk, dv);
-  return bwd_layout(T, N, Hv, dk, dv).end;
+  if (!bwd) return gdn::chunk_fwd_workspace(T, N, Hv, dk, dv, dt);
+  return bwd_layout(T, N, Hv, dk, dv, dt).end;
 }
 
 extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v,
@@ -770,7 +770,7 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const 
     return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: null gradient pointer");
   if (ld_dqk < (int64_t)Hk * dk || ld_dv < (int64_t)Hv * dv)
     return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: gradient row strides smaller than the head blocks");
-  const BwdLayout L = bwd_layout(T, N, Hv, dk, dv);
+  const BwdLayout L = bwd_layout(T, N, Hv, dk, dv, dt);
   if (!ws || ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_bwd: workspace needs %zu bytes, 256-byte aligned",
                      L.end);

@@ -42,6 +42,7 @@
 
 #include "chunk_common.h"
 #include "chunk_plan.h"
+#include "chunk_prep.h"
 #include "gdn_internal.h"
 
 namespace gdn_chunk {
@@ -69,6 +70,7 @@ struct LoopArgs {
   float* seg_state;  // [seg_cap][Hv][DK][DK+DV] summaries
   float* seg_init;   // [seg_cap][Hv][DK][DV] initial states of non-first segments
   float* states;     // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk
+  const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
 };
 
 // LDS of the chunk loop (one chunk of one head at a time; rows padded by
@@ -472,56 +474,31 @@ void chunk_loop_kernel(LoopArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Producer/consumer form of the chunk loop (bf16 activations).
+// State pass over prepared chunks (bf16 activations).
 //
-// The per-chunk work splits into a state-independent part (stage the rows,
-// the l2norm factors and the cumsum of g, the gram tiles L and P, the
-// inverted diagonal blocks D) and the chain through the state (k S, the
-// substitution, q S + P v_new, the state update).  A workgroup holds NC
-// consumer waves, each owning 32 state columns, and four producer waves that
-// prepare chunk c + 1 into one of two LDS buffers while the consumers run
-// chunk c from the other, so every SIMD interleaves a producer and a consumer
-// wave.  Each iteration has two phases separated by workgroup barriers:
-//   phase 1  producers: prefetched rows -> LDS (raw q, k, v), row factors,
-//            G, beta, e^G; then the global loads of the chunk after next;
-//            consumers: (k S), right-hand side, blocked substitution;
-//   phase 2  producers: L tiles of row block pw and P tiles of row block
-//            3 - pw (five tiles per wave), then D_pw from their own L_pw,pw;
-//            consumers: o = (rq e^G) o (q S) + P v_new stored from LDS
-//            staging of their own columns, S <- e^{G_C} S + k^T (d o v_new).
-// A buffer written by producers in iteration i is read by consumers in
-// iteration i + 1 and rewritten in iteration i + 2, after two barriers.
-//
-// The substitution operands are stored ready for the matrix cores: N =
-// -diag(beta) L off the diagonal and D on it, both bf16 (the rounding the
-// bf16 products apply anyway).  Operands whose contraction index runs down
-// the stored rows (k^T in the state update, v in C layout) are read with the
-// transposing LDS load.
+// chunk_prep.h has produced, for every (chunk, value head), the record of
+// state-independent operators.  What is left per chunk is the chain through
+// the state:
+//   x = k S and o = q S (S's accumulators are the B operands directly),
+//   x_i = A_i v_i - B_i x_i - sum_{m<i} E_im x_m over the four 16-row blocks,
+//   o = fo o o + P x  (staged through LDS, written as 16-byte row pieces),
+//   S <- eC S + k^T (fd o x)  (k^T read with the transposing LDS load).
+// A workgroup owns one (segment, value head) and holds NC consumer waves, each
+// owning 32 state columns as MFMA accumulator tiles, plus four loader waves
+// that copy chunk c + 1 (rows of q, k, v and the record) into one of two LDS
+// buffers while the consumers run chunk c from the other.  One workgroup
+// barrier per chunk separates the two.
 
-// LDS of one buffer.  Per-row arrays first: ds immediate offsets reach 64 KiB.
+// One LDS buffer: raw rows (16-byte padded) and the record.
 template <typename O, int DK, int DV, bool HAS_Q>
 struct WsSmem {
   static constexpr int PAD = 16 / (int)sizeof(O);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDV = DV + PAD;
-  static constexpr int LDP = BT + PAD;
-  alignas(16) float G[BT];
-  alignas(16) float beta[BT];
-  alignas(16) float eg[BT];  // exp(G)
-  alignas(16) float rq[BT];  // scale / |q| (scale without l2norm)
-  alignas(16) float rk[BT];  // 1 / |k| (1 without l2norm)
-  alignas(16) O n[BT * LDP];  // -beta_r L[r][c] below the diagonal blocks, D_b on them
-  alignas(16) O p[HAS_Q ? BT * LDP : 8];
+  alignas(16) char rec[kRecBytes];
   alignas(16) O k[BT * LDK];
   alignas(16) O q[HAS_Q ? BT * LDK : 8];
   alignas(16) O v[BT * LDV];
-};
-
-// Producer scratch for the diagonal inversion (one set per producer wave,
-// used within one phase): the fp32 L_bb tile and a work tile.
-constexpr int kScLd = 20;  // 16 + 4 floats: 16-byte aligned rows
-struct WsScratch {
-  alignas(16) float t[4][2][16 * kScLd];
 };
 
 template <typename E, int DK, int DV, int MODE>
@@ -530,59 +507,74 @@ struct WsCfg {
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
   static constexpr int CW = 32;                                // columns per consumer wave
   static constexpr int NC = NSC / CW;                          // consumer waves
-  static constexpr int NP = 4;                                 // producer waves
-  static constexpr int NT = (NC + NP) * 64;
+  static constexpr int NL = 4;                                 // loader waves
+  static constexpr int NT = (NC + NL) * 64;
   typedef WsSmem<E, DK, DV, OUT> SM;
-  typedef Prefetch<E, DK, DV, NP * 64, OUT> PF;
-  // both buffers and the scratch within the 160 KiB of LDS of a CU
-  static constexpr bool FITS = 2 * sizeof(SM) + sizeof(WsScratch) <= 160 * 1024;
+  // bytes of the record the consumers read (P only for the output)
+  static constexpr int REC0 = OUT ? 0 : kRecA;
+  static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
 };
 
-// Make this wave's LDS writes visible to its own later reads from other lanes.
-GDN_DEV void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Loader registers: one chunk's rows and record, 16-byte vectors.
+template <typename E, int DK, int DV, bool HAS_Q, int REC0>
+struct WsLoad {
+  typedef typename Vec16<E>::type V16;
+  static constexpr int NTL = 256;  // loader threads
+  static constexpr int VE = Vec16<E>::N;
+  static constexpr int QPR = DK / VE, VPR = DV / VE;
+  static constexpr int PQ = BT * QPR / NTL, PV = BT * VPR / NTL;
+  static constexpr int RV = (kRecBytes - REC0) / 16;  // record vectors
+  static constexpr int PR = (RV + NTL - 1) / NTL;
+  static_assert(BT * QPR % NTL == 0 && BT * VPR % NTL == 0, "loader split");
+  V16 q[HAS_Q ? PQ : 1], k[PQ], v[PV];
+  floatx4 r[PR];
 
-// D = (I + N)^-1 for N = diag(bb) L, L strictly lower 16x16, so N^16 = 0 and
-// (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8): six fp32 products on the
-// matrix cores by one whole wave.  Lt: L in fp32 [16][kScLd] (A operands are
-// read from it), NC: N in C layout (N[4(lane/16)+j][lane%16]), sc: a work
-// tile.  The C layout of a product is the B operand of the next.  Returns D
-// in C layout.
-GDN_DEV floatx4 invert_unit_lower16(const float* Lt, const float* bb, const floatx4& NC, float* sc,
-                                    int lane) {
-  typedef Tile16<float> F;
-  const int g4 = lane >> 4, ln = lane & 15;
-  const floatx4 NA = F::load_f32(Lt, kScLd, 0, 0, bb[ln], lane);  // A[r][k] = beta_r L[r][k]
-  floatx4 N2 = zero4();
-  F::mma(N2, NA, NC);
+  GDN_DEV void load(const E* qp, const E* kp, int64_t ld_qk, const E* vp, int64_t ld_v,
+                    const char* rec, int64_t tc, int64_t te, int tid) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kScLd + ln] = N2[j];
-  wave_lds_sync();
-  const floatx4 N2A = F::load(sc, kScLd, 0, 0, lane);
-  floatx4 N4 = zero4();
-  F::mma(N4, N2A, N2);
-  wave_lds_sync();  // every lane has read N^2 before it is overwritten
+    for (int p = 0; p < PQ; p++) {
+      const int i = tid + NTL * p;
+      const int row = i / QPR, vi = i % QPR;
+      const int64_t t = tc + row;
+      const bool ok = t < te;
+      if constexpr (HAS_Q) q[p] = ok ? *reinterpret_cast<const V16*>(qp + t * ld_qk + vi * VE) : zero_vec16<E>();
+      k[p] = ok ? *reinterpret_cast<const V16*>(kp + t * ld_qk + vi * VE) : zero_vec16<E>();
+    }
 #pragma unroll
-  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kScLd + ln] = N4[j];
-  wave_lds_sync();
-  const floatx4 N4A = F::load(sc, kScLd, 0, 0, lane);
-  floatx4 N8 = zero4();
-  F::mma(N8, N4A, N4);
-  // R1 = (I + N^4)(I + N^8), R2 = (I + N^2) R1, D = (I - N) R2
-  floatx4 R1 = N4 + N8;
+    for (int p = 0; p < PV; p++) {
+      const int i = tid + NTL * p;
+      const int row = i / VPR, vi = i % VPR;
+      const int64_t t = tc + row;
+      v[p] = t < te ? *reinterpret_cast<const V16*>(vp + t * ld_v + vi * VE) : zero_vec16<E>();
+    }
 #pragma unroll
-  for (int j = 0; j < 4; j++) R1[j] += (4 * g4 + j == ln) ? 1.f : 0.f;
-  F::mma(R1, N4A, N8);
-  floatx4 R2 = R1;
-  F::mma(R2, N2A, R1);
-  floatx4 t = zero4();
-  F::mma(t, NA, R2);
-  return R2 - t;
-}
+    for (int p = 0; p < PR; p++) {
+      const int i = tid + NTL * p;
+      if (i < RV) r[p] = *reinterpret_cast<const floatx4*>(rec + REC0 + 16 * i);
+    }
+  }
+  template <class SM>
+  GDN_DEV void store(SM& sm, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PQ; p++) {
+      const int i = tid + NTL * p;
+      const int row = i / QPR, vi = i % QPR;
+      if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vi * VE) = q[p];
+      *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vi * VE) = k[p];
+    }
+#pragma unroll
+    for (int p = 0; p < PV; p++) {
+      const int i = tid + NTL * p;
+      const int row = i / VPR, vi = i % VPR;
+      *reinterpret_cast<V16*>(sm.v + row * SM::LDV + vi * VE) = v[p];
+    }
+#pragma unroll
+    for (int p = 0; p < PR; p++) {
+      const int i = tid + NTL * p;
+      if (i < RV) *reinterpret_cast<floatx4*>(sm.rec + REC0 + 16 * i) = r[p];
+    }
+  }
+};
 
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
@@ -591,17 +583,18 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef Mfma<O> M;
   typedef Tile16<O> T16;
   typedef typename M::frag Fr;
+  typedef typename T16::frag Fr16;
   constexpr int NC = CF::NC;
   constexpr int CW = CF::CW;
-  constexpr int NN = CW / 16;  // 16-column tiles per consumer wave
-  constexpr int KS = M::KSTEP;
+  constexpr int NN = CW / 16;   // 16-column tiles per consumer wave
+  constexpr int KS = M::KSTEP;  // 32
   constexpr int NSK = DK / KS;  // contraction steps over dk
   constexpr int NSB = BT / KS;  // contraction steps over the chunk
   constexpr int DKT = DK / 16;  // state row tiles
   constexpr bool OUT = CF::OUT;
   typedef typename CF::SM SM;
+  static_assert(KS == 32, "bf16 fragments");
   __shared__ SM buf[2];
-  __shared__ WsScratch scr;
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= a.counts[0]) return;
@@ -614,127 +607,27 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g4 = lane >> 4, ln = lane & 15;
   const int nchunks = (int)((te - tb + BT - 1) / BT);
+  const int chunk0 = a.seg_chunk0[seg];
+  const char* recs = a.rec + (int64_t)h * kRecBytes;  // + chunk * Hv * kRecBytes
 
-  // upper tiles of P stay zero in both buffers
-  if constexpr (OUT)
-    for (int e = tid; e < 2 * BT * BT; e += CF::NT) {
-      const int b = e / (BT * BT), r = (e / BT) % BT, c = e % BT;
-      if ((c >> 4) > (r >> 4)) buf[b].p[r * SM::LDP + c] = from_f<O>(0.f);
-    }
-
-  // The two roles run separate loops with the same barrier sequence (two per
-  // iteration, iterations -1 .. nchunks-1), so each keeps only its own
-  // registers live.
   if (wave >= NC) {
-    // ======================= producers =======================
-    const int pw = wave - NC;  // L row block; P row block 3 - pw
-    const int iq = 3 - pw;
-    const int ptid = tid - NC * 64;
+    // ======================= loaders =======================
+    typedef WsLoad<E, DK, DV, OUT, CF::REC0> LD;
+    const int ltid = tid - NC * 64;
     const int qa = h / (Hv / a.Hk);
     const E* qp = (const E*)a.q + (int64_t)qa * DK;
     const E* kp = (const E*)a.k + (int64_t)qa * DK;
     const E* vp = (const E*)a.v + (int64_t)h * DV;
-    const float* gp = a.g + h;
-    const float* bp = a.beta + h;
-    float* Lt = scr.t[pw][0];
-    float* sc = scr.t[pw][1];
-    typename CF::PF pf;
-    if (nchunks > 0) pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb, te, ptid);
+    const int64_t rstride = (int64_t)Hv * kRecBytes;
+    LD ld;
+    if (nchunks > 0) ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + chunk0 * rstride, tb, te, ltid);
     for (int it = -1; it < nchunks; it++) {
-      const int pc = it + 1;  // the chunk prepared
-      SM& P = buf[pc & 1];
+      const int pc = it + 1;
       if (pc < nchunks) {
-        stage_raw(P, pf, a.scale, a.use_l2norm, ptid);
+        ld.store(buf[pc & 1], ltid);
         if (pc + 1 < nchunks)
-          pf.load(qp, kp, a.ld_qk, vp, a.ld_v, gp, bp, Hv, tb + (int64_t)(pc + 1) * BT, te, ptid);
-      }
-      lds_barrier();
-      if (pc < nchunks) {
-        // Five independent tiles a wave: the diagonal L(pw,pw) and P(iq,iq),
-        // and the three off-diagonal ones, L(pw, j < pw) then P(iq, j < iq).
-        // Off the diagonal the decay factors as e^{G_r - G_0} e^{G_0 - G_c}
-        // with G_0 = G at the row block's first row: both factors <= 1.
-        const int rL = 16 * pw + 4 * g4, rP = 16 * iq + 4 * g4;  // this lane's first rows
-        floatx4 GL, fL, bL, GP, fP;
-        GL = *reinterpret_cast<const floatx4*>(P.G + rL);
-        fL = *reinterpret_cast<const floatx4*>(P.rk + rL);
-        bL = *reinterpret_cast<const floatx4*>(P.beta + rL);
-        if constexpr (OUT) {
-          GP = *reinterpret_cast<const floatx4*>(P.G + rP);
-          fP = *reinterpret_cast<const floatx4*>(P.rq + rP);
-        }
-        floatx4 accD = zero4(), accDP = zero4(), accO[3];
-#pragma unroll
-        for (int t = 0; t < 3; t++) accO[t] = zero4();
-        // one contraction step at a time (kept rolled: the producer holds the
-        // next chunk's rows in registers meanwhile); each A operand serves
-        // every tile of its row block
-#pragma unroll 1
-        for (int s = 0; s < NSK; s++) {
-          const Fr ak = M::load(P.k, SM::LDK, 16 * pw, s * KS, lane);
-          Fr aq;
-          if constexpr (OUT) aq = M::load(P.q, SM::LDK, 16 * iq, s * KS, lane);
-          M::mma(accD, ak, M::load(P.k, SM::LDK, 16 * pw, s * KS, lane));
-          if constexpr (OUT) M::mma(accDP, aq, M::load(P.k, SM::LDK, 16 * iq, s * KS, lane));
-#pragma unroll
-          for (int t = 0; t < 3; t++) {
-            if (!OUT && t >= pw) break;
-            const int j = t < pw ? t : t - pw;
-            M::mma(accO[t], t < pw ? ak : aq, M::load(P.k, SM::LDK, 16 * j, s * KS, lane));
-          }
-        }
-        // diagonal L tile: fp32 to the scratch (inversion), N off its blocks
-        floatx4 NCd;
-        {
-          const int col = 16 * pw + ln;
-          const float Gc = P.G[col], fc = P.rk[col];
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const int row = rL + jj;
-            const float e = __expf(fminf(GL[jj] - Gc, 0.f));  // clamped: masked entries stay finite
-            const float val = row > col ? accD[jj] * fL[jj] * fc * e : 0.f;
-            Lt[(4 * g4 + jj) * kScLd + ln] = val;
-            NCd[jj] = bL[jj] * val;
-          }
-        }
-        if constexpr (OUT) {
-          const int col = 16 * iq + ln;
-          const float Gc = P.G[col], fc = P.rk[col];
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const int row = rP + jj;
-            const float e = __expf(fminf(GP[jj] - Gc, 0.f));
-            P.p[row * SM::LDP + col] = from_f<O>(row >= col ? accDP[jj] * fP[jj] * fc * e : 0.f);
-          }
-        }
-        {
-          const float G0L = P.G[16 * pw], G0P = OUT ? P.G[16 * iq] : 0.f;
-          floatx4 aL, aP;
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            aL[jj] = -bL[jj] * fL[jj] * __expf(GL[jj] - G0L);
-            if constexpr (OUT) aP[jj] = fP[jj] * __expf(GP[jj] - G0P);
-          }
-#pragma unroll
-          for (int t = 0; t < 3; t++) {
-            if (!OUT && t >= pw) break;
-            const bool isL = t < pw;
-            const int j = isL ? t : t - pw;
-            const int col = 16 * j + ln;
-            const float bc = P.rk[col] * __expf((isL ? G0L : G0P) - P.G[col]);
-            O* dst = isL ? P.n : P.p;
-            const int r0 = isL ? rL : rP;
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++)
-              dst[(r0 + jj) * SM::LDP + col] = from_f<O>(accO[t][jj] * (isL ? aL[jj] : aP[jj]) * bc);
-          }
-        }
-        // D_pw = (I + diag(beta) L_pw,pw)^-1, written as bf16 on the diagonal
-        wave_lds_sync();
-        const floatx4 D = invert_unit_lower16(Lt, P.beta + 16 * pw, NCd, sc, lane);
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++)
-          P.n[(16 * pw + 4 * g4 + jj) * SM::LDP + 16 * pw + ln] = from_f<O>(D[jj]);
+          ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (chunk0 + pc + 1) * rstride,
+                  tb + (int64_t)(pc + 1) * BT, te, ltid);
       }
       lds_barrier();
     }
@@ -771,13 +664,12 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   constexpr int VE = Vec16<E>::N;
   floatx4 x[4][NN], o[OUT ? 4 : 1][NN];
   for (int it = -1; it < nchunks; it++) {
-    SM& C = buf[it & 1];
-
-    // ---------------- phase 1: k S, right-hand side, substitution
     if (it >= 0) {
+      SM& C = buf[it & 1];
+      const char* R = C.rec;
       if constexpr (MODE == kStates) {
         // the state entering this chunk, for the backward
-        float* dst = a.states + ((int64_t)(a.seg_chunk0[seg] + it) * Hv + h) * DK * DV;
+        float* dst = a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
 #pragma unroll
         for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
@@ -786,8 +678,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
             for (int j = 0; j < 4; j++)
               dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
       }
-      // k S (into x) and q S (into o), one contraction step of S's operand
-      // at a time
+      // k S (into x) and q S (into o), one contraction step of S at a time
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)
 #pragma unroll
@@ -812,55 +703,38 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           }
         }
       }
-      // right-hand side beta o (v - e^G o rk o (k S)) for this wave's columns
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        const floatx4 bt = *reinterpret_cast<const floatx4*>(C.beta + 16 * mt + 4 * g4);
-        const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
-        const floatx4 rk = *reinterpret_cast<const floatx4*>(C.rk + 16 * mt + 4 * g4);
-#pragma unroll
-        for (int nt = 0; nt < NN; nt++) {
-          bf16x4 vv;
-          if (!mcol) vv = lds_rows4_tr(C.v, SM::LDV, 16 * mt, vc0 + 16 * nt, lane);
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const float v = mcol ? 0.f : (float)vv[j];
-            x[mt][nt][j] = bt[j] * (v - eg[j] * rk[j] * x[mt][nt][j]);
-          }
-        }
-      }
-      // v_new = (I + diag(beta) L)^-1 rhs by block rows:
-      // x_i <- D_i (x_i + sum_{m<i} N_im x_m),  N = -diag(beta) L
+      // x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m
+      Fr16 xb[4][NN];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-#pragma unroll
-        for (int m = 0; m < i; m++) {
-          const typename T16::frag nf = T16::load(C.n, SM::LDP, 16 * i, 16 * m, lane);
-#pragma unroll
-          for (int nt = 0; nt < NN; nt++) T16::mma(x[i][nt], nf, T16::from_acc(x[m][nt]));
-        }
-        const typename T16::frag df = T16::load(C.n, SM::LDP, 16 * i, 16 * i, lane);
+        const Fr16 fa = *reinterpret_cast<const Fr16*>(R + kRecA + i * 512 + lane * 8);
+        const Fr16 fb = *reinterpret_cast<const Fr16*>(R + kRecNB + i * 512 + lane * 8);
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) {
-          floatx4 y = zero4();
-          T16::mma(y, df, T16::from_acc(x[i][nt]));
-          x[i][nt] = y;
+          floatx4 acc = zero4();
+          if (!mcol) T16::mma(acc, fa, lds_rows4_tr(C.v, SM::LDV, 16 * i, vc0 + 16 * nt, lane));
+          T16::mma(acc, fb, T16::from_acc(x[i][nt]));
+          x[i][nt] = acc;
         }
+#pragma unroll
+        for (int m = 0; m < i; m++) {
+          const Fr16 fe = *reinterpret_cast<const Fr16*>(R + kRecNE + e_pair(i, m) * 512 + lane * 8);
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) T16::mma(x[i][nt], fe, xb[m][nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) xb[i][nt] = T16::from_acc(x[i][nt]);
       }
-    }
-    lds_barrier();
-
-    // ---------------- phase 2: output, state update
-    if (it >= 0) {
-      const float GC = C.G[BT - 1];
+      const float* Fo = reinterpret_cast<const float*>(R + kRecF);
+      const float* Fd = Fo + 64;
+      const float eC = Fo[128];
       if constexpr (OUT) {
-        // o = (rq e^G) o (q S) + P v_new, staged over this wave's columns of v
+        // o = fo o (q S) + P x, staged over this wave's columns of v
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const floatx4 eg = *reinterpret_cast<const floatx4*>(C.eg + 16 * mt + 4 * g4);
-          const floatx4 rq = *reinterpret_cast<const floatx4*>(C.rq + 16 * mt + 4 * g4);
+          const floatx4 fo = *reinterpret_cast<const floatx4*>(Fo + 16 * mt + 4 * g4);
 #pragma unroll
-          for (int nt = 0; nt < NN; nt++) o[mt][nt] *= eg * rq;
+          for (int nt = 0; nt < NN; nt++) o[mt][nt] *= fo;
         }
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
@@ -868,10 +742,10 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) xs[nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
-          for (int mt = 0; mt < 4; mt++) {
-            const Fr pfrag = M::load(C.p, SM::LDP, 16 * mt, s * KS, lane);
+          for (int mt = 2 * s; mt < 4; mt++) {
+            const Fr pf = *reinterpret_cast<const Fr*>(R + kRecP + p_frag(mt, s) * 1024 + lane * 16);
 #pragma unroll
-            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], pfrag, xs[nt]);
+            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], pf, xs[nt]);
           }
         }
 #pragma unroll
@@ -895,24 +769,18 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
                 *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
         }
       }
-      // S <- e^{G_C} S + k^T (rk e^{G_C - G} o v_new)
+      // S <- eC S + k^T (fd o x)
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
-        const floatx4 G = *reinterpret_cast<const floatx4*>(C.G + 16 * mt + 4 * g4);
-        const floatx4 rk = *reinterpret_cast<const floatx4*>(C.rk + 16 * mt + 4 * g4);
+        const floatx4 fd = *reinterpret_cast<const floatx4*>(Fd + 16 * mt + 4 * g4);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float d = rk[j] * __expf(GC - G[j]);
-#pragma unroll
-          for (int nt = 0; nt < NN; nt++) x[mt][nt][j] *= d;
-        }
+        for (int nt = 0; nt < NN; nt++) x[mt][nt] *= fd;
       }
-      const float eC = __expf(GC);
-      Fr xb[NSB][NN];
+      Fr xv[NSB][NN];
 #pragma unroll
       for (int s = 0; s < NSB; s++)
 #pragma unroll
-        for (int nt = 0; nt < NN; nt++) xb[s][nt] = acc_as_b<O>(x, s, nt);
+        for (int nt = 0; nt < NN; nt++) xv[s][nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++) {
         floatx4 acc[NN];
@@ -921,16 +789,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
           // A = k^T: dk rows 16 mt.., tokens s KS.. down the stored rows
-          Fr kf;
-          if constexpr (KS == 32) {
-            const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, 16 * mt, lane);
-            const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, 16 * mt, lane);
-            kf = Fr{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          } else {
-            kf = M::load_col(C.k, SM::LDK, 16 * mt, s * KS, lane);
-          }
+          const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, 16 * mt, lane);
+          const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, 16 * mt, lane);
+          const Fr kf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xb[s][nt]);
+          for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xv[s][nt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
@@ -1010,12 +873,21 @@ __global__ __launch_bounds__(256) void empty_seq_state_kernel(const int32_t* __r
   for (int i = threadIdx.x; i < dd; i += 256) ht[base + i] = h0 ? h0[base + i] : 0.f;
 }
 
-// One pass of the chunk loop over every segment: the producer/consumer form
-// for bfloat16 when its two buffers fit in LDS, else the single-buffer form.
+// bfloat16 runs the prepared-chunk state pass (its two buffers fit in LDS);
+// float32 the single-buffer chunk loop.
+template <typename E, int DK, int DV, int MODE>
+constexpr bool uses_prep() {
+  if constexpr (std::is_same<E, bf16>::value)
+    return WsCfg<E, DK, DV, MODE>::FITS && WsCfg<E, DK, DV, kSummary>::FITS;
+  else
+    return false;
+}
+
+// One pass of the chunk loop over every segment.
 template <typename E, int DK, int DV, int MODE>
 void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
   const dim3 grid((unsigned)pl.seg_cap, a.Hv);
-  if constexpr (std::is_same<E, bf16>::value && WsCfg<E, DK, DV, MODE>::FITS) {
+  if constexpr (uses_prep<E, DK, DV, MODE>()) {
     hipLaunchKernelGGL((chunk_ws_kernel<E, DK, DV, MODE>), grid, dim3(WsCfg<E, DK, DV, MODE>::NT), 0,
                        stream, a);
   } else {
@@ -1029,7 +901,8 @@ void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
 template <typename E, int DK, int DV, int FINAL>
 int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl, char* ws,
                  bool with_chunks, hipStream_t stream) {
-  PlanPtrs pp = pl.ptrs(ws, with_chunks);
+  constexpr bool PREP = uses_prep<E, DK, DV, FINAL>();
+  PlanPtrs pp = pl.ptrs(ws, with_chunks || PREP);
   a.seg_table = pp.table;
   a.counts = pp.counts;
   a.seg_chunk0 = pp.seg_chunk0;
@@ -1038,6 +911,13 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, (int)pl.seg_len,
                      (int)pl.seg_cap, (int)pl.chunk_cap, pp);
   if (int rc = gdn::check_launch("chunk plan")) return rc;
+  if constexpr (PREP) {
+    char* rec = ws + pl.off_rec;
+    a.rec = rec;
+    PrepArgs pa{a.q, a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.scale, a.use_l2norm, pp.chunk_tab,
+                pp.counts, rec};
+    if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
+  }
   if (pl.split) {
     launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;

@@ -104,7 +104,7 @@ struct Plan {
   int64_t seg_cap, chunk_cap;
   bool split;  // some sequence may have more than one segment
   size_t off_counts, off_table, off_seg_chunk0, off_seq_off, off_seq_nseg, off_seq_chunk_off,
-      off_chunk_tab, off_state, off_init, end;
+      off_chunk_tab, off_state, off_init, off_rec, end;
 
   PlanPtrs ptrs(char* ws, bool with_chunks) const {
     PlanPtrs p;
@@ -119,9 +119,10 @@ struct Plan {
   }
 };
 
-// seg_chunks: chunks per segment (0 = pick from the device size and the
-// number of (sequence, head) chains; GDN_SEG_CHUNKS overrides for tuning).
-inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) {
+// Segment length from the device size and the number of (sequence, head)
+// chains (GDN_SEG_CHUNKS overrides it for tuning).  rec_bytes: bytes of the
+// prepared record per (chunk, value head), 0 when the state pass takes none.
+inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes) {
   Plan p{};
   const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
   int64_t per = 1;
@@ -158,6 +159,7 @@ inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv) 
   p.off_chunk_tab = take(sizeof(int4) * (size_t)p.chunk_cap);
   p.off_state = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * (dk + dv) : 0);
   p.off_init = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * dv : 0);
+  p.off_rec = take(rec_bytes * (size_t)p.chunk_cap * Hv);
   p.end = o;
   return p;
 }

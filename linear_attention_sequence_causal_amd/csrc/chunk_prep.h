@@ -1,0 +1,355 @@
+// chunk_prep.h -- the state-independent part of every chunk, for all chunks
+// at once (hyper-parallel "linear_attention_context_parallel.py",
+// _prepare_gdn_chunks_for_summary: the prepared chunks that the state pass
+// then consumes).
+//
+// For one chunk of 64 tokens and one value head, with G the in-chunk cumsum
+// of g, Gamma_rc = e^{G_r - G_c}, rk / rq the l2norm factors of k and q (rq
+// includes the q scale), L = strict-lower(kh kh^T o Gamma) split into 16 x 16
+// blocks L_im and D_i = (I + diag(beta_i) L_ii)^-1, the chunk's corrected
+// values solve (I + diag(beta) L) x = diag(beta)(v - diag(e^G rk) k S).
+// Blockwise, with A_i = D_i diag(beta_i):
+//   x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m,
+//   B_i = A_i diag(e^G rk)_i,  E_im = A_i L_im,
+// so the state pass needs, besides q, k and v, only these 16 x 16 operators,
+// the decayed q k^T (P, with the q scale) and three row factors:
+//   fo = e^G rq  (o = fo o (q S) + P x),
+//   fd = rk e^{G_C - G}  (S <- e^{G_C} S + k^T (fd o x)),  eC = e^{G_C}.
+//
+// One workgroup computes the raw products q k^T and k k^T of a chunk once per
+// q/k head and serves every value head of that head (GQA).  The record of a
+// (chunk, value head) stores each operator as MFMA A fragments in lane order,
+// so the state pass copies it into LDS and reads each lane's fragment with
+// one load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "chunk_common.h"
+#include "chunk_plan.h"
+#include "gdn_internal.h"
+
+namespace gdn_chunk {
+
+// Record of one (chunk, value head), bytes:
+//   [kRecP,  +6 KiB)  P as six 16x16x32 A fragments (16 B a lane): row block
+//                     mt, contraction half s, for (mt, s) in kPFrag order
+//   [kRecA,  +2 KiB)  A_i, i = 0..3, 16x16x16 A fragments (8 B a lane)
+//   [kRecNB, +2 KiB)  -B_i
+//   [kRecNE, +3 KiB)  -E_im for (i, m) in kEPair order
+//   [kRecF, ...)      fo[64], fd[64], eC (fp32)
+constexpr int kRecP = 0;
+constexpr int kRecA = 6 * 1024;
+constexpr int kRecNB = kRecA + 4 * 512;
+constexpr int kRecNE = kRecNB + 4 * 512;
+constexpr int kRecF = kRecNE + 6 * 512;
+constexpr int kRecBytes = 14 * 1024;
+static_assert(kRecF + 2 * 256 + 16 <= kRecBytes, "record layout");
+
+// P fragments that are not entirely above the diagonal: (mt, s) = index.
+__host__ __device__ constexpr int p_frag(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : 2 * mt - 2 + s; }
+// (i, m) of the six blocks below the diagonal, in record order.
+__host__ __device__ constexpr int e_pair(int i, int m) { return i * (i - 1) / 2 + m; }
+
+namespace {
+
+constexpr int kPrepLd = 64 + 8;  // bf16 staging tiles [64][kPrepLd]
+constexpr int kPrepScLd = 20;    // fp32 16 x 16 scratch rows (16 + 4)
+
+template <int DK>
+struct PrepSmem {
+  static constexpr int LDK = DK + 8;
+  alignas(16) bf16 q[64 * LDK];
+  alignas(16) bf16 k[64 * LDK];
+  alignas(16) bf16 sp[64 * kPrepLd];  // P, C-layout writes
+  alignas(16) bf16 sn[64 * kPrepLd];  // A_i on the diagonal blocks, -E_im below
+  alignas(16) bf16 sb[64 * 24];       // -B_i in rows 16 i .. 16 i + 15
+  alignas(16) float rq[64];
+  alignas(16) float rk[64];
+  alignas(16) float wv[4][4][64];              // per wave: G, e^G, beta, e^G rk
+  alignas(16) float sc[4][2][16 * kPrepScLd];  // per wave: fp32 L_ii, work tile
+};
+
+struct PrepArgs {
+  const void* q;
+  const void* k;
+  int64_t ld_qk;
+  const float* g;
+  const float* beta;
+  int Hk, Hv;
+  float scale;
+  int use_l2norm;
+  const int4* chunk_tab;
+  const int32_t* counts;
+  char* rec;
+};
+
+// (I + N)^-1 for N = diag(bb) L, L strictly lower 16 x 16 (Lt: fp32, rows of
+// kPrepScLd), NC: N in C layout; sc: work tile.  N^16 = 0, so the inverse is
+// (I - N)(I + N^2)(I + N^4)(I + N^8): six fp32 products.  Returns C layout.
+GDN_DEV floatx4 prep_invert16(const float* Lt, const float* bb, const floatx4& NC, float* sc, int lane) {
+  typedef Tile16<float> F;
+  const int g4 = lane >> 4, ln = lane & 15;
+  const floatx4 NA = F::load_f32(Lt, kPrepScLd, 0, 0, bb[ln], lane);
+  floatx4 N2 = zero4();
+  F::mma(N2, NA, NC);
+#pragma unroll
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kPrepScLd + ln] = N2[j];
+  wave_lds_sync();
+  const floatx4 N2A = F::load(sc, kPrepScLd, 0, 0, lane);
+  floatx4 N4 = zero4();
+  F::mma(N4, N2A, N2);
+  wave_lds_sync();
+#pragma unroll
+  for (int j = 0; j < 4; j++) sc[(4 * g4 + j) * kPrepScLd + ln] = N4[j];
+  wave_lds_sync();
+  const floatx4 N4A = F::load(sc, kPrepScLd, 0, 0, lane);
+  floatx4 N8 = zero4();
+  F::mma(N8, N4A, N4);
+  floatx4 R1 = N4 + N8;
+#pragma unroll
+  for (int j = 0; j < 4; j++) R1[j] += (4 * g4 + j == ln) ? 1.f : 0.f;
+  F::mma(R1, N4A, N8);
+  floatx4 R2 = R1;
+  F::mma(R2, N2A, R1);
+  floatx4 t = zero4();
+  F::mma(t, NA, R2);
+  return R2 - t;
+}
+
+// One (chunk, q/k head) per workgroup of four waves.  Wave w owns the L
+// blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
+// the wave) and the P blocks of row block 3 - w.
+template <int DK>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
+  typedef Mfma<bf16> M;
+  typedef M::frag Fr;
+  typedef Tile16<float> F;
+  typedef PrepSmem<DK> SM;
+  constexpr int LDK = SM::LDK;
+  constexpr int NSK = DK / 32;
+  __shared__ SM sm;
+
+  const int chunk = blockIdx.x, qa = blockIdx.y;
+  if (chunk >= a.counts[1]) return;
+  const int4 ce = a.chunk_tab[chunk];
+  const int64_t tc = ce.x, te = ce.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, ln = lane & 15;
+  const int iq = 3 - w;
+  const int GR = a.Hv / a.Hk;
+
+  // raw rows (zero past the sequence end) and the l2norm factors
+  {
+    typedef bf16x8 V;
+    constexpr int QPR = DK / 8;
+    const bf16* qp = (const bf16*)a.q + (int64_t)qa * DK;
+    const bf16* kp = (const bf16*)a.k + (int64_t)qa * DK;
+#pragma unroll
+    for (int p = 0; p < 64 * QPR / 256; p++) {
+      const int i = tid + 256 * p;
+      const int row = i / QPR, vi = i % QPR;
+      const int64_t t = tc + row;
+      V qv = zero_vec16<bf16>(), kv = zero_vec16<bf16>();
+      if (t < te) {
+        qv = *reinterpret_cast<const V*>(qp + t * a.ld_qk + vi * 8);
+        kv = *reinterpret_cast<const V*>(kp + t * a.ld_qk + vi * 8);
+      }
+      *reinterpret_cast<V*>(sm.q + row * LDK + vi * 8) = qv;
+      *reinterpret_cast<V*>(sm.k + row * LDK + vi * 8) = kv;
+      const float qs = row_group_sum<QPR>(sum_sq(qv)), ks = row_group_sum<QPR>(sum_sq(kv));
+      if (vi == 0) {
+        sm.rq[row] = a.use_l2norm ? a.scale * __builtin_amdgcn_rsqf(qs + 1e-6f) : a.scale;
+        sm.rk[row] = a.use_l2norm ? __builtin_amdgcn_rsqf(ks + 1e-6f) : 1.f;
+      }
+    }
+    // blocks of P above the diagonal that the fragments include stay zero
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e / 64, c = e % 64;
+      if ((c >> 4) > (r >> 4)) sm.sp[r * kPrepLd + c] = (bf16)0.f;
+    }
+  }
+  __syncthreads();
+
+  // raw products of this wave's five blocks: k_w k_w^T, q_iq k_iq^T, then the
+  // three below the diagonal: k_w k_t^T (t < w), q_iq k_(t-w)^T
+  floatx4 rD = zero4(), rDP = zero4(), rO[3];
+#pragma unroll
+  for (int t = 0; t < 3; t++) rO[t] = zero4();
+#pragma unroll
+  for (int s = 0; s < NSK; s++) {
+    const Fr ak = M::load(sm.k, LDK, 16 * w, 32 * s, lane);
+    const Fr aq = M::load(sm.q, LDK, 16 * iq, 32 * s, lane);
+    M::mma(rD, ak, M::load(sm.k, LDK, 16 * w, 32 * s, lane));
+    M::mma(rDP, aq, M::load(sm.k, LDK, 16 * iq, 32 * s, lane));
+#pragma unroll
+    for (int t = 0; t < 3; t++) {
+      const int j = t < w ? t : t - w;
+      M::mma(rO[t], t < w ? ak : aq, M::load(sm.k, LDK, 16 * j, 32 * s, lane));
+    }
+  }
+  float rkL[4], rqP[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; jj++) {
+    rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
+    rqP[jj] = sm.rq[16 * iq + 4 * g4 + jj];
+  }
+  float* Lt = sm.sc[w][0];
+  float* wk = sm.sc[w][1];
+  float* G = sm.wv[w][0];
+  float* eG = sm.wv[w][1];
+  float* bt = sm.wv[w][2];
+  float* fk = sm.wv[w][3];
+
+  for (int r = 0; r < GR; r++) {
+    const int h = qa * GR + r;
+    char* rec = a.rec + ((int64_t)chunk * a.Hv + h) * kRecBytes;
+    // gates of the 64 tokens, one per lane (zero past the end), cumsum
+    const int64_t t = tc + lane;
+    float gv = 0.f, bv = 0.f;
+    if (t < te) {
+      gv = a.g[t * a.Hv + h];
+      bv = a.beta[t * a.Hv + h];
+    }
+    float Gv = gv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(Gv, off, 64);
+      if (lane >= off) Gv += o;
+    }
+    const float GC = __shfl(Gv, 63, 64);
+    const float egv = __expf(Gv);
+    G[lane] = Gv;
+    eG[lane] = egv;
+    bt[lane] = bv;
+    fk[lane] = egv * sm.rk[lane];
+    if (w == 0) {
+      float* F32 = reinterpret_cast<float*>(rec + kRecF);
+      F32[lane] = egv * sm.rq[lane];                       // fo
+      F32[64 + lane] = sm.rk[lane] * __expf(GC - Gv);      // fd
+      if (lane == 0) F32[128] = __expf(GC);                // eC
+    }
+    wave_lds_sync();
+
+    // diagonal L block -> fp32 scratch, then D, A = D diag(beta), -B
+    floatx4 NC;
+    {
+      const int c = 16 * w + ln;
+      const float Gc = G[c], fc = sm.rk[c];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int row = 16 * w + 4 * g4 + jj;
+        const float e = __expf(fminf(G[row] - Gc, 0.f));  // clamped: masked entries stay finite
+        const float val = row > c ? rD[jj] * rkL[jj] * fc * e : 0.f;
+        Lt[(4 * g4 + jj) * kPrepScLd + ln] = val;
+        NC[jj] = bt[row] * val;
+      }
+    }
+    wave_lds_sync();
+    const floatx4 D = prep_invert16(Lt, bt + 16 * w, NC, wk, lane);
+    floatx4 Ai;
+    {
+      const float bc = bt[16 * w + ln], fc = fk[16 * w + ln];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int row = 16 * w + 4 * g4 + jj;
+        Ai[jj] = D[jj] * bc;
+        sm.sn[row * kPrepLd + 16 * w + ln] = (bf16)Ai[jj];
+        sm.sb[row * 24 + ln] = (bf16)(-Ai[jj] * fc);
+      }
+    }
+    // E_wm = A_w L_wm for m < w (A_w as A operand through the work tile)
+    if (w > 0) {
+      wave_lds_sync();  // the inversion's last reads of the work tile are done
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) wk[(4 * g4 + jj) * kPrepScLd + ln] = Ai[jj];
+      wave_lds_sync();
+      const floatx4 AA = F::load(wk, kPrepScLd, 0, 0, lane);
+      const float G0 = G[16 * w];
+#pragma unroll
+      for (int t = 0; t < 3; t++) {
+        if (t >= w) break;
+        const int c = 16 * t + ln;
+        // decay factored as e^{G_r - G_0} e^{G_0 - G_c}, both <= 1
+        const float bcol = sm.rk[c] * __expf(G0 - G[c]);
+        floatx4 Lm;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int row = 16 * w + 4 * g4 + jj;
+          Lm[jj] = rO[t][jj] * rkL[jj] * __expf(G[row] - G0) * bcol;
+        }
+        floatx4 E = zero4();
+        F::mma(E, AA, Lm);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          sm.sn[(16 * w + 4 * g4 + jj) * kPrepLd + c] = (bf16)(-E[jj]);
+      }
+    }
+    // P blocks of row block iq
+    {
+      const int c = 16 * iq + ln;
+      const float Gc = G[c], fc = sm.rk[c];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int row = 16 * iq + 4 * g4 + jj;
+        const float e = __expf(fminf(G[row] - Gc, 0.f));
+        sm.sp[row * kPrepLd + c] = (bf16)(row >= c ? rDP[jj] * rqP[jj] * fc * e : 0.f);
+      }
+      const float G0 = G[16 * iq];
+#pragma unroll
+      for (int t = 0; t < 3; t++) {
+        if (t < w) continue;
+        const int j = t - w;
+        const int cj = 16 * j + ln;
+        const float bcol = sm.rk[cj] * __expf(G0 - G[cj]);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int row = 16 * iq + 4 * g4 + jj;
+          sm.sp[row * kPrepLd + cj] = (bf16)(rO[t][jj] * rqP[jj] * __expf(G[row] - G0) * bcol);
+        }
+      }
+    }
+    __syncthreads();
+    // copy the operators out as A fragments in lane order
+    for (int i = tid; i < 6 * 64; i += 256) {
+      const int f = i >> 6, l = i & 63;
+      const int mt = f == 0 ? 0 : f == 1 ? 1 : (f + 2) >> 1, s = f < 2 ? 0 : (f & 1);
+      const bf16* src = sm.sp + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
+      bf16x8 v;
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      *reinterpret_cast<bf16x8*>(rec + kRecP + f * 1024 + l * 16) = v;
+    }
+    for (int i = tid; i < 14 * 64; i += 256) {
+      const int f = i >> 6, l = i & 63;
+      const bf16* src;
+      int off;
+      if (f < 4) {
+        src = sm.sn + (16 * f + (l & 15)) * kPrepLd + 16 * f + 4 * (l >> 4);
+        off = kRecA + f * 512;
+      } else if (f < 8) {
+        src = sm.sb + (16 * (f - 4) + (l & 15)) * 24 + 4 * (l >> 4);
+        off = kRecNB + (f - 4) * 512;
+      } else {
+        const int e = f - 8;
+        const int ii = e == 0 ? 1 : e < 3 ? 2 : 3, mm = e - ii * (ii - 1) / 2;
+        src = sm.sn + (16 * ii + (l & 15)) * kPrepLd + 16 * mm + 4 * (l >> 4);
+        off = kRecNE + e * 512;
+      }
+      *reinterpret_cast<bf16x4*>(rec + off + l * 8) = *reinterpret_cast<const bf16x4*>(src);
+    }
+    __syncthreads();  // staging is rewritten for the next value head
+  }
+}
+
+template <int DK>
+int launch_prep(const PrepArgs& a, int64_t chunk_cap, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)chunk_cap, a.Hk), dim3(256), 0, stream, a);
+  return gdn::check_launch("chunk prep");
+}
+
+}  // namespace
+}  // namespace gdn_chunk

@@ -256,6 +256,14 @@ GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane) 
 
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Make this wave's LDS writes visible to its own later reads from other lanes.
+GDN_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Workgroup barrier for hand-offs through LDS only: waits for this wave's LDS
 // operations, not for its global loads and stores in flight (the release
 // fence of __syncthreads() would drain those too).  The memory clobber keeps
