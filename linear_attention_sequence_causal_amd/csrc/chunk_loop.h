@@ -71,6 +71,7 @@ struct LoopArgs {
   float* seg_init;   // [seg_cap][Hv][DK][DV] initial states of non-first segments
   float* states;     // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk
   const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
+  int seg_cap;       // capacity of the segment table
 };
 
 // LDS of the chunk loop (one chunk of one head at a time; rows padded by
@@ -489,6 +490,13 @@ void chunk_loop_kernel(LoopArgs a) {
 // buffers while the consumers run chunk c from the other.  One workgroup
 // barrier per chunk separates the two.
 
+// The state's dk rows are kept permuted in registers: row r of accumulator
+// tile mt holds dk = 32(mt/2) + 8(r/4) + 4(mt%2) + r%4.  Then the eight
+// contraction elements a lane supplies to a 16x16x32 product (rows 4g..4g+3
+// of tiles 2s and 2s+1) are dk 32s + 8g .. 32s + 8g + 7, contiguous in a k or
+// q row: one 16-byte LDS read per fragment.
+GDN_DEV int dk_of_row(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3); }
+
 // One LDS buffer: raw rows (16-byte padded) and the record.
 template <typename O, int DK, int DV, bool HAS_Q>
 struct WsSmem {
@@ -596,8 +604,14 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   static_assert(KS == 32, "bf16 fragments");
   __shared__ SM buf[2];
 
-  const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= a.counts[0]) return;
+  // Workgroup order: the value heads of one q/k head and segment take ids 8
+  // apart, so they run together on one XCD (ids go round-robin over the 8
+  // XCDs) and share q and k through its L2.
+  const int GR = a.Hv / a.Hk;
+  const int id = blockIdx.x;
+  const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
+  const int seg = grp % a.seg_cap, h = (grp / a.seg_cap) * GR + member;
+  if (grp >= a.seg_cap * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (MODE == kSummary && (ent.w & kLast)) return;
   const int n = ent.x;
@@ -652,7 +666,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
+          const int row = dk_of_row(mt, 4 * g4 + j), col = c0 + 16 * nt + ln;
           float v = 0.f;
           if (mcol) v = (row == col) ? 1.f : 0.f;
           else if (src) v = src[row * DV + col];
@@ -676,7 +690,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           for (int nt = 0; nt < NN; nt++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
+              dst[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
       }
       // k S (into x) and q S (into o), one contraction step of S at a time
 #pragma unroll
@@ -693,18 +707,18 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         for (int nt = 0; nt < NN; nt++) b[nt] = acc_as_b<O>(S, s, nt);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const Fr kf = M::load(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          const Fr kf = M::load_k8(C.k, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
           if constexpr (OUT) {
-            const Fr qf = M::load(C.q, SM::LDK, 16 * mt, s * KS, lane);
+            const Fr qf = M::load_k8(C.q, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
             for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], qf, b[nt]);
           }
         }
       }
-      // x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m
-      Fr16 xb[4][NN];
+      // x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m: the first two terms
+      // of every block do not depend on the others and go first
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const Fr16 fa = *reinterpret_cast<const Fr16*>(R + kRecA + i * 512 + lane * 8);
@@ -716,6 +730,10 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           T16::mma(acc, fb, T16::from_acc(x[i][nt]));
           x[i][nt] = acc;
         }
+      }
+      Fr16 xb[4][NN];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
 #pragma unroll
         for (int m = 0; m < i; m++) {
           const Fr16 fe = *reinterpret_cast<const Fr16*>(R + kRecNE + e_pair(i, m) * 512 + lane * 8);
@@ -755,19 +773,6 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
             for (int j = 0; j < 4; j++)
               C.v[(16 * mt + 4 * g4 + j) * SM::LDV + c0 + 16 * nt + ln] = from_f<O>(o[mt][nt][j]);
-        // this wave's columns of the 64 rows, as 16-byte pieces
-        wave_lds_sync();
-        constexpr int PPR = CW / VE;  // pieces per row
-        const int64_t tc = tb + (int64_t)it * BT;
-        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0);
-#pragma unroll
-        for (int p = 0; p < BT * PPR / 64; p++) {
-          const int i = lane + 64 * p;
-          const int row = i / PPR, vi = i % PPR;
-          if (tc + row < te)
-            *reinterpret_cast<V16*>(op + row * o_ld + vi * VE) =
-                *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
-        }
       }
       // S <- eC S + k^T (fd o x)
 #pragma unroll
@@ -788,15 +793,33 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         for (int nt = 0; nt < NN; nt++) acc[nt] = S[mt][nt] * eC;
 #pragma unroll
         for (int s = 0; s < NSB; s++) {
-          // A = k^T: dk rows 16 mt.., tokens s KS.. down the stored rows
-          const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, 16 * mt, lane);
-          const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, 16 * mt, lane);
+          // A = k^T: the dk rows of tile mt (permuted), tokens s KS.. down the
+          // stored rows
+          const int cdk = 32 * (mt >> 1) + 4 * (mt & 1);
+          const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, cdk, lane, 8);
+          const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, cdk, lane, 8);
           const Fr kf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xv[s][nt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
+      }
+      if constexpr (OUT) {
+        // the staged o, this wave's columns of the 64 rows, as 16-byte pieces
+        // (staged before the state update, whose products hide the latency)
+        wave_lds_sync();
+        constexpr int PPR = CW / VE;  // pieces per row
+        const int64_t tc = tb + (int64_t)it * BT;
+        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0);
+#pragma unroll
+        for (int p = 0; p < BT * PPR / 64; p++) {
+          const int i = lane + 64 * p;
+          const int row = i / PPR, vi = i % PPR;
+          if (tc + row < te)
+            *reinterpret_cast<V16*>(op + row * o_ld + vi * VE) =
+                *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
+        }
       }
     }
     lds_barrier();
@@ -818,7 +841,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int row = 16 * mt + 4 * g4 + j, col = c0 + 16 * nt + ln;
+          const int row = dk_of_row(mt, 4 * g4 + j), col = c0 + 16 * nt + ln;
           dst[row * ld + col] = S[mt][nt][j];
         }
   }
@@ -888,8 +911,10 @@ template <typename E, int DK, int DV, int MODE>
 void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
   const dim3 grid((unsigned)pl.seg_cap, a.Hv);
   if constexpr (uses_prep<E, DK, DV, MODE>()) {
-    hipLaunchKernelGGL((chunk_ws_kernel<E, DK, DV, MODE>), grid, dim3(WsCfg<E, DK, DV, MODE>::NT), 0,
-                       stream, a);
+    const int64_t unit = 8 * (int64_t)(a.Hv / a.Hk);
+    const int64_t n = (pl.seg_cap * a.Hv + unit - 1) / unit * unit;
+    hipLaunchKernelGGL((chunk_ws_kernel<E, DK, DV, MODE>), dim3((unsigned)n),
+                       dim3(WsCfg<E, DK, DV, MODE>::NT), 0, stream, a);
   } else {
     hipLaunchKernelGGL((chunk_loop_kernel<E, DK, DV, MODE>), grid, dim3(LoopCfg<E, DK, DV, MODE>::NT),
                        0, stream, a);
@@ -903,6 +928,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
                  bool with_chunks, hipStream_t stream) {
   constexpr bool PREP = uses_prep<E, DK, DV, FINAL>();
   PlanPtrs pp = pl.ptrs(ws, with_chunks || PREP);
+  a.seg_cap = (int)pl.seg_cap;
   a.seg_table = pp.table;
   a.counts = pp.counts;
   a.seg_chunk0 = pp.seg_chunk0;

@@ -56,18 +56,28 @@ namespace {
 constexpr int kPrepLd = 64 + 8;  // bf16 staging tiles [64][kPrepLd]
 constexpr int kPrepScLd = 20;    // fp32 16 x 16 scratch rows (16 + 4)
 
+// The raw rows are dead once the products are formed, so the per-head staging
+// shares their space (four workgroups fit a CU).
 template <int DK>
 struct PrepSmem {
   static constexpr int LDK = DK + 8;
-  alignas(16) bf16 q[64 * LDK];
-  alignas(16) bf16 k[64 * LDK];
-  alignas(16) bf16 sp[64 * kPrepLd];  // P, C-layout writes
-  alignas(16) bf16 sn[64 * kPrepLd];  // A_i on the diagonal blocks, -E_im below
-  alignas(16) bf16 sb[64 * 24];       // -B_i in rows 16 i .. 16 i + 15
+  struct Rows {
+    alignas(16) bf16 q[64 * LDK];
+    alignas(16) bf16 k[64 * LDK];
+  };
+  struct Stage {
+    alignas(16) bf16 sp[64 * kPrepLd];  // P, C-layout writes
+    alignas(16) bf16 sn[64 * kPrepLd];  // A_i on the diagonal blocks, -E_im below
+    alignas(16) bf16 sb[64 * 24];       // -B_i in rows 16 i .. 16 i + 15
+    alignas(16) float sc[4][2][16 * kPrepScLd];  // per wave: fp32 L_ii, work tile
+  };
+  union {
+    Rows r;
+    Stage s;
+  } u;
   alignas(16) float rq[64];
   alignas(16) float rk[64];
-  alignas(16) float wv[4][4][64];              // per wave: G, e^G, beta, e^G rk
-  alignas(16) float sc[4][2][16 * kPrepScLd];  // per wave: fp32 L_ii, work tile
+  alignas(16) float wv[4][4][64];  // per wave: G, e^G, beta, e^G rk
 };
 
 struct PrepArgs {
@@ -121,7 +131,7 @@ GDN_DEV floatx4 prep_invert16(const float* Lt, const float* bb, const floatx4& N
 // blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
 // the wave) and the P blocks of row block 3 - w.
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void chunk_prep_kernel(PrepArgs a) {
   typedef Mfma<bf16> M;
   typedef M::frag Fr;
   typedef Tile16<float> F;
@@ -156,18 +166,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         qv = *reinterpret_cast<const V*>(qp + t * a.ld_qk + vi * 8);
         kv = *reinterpret_cast<const V*>(kp + t * a.ld_qk + vi * 8);
       }
-      *reinterpret_cast<V*>(sm.q + row * LDK + vi * 8) = qv;
-      *reinterpret_cast<V*>(sm.k + row * LDK + vi * 8) = kv;
+      *reinterpret_cast<V*>(sm.u.r.q + row * LDK + vi * 8) = qv;
+      *reinterpret_cast<V*>(sm.u.r.k + row * LDK + vi * 8) = kv;
       const float qs = row_group_sum<QPR>(sum_sq(qv)), ks = row_group_sum<QPR>(sum_sq(kv));
       if (vi == 0) {
         sm.rq[row] = a.use_l2norm ? a.scale * __builtin_amdgcn_rsqf(qs + 1e-6f) : a.scale;
         sm.rk[row] = a.use_l2norm ? __builtin_amdgcn_rsqf(ks + 1e-6f) : 1.f;
       }
-    }
-    // blocks of P above the diagonal that the fragments include stay zero
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int r = e / 64, c = e % 64;
-      if ((c >> 4) > (r >> 4)) sm.sp[r * kPrepLd + c] = (bf16)0.f;
     }
   }
   __syncthreads();
@@ -179,14 +184,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   for (int t = 0; t < 3; t++) rO[t] = zero4();
 #pragma unroll
   for (int s = 0; s < NSK; s++) {
-    const Fr ak = M::load(sm.k, LDK, 16 * w, 32 * s, lane);
-    const Fr aq = M::load(sm.q, LDK, 16 * iq, 32 * s, lane);
-    M::mma(rD, ak, M::load(sm.k, LDK, 16 * w, 32 * s, lane));
-    M::mma(rDP, aq, M::load(sm.k, LDK, 16 * iq, 32 * s, lane));
+    const Fr ak = M::load(sm.u.r.k, LDK, 16 * w, 32 * s, lane);
+    const Fr aq = M::load(sm.u.r.q, LDK, 16 * iq, 32 * s, lane);
+    M::mma(rD, ak, M::load(sm.u.r.k, LDK, 16 * w, 32 * s, lane));
+    M::mma(rDP, aq, M::load(sm.u.r.k, LDK, 16 * iq, 32 * s, lane));
 #pragma unroll
     for (int t = 0; t < 3; t++) {
       const int j = t < w ? t : t - w;
-      M::mma(rO[t], t < w ? ak : aq, M::load(sm.k, LDK, 16 * j, 32 * s, lane));
+      M::mma(rO[t], t < w ? ak : aq, M::load(sm.u.r.k, LDK, 16 * j, 32 * s, lane));
     }
   }
   float rkL[4], rqP[4];
@@ -195,22 +200,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
     rqP[jj] = sm.rq[16 * iq + 4 * g4 + jj];
   }
-  float* Lt = sm.sc[w][0];
-  float* wk = sm.sc[w][1];
+  __syncthreads();  // every wave's products are formed: the rows' space is reused
+  // blocks of P above the diagonal that the fragments include stay zero
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e / 64, c = e % 64;
+    if ((c >> 4) > (r >> 4)) sm.u.s.sp[r * kPrepLd + c] = (bf16)0.f;
+  }
+  float* Lt = sm.u.s.sc[w][0];
+  float* wk = sm.u.s.sc[w][1];
   float* G = sm.wv[w][0];
   float* eG = sm.wv[w][1];
   float* bt = sm.wv[w][2];
   float* fk = sm.wv[w][3];
 
+  // gates of the 64 tokens, one per lane (zero past the end), loaded one
+  // value head ahead
+  const int64_t tg = tc + lane;
+  float gn = 0.f, bn = 0.f;
+  if (tg < te) {
+    gn = a.g[tg * a.Hv + qa * GR];
+    bn = a.beta[tg * a.Hv + qa * GR];
+  }
   for (int r = 0; r < GR; r++) {
     const int h = qa * GR + r;
     char* rec = a.rec + ((int64_t)chunk * a.Hv + h) * kRecBytes;
-    // gates of the 64 tokens, one per lane (zero past the end), cumsum
-    const int64_t t = tc + lane;
-    float gv = 0.f, bv = 0.f;
-    if (t < te) {
-      gv = a.g[t * a.Hv + h];
-      bv = a.beta[t * a.Hv + h];
+    const float gv = gn, bv = bn;
+    if (r + 1 < GR && tg < te) {
+      gn = a.g[tg * a.Hv + h + 1];
+      bn = a.beta[tg * a.Hv + h + 1];
     }
     float Gv = gv;
 #pragma unroll
@@ -255,8 +272,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       for (int jj = 0; jj < 4; jj++) {
         const int row = 16 * w + 4 * g4 + jj;
         Ai[jj] = D[jj] * bc;
-        sm.sn[row * kPrepLd + 16 * w + ln] = (bf16)Ai[jj];
-        sm.sb[row * 24 + ln] = (bf16)(-Ai[jj] * fc);
+        sm.u.s.sn[row * kPrepLd + 16 * w + ln] = (bf16)Ai[jj];
+        sm.u.s.sb[row * 24 + ln] = (bf16)(-Ai[jj] * fc);
       }
     }
     // E_wm = A_w L_wm for m < w (A_w as A operand through the work tile)
@@ -283,7 +300,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         F::mma(E, AA, Lm);
 #pragma unroll
         for (int jj = 0; jj < 4; jj++)
-          sm.sn[(16 * w + 4 * g4 + jj) * kPrepLd + c] = (bf16)(-E[jj]);
+          sm.u.s.sn[(16 * w + 4 * g4 + jj) * kPrepLd + c] = (bf16)(-E[jj]);
       }
     }
     // P blocks of row block iq
@@ -294,7 +311,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       for (int jj = 0; jj < 4; jj++) {
         const int row = 16 * iq + 4 * g4 + jj;
         const float e = __expf(fminf(G[row] - Gc, 0.f));
-        sm.sp[row * kPrepLd + c] = (bf16)(row >= c ? rDP[jj] * rqP[jj] * fc * e : 0.f);
+        sm.u.s.sp[row * kPrepLd + c] = (bf16)(row >= c ? rDP[jj] * rqP[jj] * fc * e : 0.f);
       }
       const float G0 = G[16 * iq];
 #pragma unroll
@@ -306,7 +323,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int row = 16 * iq + 4 * g4 + jj;
-          sm.sp[row * kPrepLd + cj] = (bf16)(rO[t][jj] * rqP[jj] * __expf(G[row] - G0) * bcol);
+          sm.u.s.sp[row * kPrepLd + cj] = (bf16)(rO[t][jj] * rqP[jj] * __expf(G[row] - G0) * bcol);
         }
       }
     }
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     for (int i = tid; i < 6 * 64; i += 256) {
       const int f = i >> 6, l = i & 63;
       const int mt = f == 0 ? 0 : f == 1 ? 1 : (f + 2) >> 1, s = f < 2 ? 0 : (f & 1);
-      const bf16* src = sm.sp + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
+      const bf16* src = sm.u.s.sp + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
       bf16x8 v;
       const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
       const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
@@ -328,15 +345,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       const bf16* src;
       int off;
       if (f < 4) {
-        src = sm.sn + (16 * f + (l & 15)) * kPrepLd + 16 * f + 4 * (l >> 4);
+        src = sm.u.s.sn + (16 * f + (l & 15)) * kPrepLd + 16 * f + 4 * (l >> 4);
         off = kRecA + f * 512;
       } else if (f < 8) {
-        src = sm.sb + (16 * (f - 4) + (l & 15)) * 24 + 4 * (l >> 4);
+        src = sm.u.s.sb + (16 * (f - 4) + (l & 15)) * 24 + 4 * (l >> 4);
         off = kRecNB + (f - 4) * 512;
       } else {
         const int e = f - 8;
         const int ii = e == 0 ? 1 : e < 3 ? 2 : 3, mm = e - ii * (ii - 1) / 2;
-        src = sm.sn + (16 * ii + (l & 15)) * kPrepLd + 16 * mm + 4 * (l >> 4);
+        src = sm.u.s.sn + (16 * ii + (l & 15)) * kPrepLd + 16 * mm + 4 * (l >> 4);
         off = kRecNE + e * 512;
       }
       *reinterpret_cast<bf16x4*>(rec + off + l * 8) = *reinterpret_cast<const bf16x4*>(src);

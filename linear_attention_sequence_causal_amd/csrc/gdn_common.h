@@ -75,6 +75,11 @@ template <> struct Mfma<bf16> {
     f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
     return f;
   }
+  // rows row0 + l%16, k indices k0 + 8g .. k0 + 8g + 7 (one 16-byte read): the
+  // contraction order of a state whose dk rows are permuted (see dk_of_row)
+  GDN_DEV static frag load_k8(const bf16* base, int ld, int row0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + ((lane & 15) * ld + 8 * (lane >> 4)) + (row0 * ld + k0));
+  }
   // same from an fp32 [rows][ld] array, element k scaled by sc[k]
   GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
                                   int lane) {
@@ -246,9 +251,11 @@ template <> struct Tile16<float> {
 // 8-byte vector read by lane 4j + i/4, so lane i points at row r0 + 4g +
 // i/4, columns c0 + 4(i%4) .. +3.  Addresses must be 8-byte aligned.
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane) {
+// With cs = 8 the four column blocks are c0, c0 + 8, c0 + 16, c0 + 24, and lane
+// i receives column c0 + 8(i/4) + i%4 (the permuted dk order of the state).
+GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane, int cs = 4) {
   const int i = lane & 15, g = lane >> 4;
-  const bf16* p = base + ((4 * g + (i >> 2)) * ld + 4 * (i & 3)) + (r0 * ld + c0);
+  const bf16* p = base + ((4 * g + (i >> 2)) * ld + cs * (i & 3)) + (r0 * ld + c0);
   typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
   const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
   return __builtin_bit_cast(bf16x4, v);
