@@ -674,8 +674,6 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         }
   }
   const int64_t o_ld = (int64_t)Hv * DV;
-  typedef typename Vec16<E>::type V16;
-  constexpr int VE = Vec16<E>::N;
   floatx4 x[4][NN], o[OUT ? 4 : 1][NN];
   for (int it = -1; it < nchunks; it++) {
     if (it >= 0) {
@@ -711,9 +709,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
           if constexpr (OUT) {
+            // o^T = S^T q^T: the state fragment is the A operand (its column
+            // index is the row of the product), q rows the B operand
             const Fr qf = M::load_k8(C.q, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
-            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], qf, b[nt]);
+            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], b[nt], qf);
           }
         }
       }
@@ -747,10 +747,13 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
       const float* Fd = Fo + 64;
       const float eC = Fo[128];
       if constexpr (OUT) {
-        // o = fo o (q S) + P x, staged over this wave's columns of v
+        // o^T = fo o (S^T q^T) + x^T P^T.  Tile o[mt][nt] holds value columns
+        // c0 + 16 nt + 4(lane/16) + j of token 16 mt + lane%16, so fo is one
+        // factor per lane, x fragments are the A operands and the record's P
+        // fragments (rows = tokens) the B operands.
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const floatx4 fo = *reinterpret_cast<const floatx4*>(Fo + 16 * mt + 4 * g4);
+          const float fo = Fo[16 * mt + ln];
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) o[mt][nt] *= fo;
         }
@@ -763,16 +766,27 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           for (int mt = 2 * s; mt < 4; mt++) {
             const Fr pf = *reinterpret_cast<const Fr*>(R + kRecP + p_frag(mt, s) * 1024 + lane * 16);
 #pragma unroll
-            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], pf, xs[nt]);
+            for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], xs[nt], pf);
           }
         }
+        // four consecutive value columns of one token per lane: one 8-byte
+        // (bf16) store per tile, straight to HBM
+        typedef E E4 __attribute__((ext_vector_type(4)));
+        const int64_t tc = tb + (int64_t)it * BT;
+        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0 + 4 * g4);
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+        for (int mt = 0; mt < 4; mt++) {
+          const int row = 16 * mt + ln;
+          if (tc + row < te) {
 #pragma unroll
-          for (int nt = 0; nt < NN; nt++)
+            for (int nt = 0; nt < NN; nt++) {
+              E4 v4;
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-              C.v[(16 * mt + 4 * g4 + j) * SM::LDV + c0 + 16 * nt + ln] = from_f<O>(o[mt][nt][j]);
+              for (int j = 0; j < 4; j++) v4[j] = from_f<E>(o[mt][nt][j]);
+              *reinterpret_cast<E4*>(op + row * o_ld + 16 * nt) = v4;
+            }
+          }
+        }
       }
       // S <- eC S + k^T (fd o x)
 #pragma unroll
@@ -804,22 +818,6 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         }
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
-      }
-      if constexpr (OUT) {
-        // the staged o, this wave's columns of the 64 rows, as 16-byte pieces
-        // (staged before the state update, whose products hide the latency)
-        wave_lds_sync();
-        constexpr int PPR = CW / VE;  // pieces per row
-        const int64_t tc = tb + (int64_t)it * BT;
-        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0);
-#pragma unroll
-        for (int p = 0; p < BT * PPR / 64; p++) {
-          const int i = lane + 64 * p;
-          const int row = i / PPR, vi = i % PPR;
-          if (tc + row < te)
-            *reinterpret_cast<V16*>(op + row * o_ld + vi * VE) =
-                *reinterpret_cast<const V16*>(C.v + row * SM::LDV + c0 + vi * VE);
-        }
       }
     }
     lds_barrier();
