@@ -480,9 +480,11 @@ void chunk_loop_kernel(LoopArgs a) {
 // chunk_prep.h has produced, for every (chunk, value head), the record of
 // state-independent operators.  What is left per chunk is the chain through
 // the state:
-//   x = k S and o = q S (S's accumulators are the B operands directly),
-//   x_i = A_i v_i - B_i x_i - sum_{m<i} E_im x_m over the four 16-row blocks,
-//   o = fo o o + P x  (staged through LDS, written as 16-byte row pieces),
+//   x = k S and o^T = S^T q^T (S's accumulators are the B, resp. A operands
+//   directly),
+//   x = T (v - fk o x)  (one lower-triangular product),
+//   o^T = fo o o^T + x^T P^T  (stored from registers, four value columns of
+//   one token per lane),
 //   S <- eC S + k^T (fd o x)  (k^T read with the transposing LDS load).
 // A workgroup owns one (segment, value head) and holds NC consumer waves, each
 // owning 32 state columns as MFMA accumulator tiles, plus four loader waves
@@ -497,10 +499,15 @@ void chunk_loop_kernel(LoopArgs a) {
 // q row: one 16-byte LDS read per fragment.
 GDN_DEV int dk_of_row(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3); }
 
-// One LDS buffer: raw rows (16-byte padded) and the record.
+// One LDS buffer: raw rows and the record.  Rows are padded by 32 bytes
+// (288-byte rows for 128 bf16), and the 16-byte chunks of a q or k row are
+// stored with the chunk index XOR-ed with bit 3 of the row.  Over 64 banks of
+// 4 bytes the 16-byte row reads of q and k, the loaders' stores and v's
+// transposing reads are then free of bank conflicts, and k's transposing
+// reads (one 8-byte half of each chunk) two-way instead of four-way.
 template <typename O, int DK, int DV, bool HAS_Q>
 struct WsSmem {
-  static constexpr int PAD = 16 / (int)sizeof(O);
+  static constexpr int PAD = 32 / (int)sizeof(O);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDV = DV + PAD;
   alignas(16) char rec[kRecBytes];
@@ -513,13 +520,15 @@ template <typename E, int DK, int DV, int MODE>
 struct WsCfg {
   static constexpr bool OUT = MODE == kOut;
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
-  static constexpr int CW = 32;                                // columns per consumer wave
+  // columns per consumer wave: 16 in the output pass (eight consumer waves, two
+  // a SIMD, like the summary's), 32 otherwise
+  static constexpr int CW = OUT && DV == 128 ? 16 : 32;
   static constexpr int NC = NSC / CW;                          // consumer waves
   static constexpr int NL = 4;                                 // loader waves
   static constexpr int NT = (NC + NL) * 64;
   typedef WsSmem<E, DK, DV, OUT> SM;
-  // bytes of the record the consumers read (P only for the output)
-  static constexpr int REC0 = OUT ? 0 : kRecA;
+  // bytes of the record the consumers read (P only in the output pass)
+  static constexpr int REC0 = OUT ? 0 : kRecT;
   static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
 };
 
@@ -567,8 +576,9 @@ struct WsLoad {
     for (int p = 0; p < PQ; p++) {
       const int i = tid + NTL * p;
       const int row = i / QPR, vi = i % QPR;
-      if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vi * VE) = q[p];
-      *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vi * VE) = k[p];
+      const int vx = vi ^ ((row >> 3) & 1);  // chunk swizzle of the q / k rows
+      if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vx * VE) = q[p];
+      *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vx * VE) = k[p];
     }
 #pragma unroll
     for (int p = 0; p < PV; p++) {
@@ -589,9 +599,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef WsCfg<E, DK, DV, MODE> CF;
   typedef E O;
   typedef Mfma<O> M;
-  typedef Tile16<O> T16;
   typedef typename M::frag Fr;
-  typedef typename T16::frag Fr16;
   constexpr int NC = CF::NC;
   constexpr int CW = CF::CW;
   constexpr int NN = CW / 16;   // 16-column tiles per consumer wave
@@ -705,47 +713,57 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
         for (int nt = 0; nt < NN; nt++) b[nt] = acc_as_b<O>(S, s, nt);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const Fr kf = M::load_k8(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          const Fr kf = M::load_k8_x(C.k, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
           if constexpr (OUT) {
             // o^T = S^T q^T: the state fragment is the A operand (its column
             // index is the row of the product), q rows the B operand
-            const Fr qf = M::load_k8(C.q, SM::LDK, 16 * mt, s * KS, lane);
+            const Fr qf = M::load_k8_x(C.q, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
             for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], b[nt], qf);
           }
         }
       }
-      // x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m: the first two terms
-      // of every block do not depend on the others and go first
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const Fr16 fa = *reinterpret_cast<const Fr16*>(R + kRecA + i * 512 + lane * 8);
-        const Fr16 fb = *reinterpret_cast<const Fr16*>(R + kRecNB + i * 512 + lane * 8);
-#pragma unroll
-        for (int nt = 0; nt < NN; nt++) {
-          floatx4 acc = zero4();
-          if (!mcol) T16::mma(acc, fa, lds_rows4_tr(C.v, SM::LDV, 16 * i, vc0 + 16 * nt, lane));
-          T16::mma(acc, fb, T16::from_acc(x[i][nt]));
-          x[i][nt] = acc;
-        }
-      }
-      Fr16 xb[4][NN];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-#pragma unroll
-        for (int m = 0; m < i; m++) {
-          const Fr16 fe = *reinterpret_cast<const Fr16*>(R + kRecNE + e_pair(i, m) * 512 + lane * 8);
-#pragma unroll
-          for (int nt = 0; nt < NN; nt++) T16::mma(x[i][nt], fe, xb[m][nt]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NN; nt++) xb[i][nt] = T16::from_acc(x[i][nt]);
-      }
       const float* Fo = reinterpret_cast<const float*>(R + kRecF);
       const float* Fd = Fo + 64;
-      const float eC = Fo[128];
+      const float* Fk = Fo + 128;
+      const float eC = Fo[192];
+      // x = T (v - fk o (k S)): the right side in accumulator layout (token
+      // rows), then one lower-triangular product with T's fragments
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const floatx4 f = *reinterpret_cast<const floatx4*>(Fk + 16 * i + 4 * g4);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          floatx4 y = -f * x[i][nt];
+          if (!mcol) {
+            const bf16x4 vv = lds_rows4_tr(C.v, SM::LDV, 16 * i, vc0 + 16 * nt, lane);
+#pragma unroll
+            for (int j = 0; j < 4; j++) y[j] += (float)vv[j];
+          }
+          x[i][nt] = y;
+        }
+      }
+      {
+        Fr ys[NSB][NN];
+#pragma unroll
+        for (int s = 0; s < NSB; s++)
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) ys[s][nt] = acc_as_b<O>(x, s, nt);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) x[mt][nt] = zero4();
+#pragma unroll
+        for (int s = 0; s < NSB; s++)
+#pragma unroll
+          for (int mt = 2 * s; mt < 4; mt++) {
+            const Fr tf = *reinterpret_cast<const Fr*>(R + kRecT + p_frag(mt, s) * 1024 + lane * 16);
+#pragma unroll
+            for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], tf, ys[s][nt]);
+          }
+      }
       if constexpr (OUT) {
         // o^T = fo o (S^T q^T) + x^T P^T.  Tile o[mt][nt] holds value columns
         // c0 + 16 nt + 4(lane/16) + j of token 16 mt + lane%16, so fo is one
@@ -767,24 +785,6 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
             const Fr pf = *reinterpret_cast<const Fr*>(R + kRecP + p_frag(mt, s) * 1024 + lane * 16);
 #pragma unroll
             for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], xs[nt], pf);
-          }
-        }
-        // four consecutive value columns of one token per lane: one 8-byte
-        // (bf16) store per tile, straight to HBM
-        typedef E E4 __attribute__((ext_vector_type(4)));
-        const int64_t tc = tb + (int64_t)it * BT;
-        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0 + 4 * g4);
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-          const int row = 16 * mt + ln;
-          if (tc + row < te) {
-#pragma unroll
-            for (int nt = 0; nt < NN; nt++) {
-              E4 v4;
-#pragma unroll
-              for (int j = 0; j < 4; j++) v4[j] = from_f<E>(o[mt][nt][j]);
-              *reinterpret_cast<E4*>(op + row * o_ld + 16 * nt) = v4;
-            }
           }
         }
       }
@@ -810,14 +810,35 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           // A = k^T: the dk rows of tile mt (permuted), tokens s KS.. down the
           // stored rows
           const int cdk = 32 * (mt >> 1) + 4 * (mt & 1);
-          const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, cdk, lane, 8);
-          const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, cdk, lane, 8);
+          const bf16x4 lo = lds_rows4_tr_x(C.k, SM::LDK, s * KS, cdk, lane);
+          const bf16x4 hi = lds_rows4_tr_x(C.k, SM::LDK, s * KS + 16, cdk, lane);
           const Fr kf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xv[s][nt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
+      }
+      if constexpr (OUT) {
+        // o, after the state update's products (which hide the latency of
+        // the last o products): four consecutive value columns of one token
+        // per lane, one 8-byte (bf16) store per tile, straight to HBM
+        typedef E E4 __attribute__((ext_vector_type(4)));
+        const int64_t tc = tb + (int64_t)it * BT;
+        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0 + 4 * g4);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const int row = 16 * mt + ln;
+          if (tc + row < te) {
+#pragma unroll
+            for (int nt = 0; nt < NN; nt++) {
+              E4 v4;
+#pragma unroll
+              for (int j = 0; j < 4; j++) v4[j] = from_f<E>(o[mt][nt][j]);
+              *reinterpret_cast<E4*>(op + row * o_ld + 16 * nt) = v4;
+            }
+          }
+        }
       }
     }
     lds_barrier();

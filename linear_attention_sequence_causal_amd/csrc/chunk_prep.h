@@ -5,22 +5,25 @@
 //
 // For one chunk of 64 tokens and one value head, with G the in-chunk cumsum
 // of g, Gamma_rc = e^{G_r - G_c}, rk / rq the l2norm factors of k and q (rq
-// includes the q scale), L = strict-lower(kh kh^T o Gamma) split into 16 x 16
-// blocks L_im and D_i = (I + diag(beta_i) L_ii)^-1, the chunk's corrected
-// values solve (I + diag(beta) L) x = diag(beta)(v - diag(e^G rk) k S).
-// Blockwise, with A_i = D_i diag(beta_i):
-//   x_i = A_i v_i - B_i (k S)_i - sum_{m<i} E_im x_m,
-//   B_i = A_i diag(e^G rk)_i,  E_im = A_i L_im,
-// so the state pass needs, besides q, k and v, only these 16 x 16 operators,
-// the decayed q k^T (P, with the q scale) and three row factors:
-//   fo = e^G rq  (o = fo o (q S) + P x),
+// includes the q scale) and L = strict-lower(kh kh^T o Gamma), the chunk's
+// corrected values solve (I + diag(beta) L) x = diag(beta)(v - fk o (k S)),
+// fk = e^G rk.  With the lower-triangular
+//   T = (I + diag(beta) L)^-1 diag(beta)
+// that is x = T (v - fk o (k S)), so the state pass needs, besides q, k and
+// v, only T, the decayed q k^T (P, with the q scale) and four row factors:
+//   fo = e^G rq  (o = fo o (q S) + P x),  fk,
 //   fd = rk e^{G_C - G}  (S <- e^{G_C} S + k^T (fd o x)),  eC = e^{G_C}.
+//
+// T is formed blockwise over 16-row blocks: D_i = (I + diag(beta_i) L_ii)^-1
+// (a nilpotent series), A_i = D_i diag(beta_i), E_im = A_i L_im, and then
+// T_ii = A_i, T_im = -sum_{m <= j < i} E_ij T_jm: column block m of T only
+// involves column block m, so each wave solves one.
 //
 // One workgroup computes the raw products q k^T and k k^T of a chunk once per
 // q/k head and serves every value head of that head (GQA).  The record of a
-// (chunk, value head) stores each operator as MFMA A fragments in lane order,
-// so the state pass copies it into LDS and reads each lane's fragment with
-// one load.
+// (chunk, value head) stores P and T as MFMA A fragments in lane order, so
+// the state pass copies it into LDS and reads each lane's fragment with one
+// load.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,29 +35,30 @@
 namespace gdn_chunk {
 
 // Record of one (chunk, value head), bytes:
-//   [kRecP,  +6 KiB)  P as six 16x16x32 A fragments (16 B a lane): row block
-//                     mt, contraction half s, for (mt, s) in kPFrag order
-//   [kRecA,  +2 KiB)  A_i, i = 0..3, 16x16x16 A fragments (8 B a lane)
-//   [kRecNB, +2 KiB)  -B_i
-//   [kRecNE, +3 KiB)  -E_im for (i, m) in kEPair order
-//   [kRecF, ...)      fo[64], fd[64], eC (fp32)
+//   [kRecP, +6 KiB)  P as six 16x16x32 A fragments (16 B a lane): row block
+//                    mt, contraction half s, for (mt, s) in p_frag order
+//   [kRecT, +6 KiB)  T, same fragments
+//   [kRecF, ...)     fo[64], fd[64], fk[64], eC (fp32)
 constexpr int kRecP = 0;
-constexpr int kRecA = 6 * 1024;
-constexpr int kRecNB = kRecA + 4 * 512;
-constexpr int kRecNE = kRecNB + 4 * 512;
-constexpr int kRecF = kRecNE + 6 * 512;
-constexpr int kRecBytes = 14 * 1024;
-static_assert(kRecF + 2 * 256 + 16 <= kRecBytes, "record layout");
+constexpr int kRecT = 6 * 1024;
+constexpr int kRecF = 12 * 1024;
+constexpr int kRecBytes = 13 * 1024;
+static_assert(kRecF + 3 * 256 + 16 <= kRecBytes, "record layout");
 
-// P fragments that are not entirely above the diagonal: (mt, s) = index.
+// Fragments of a 64 x 64 lower-triangular operator that are not entirely
+// above the diagonal: (row block mt, contraction half s) -> index.
 __host__ __device__ constexpr int p_frag(int mt, int s) { return mt == 0 ? 0 : mt == 1 ? 1 : 2 * mt - 2 + s; }
-// (i, m) of the six blocks below the diagonal, in record order.
-__host__ __device__ constexpr int e_pair(int i, int m) { return i * (i - 1) / 2 + m; }
 
 namespace {
 
 constexpr int kPrepLd = 64 + 8;  // bf16 staging tiles [64][kPrepLd]
 constexpr int kPrepScLd = 20;    // fp32 16 x 16 scratch rows (16 + 4)
+
+// fp32 16 x 16 tiles of the staging area, per wave w from prep_tile0(w):
+// wave 0: L_00 and a work tile; wave w > 0: L_ww and the work tile of its
+// inversion, which then hold A_w and E_w0, followed by E_w1 .. E_w,w-1.
+__host__ __device__ constexpr int prep_tile0(int w) { return w == 0 ? 0 : w * (w + 1) / 2 + 1; }
+constexpr int kPrepTiles = 11;
 
 // The raw rows are dead once the products are formed, so the per-head staging
 // shares their space (four workgroups fit a CU).
@@ -67,9 +71,8 @@ struct PrepSmem {
   };
   struct Stage {
     alignas(16) bf16 sp[64 * kPrepLd];  // P, C-layout writes
-    alignas(16) bf16 sn[64 * kPrepLd];  // A_i on the diagonal blocks, -E_im below
-    alignas(16) bf16 sb[64 * 24];       // -B_i in rows 16 i .. 16 i + 15
-    alignas(16) float sc[4][2][16 * kPrepScLd];  // per wave: fp32 L_ii, work tile
+    alignas(16) bf16 st[64 * kPrepLd];  // T
+    alignas(16) float sc[kPrepTiles][16 * kPrepScLd];
   };
   union {
     Rows r;
@@ -140,7 +143,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   constexpr int NSK = DK / 32;
   __shared__ SM sm;
 
-  const int chunk = blockIdx.x, qa = blockIdx.y;
+  // Workgroup order: the q/k heads of one chunk take ids 8 apart, so they run
+  // together on one XCD (ids go round-robin over the 8 XCDs) and read the
+  // chunk's lines of g and beta (all heads of a token share a line) through
+  // its L2 once.
+  const int id = blockIdx.x;
+  const int qa = (id >> 3) % a.Hk, chunk = (id / (8 * a.Hk)) * 8 + (id & 7);
   if (chunk >= a.counts[1]) return;
   const int4 ce = a.chunk_tab[chunk];
   const int64_t tc = ce.x, te = ce.y;
@@ -201,13 +209,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     rqP[jj] = sm.rq[16 * iq + 4 * g4 + jj];
   }
   __syncthreads();  // every wave's products are formed: the rows' space is reused
-  // blocks of P above the diagonal that the fragments include stay zero
+  // blocks above the diagonal that the fragments include stay zero
   for (int e = tid; e < 64 * 64; e += 256) {
     const int r = e / 64, c = e % 64;
-    if ((c >> 4) > (r >> 4)) sm.u.s.sp[r * kPrepLd + c] = (bf16)0.f;
+    if ((c >> 4) > (r >> 4)) {
+      sm.u.s.sp[r * kPrepLd + c] = (bf16)0.f;
+      sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
+    }
   }
-  float* Lt = sm.u.s.sc[w][0];
-  float* wk = sm.u.s.sc[w][1];
+  float* const tiles = sm.u.s.sc[prep_tile0(w)];
+  float* Lt = tiles;                   // L_ww, then A_w
+  float* wk = tiles + 16 * kPrepScLd;  // work tile, then E_w0
   float* G = sm.wv[w][0];
   float* eG = sm.wv[w][1];
   float* bt = sm.wv[w][2];
@@ -237,19 +249,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     }
     const float GC = __shfl(Gv, 63, 64);
     const float egv = __expf(Gv);
+    const float fkv = egv * sm.rk[lane];
     G[lane] = Gv;
     eG[lane] = egv;
     bt[lane] = bv;
-    fk[lane] = egv * sm.rk[lane];
+    fk[lane] = fkv;
     if (w == 0) {
       float* F32 = reinterpret_cast<float*>(rec + kRecF);
       F32[lane] = egv * sm.rq[lane];                       // fo
       F32[64 + lane] = sm.rk[lane] * __expf(GC - Gv);      // fd
-      if (lane == 0) F32[128] = __expf(GC);                // eC
+      F32[128 + lane] = fkv;                               // fk
+      if (lane == 0) F32[192] = __expf(GC);                // eC
     }
     wave_lds_sync();
 
-    // diagonal L block -> fp32 scratch, then D, A = D diag(beta), -B
+    // diagonal L block -> fp32 scratch, then D and A_w = D diag(beta)
     floatx4 NC;
     {
       const int c = 16 * w + ln;
@@ -267,22 +281,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     const floatx4 D = prep_invert16(Lt, bt + 16 * w, NC, wk, lane);
     floatx4 Ai;
     {
-      const float bc = bt[16 * w + ln], fc = fk[16 * w + ln];
+      const float bc = bt[16 * w + ln];
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int row = 16 * w + 4 * g4 + jj;
-        Ai[jj] = D[jj] * bc;
-        sm.u.s.sn[row * kPrepLd + 16 * w + ln] = (bf16)Ai[jj];
-        sm.u.s.sb[row * 24 + ln] = (bf16)(-Ai[jj] * fc);
-      }
+      for (int jj = 0; jj < 4; jj++) Ai[jj] = D[jj] * bc;
     }
-    // E_wm = A_w L_wm for m < w (A_w as A operand through the work tile)
+    // E_wm = A_w L_wm for m < w (A_w as A operand through LDS), kept in fp32
+    // for the column solves of the other waves
     if (w > 0) {
-      wave_lds_sync();  // the inversion's last reads of the work tile are done
+      wave_lds_sync();  // the inversion's last reads of its tiles are done
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) wk[(4 * g4 + jj) * kPrepScLd + ln] = Ai[jj];
+      for (int jj = 0; jj < 4; jj++) Lt[(4 * g4 + jj) * kPrepScLd + ln] = Ai[jj];
       wave_lds_sync();
-      const floatx4 AA = F::load(wk, kPrepScLd, 0, 0, lane);
+      const floatx4 AA = F::load(Lt, kPrepScLd, 0, 0, lane);
       const float G0 = G[16 * w];
 #pragma unroll
       for (int t = 0; t < 3; t++) {
@@ -298,9 +308,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
         }
         floatx4 E = zero4();
         F::mma(E, AA, Lm);
+        float* et = wk + t * (16 * kPrepScLd);
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++)
-          sm.u.s.sn[(16 * w + 4 * g4 + jj) * kPrepLd + c] = (bf16)(-E[jj]);
+        for (int jj = 0; jj < 4; jj++) et[(4 * g4 + jj) * kPrepScLd + ln] = E[jj];
       }
     }
     // P blocks of row block iq
@@ -327,36 +337,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
         }
       }
     }
+    __syncthreads();  // every E block is in place
+    // column block m = w of T: T_ww = A_w, T_iw = -sum_{w <= j < i} E_ij T_jw
+    {
+      floatx4 Tc[4];  // static indices only (w is a runtime value)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (i <= w) {
+          Tc[i] = i == w ? Ai : zero4();
+          continue;
+        }
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int j = 0; j < 3; j++) {
+          if (j < w || j >= i) continue;
+          // E_ij: tile j + 1 of wave i (tile 0 holds A_i)
+          const float* et = sm.u.s.sc[prep_tile0(i) + 1 + j];
+          F::mma(acc, F::load(et, kPrepScLd, 0, 0, lane), Tc[j]);
+        }
+        Tc[i] = -acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (i < w) continue;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          sm.u.s.st[(16 * i + 4 * g4 + jj) * kPrepLd + 16 * w + ln] = (bf16)Tc[i][jj];
+      }
+    }
     __syncthreads();
-    // copy the operators out as A fragments in lane order
-    for (int i = tid; i < 6 * 64; i += 256) {
-      const int f = i >> 6, l = i & 63;
-      const int mt = f == 0 ? 0 : f == 1 ? 1 : (f + 2) >> 1, s = f < 2 ? 0 : (f & 1);
-      const bf16* src = sm.u.s.sp + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
+    // copy P and T out as A fragments in lane order
+    for (int i = tid; i < 12 * 64; i += 256) {
+      const int f6 = (i >> 6) % 6, l = i & 63;
+      const bool isT = i >= 6 * 64;
+      const int mt = f6 == 0 ? 0 : f6 == 1 ? 1 : (f6 + 2) >> 1, s = f6 < 2 ? 0 : (f6 & 1);
+      const bf16* src = (isT ? sm.u.s.st : sm.u.s.sp) + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
       bf16x8 v;
       const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
       const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
       v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-      *reinterpret_cast<bf16x8*>(rec + kRecP + f * 1024 + l * 16) = v;
-    }
-    for (int i = tid; i < 14 * 64; i += 256) {
-      const int f = i >> 6, l = i & 63;
-      const bf16* src;
-      int off;
-      if (f < 4) {
-        src = sm.u.s.sn + (16 * f + (l & 15)) * kPrepLd + 16 * f + 4 * (l >> 4);
-        off = kRecA + f * 512;
-      } else if (f < 8) {
-        src = sm.u.s.sb + (16 * (f - 4) + (l & 15)) * 24 + 4 * (l >> 4);
-        off = kRecNB + (f - 4) * 512;
-      } else {
-        const int e = f - 8;
-        const int ii = e == 0 ? 1 : e < 3 ? 2 : 3, mm = e - ii * (ii - 1) / 2;
-        src = sm.u.s.sn + (16 * ii + (l & 15)) * kPrepLd + 16 * mm + 4 * (l >> 4);
-        off = kRecNE + e * 512;
-      }
-      *reinterpret_cast<bf16x4*>(rec + off + l * 8) = *reinterpret_cast<const bf16x4*>(src);
+      *reinterpret_cast<bf16x8*>(rec + (isT ? kRecT : kRecP) + f6 * 1024 + l * 16) = v;
     }
     __syncthreads();  // staging is rewritten for the next value head
   }
@@ -364,7 +385,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
 
 template <int DK>
 int launch_prep(const PrepArgs& a, int64_t chunk_cap, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)chunk_cap, a.Hk), dim3(256), 0, stream, a);
+  const int64_t n = (chunk_cap + 7) / 8 * 8 * a.Hk;
+  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)n), dim3(256), 0, stream, a);
   return gdn::check_launch("chunk prep");
 }
 
