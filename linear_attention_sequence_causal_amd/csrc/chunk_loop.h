@@ -505,14 +505,19 @@ GDN_DEV int dk_of_row(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 
 // 4 bytes the 16-byte row reads of q and k, the loaders' stores and v's
 // transposing reads are then free of bank conflicts, and k's transposing
 // reads (one 8-byte half of each chunk) two-way instead of four-way.
-template <typename O, int DK, int DV, bool HAS_Q>
+template <typename O, int DK, int DV, bool OUT>
 struct WsSmem {
   static constexpr int PAD = 32 / (int)sizeof(O);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDV = DV + PAD;
-  alignas(16) char rec[kRecBytes];
+  // bytes of the record the pass reads (G and rk only in the output pass)
+  static constexpr int REC = OUT ? kRecEnd : kRecG;
+  alignas(16) char rec[REC];
+  alignas(16) char p[OUT ? 6 * 1024 : 16];  // P fragments, made by the loaders
+  alignas(16) float fo[OUT ? 64 : 4];       // e^G rq
+  alignas(16) float rq[OUT ? 64 : 4];       // l2norm factors of q (with the scale)
   alignas(16) O k[BT * LDK];
-  alignas(16) O q[HAS_Q ? BT * LDK : 8];
+  alignas(16) O q[OUT ? BT * LDK : 8];
   alignas(16) O v[BT * LDV];
 };
 
@@ -527,22 +532,22 @@ struct WsCfg {
   static constexpr int NL = 4;                                 // loader waves
   static constexpr int NT = (NC + NL) * 64;
   typedef WsSmem<E, DK, DV, OUT> SM;
-  // bytes of the record the consumers read (P only in the output pass)
-  static constexpr int REC0 = OUT ? 0 : kRecT;
   static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
 };
 
-// Loader registers: one chunk's rows and record, 16-byte vectors.
-template <typename E, int DK, int DV, bool HAS_Q, int REC0>
+// Loader registers: one chunk's rows and the first RECB bytes of its record,
+// 16-byte vectors.
+template <typename E, int DK, int DV, bool HAS_Q, int RECB>
 struct WsLoad {
   typedef typename Vec16<E>::type V16;
   static constexpr int NTL = 256;  // loader threads
   static constexpr int VE = Vec16<E>::N;
   static constexpr int QPR = DK / VE, VPR = DV / VE;
   static constexpr int PQ = BT * QPR / NTL, PV = BT * VPR / NTL;
-  static constexpr int RV = (kRecBytes - REC0) / 16;  // record vectors
+  static constexpr int RV = RECB / 16;  // record vectors
   static constexpr int PR = (RV + NTL - 1) / NTL;
-  static_assert(BT * QPR % NTL == 0 && BT * VPR % NTL == 0, "loader split");
+  static_assert(BT * QPR % NTL == 0 && BT * VPR % NTL == 0 && RECB % 16 == 0, "loader split");
+  static_assert(QPR <= 16 && NTL % QPR == 0, "a q row within one 16-lane group");
   V16 q[HAS_Q ? PQ : 1], k[PQ], v[PV];
   floatx4 r[PR];
 
@@ -567,17 +572,23 @@ struct WsLoad {
 #pragma unroll
     for (int p = 0; p < PR; p++) {
       const int i = tid + NTL * p;
-      if (i < RV) r[p] = *reinterpret_cast<const floatx4*>(rec + REC0 + 16 * i);
+      if (i < RV) r[p] = *reinterpret_cast<const floatx4*>(rec + 16 * i);
     }
   }
+  // rows into LDS (q and k chunk-swizzled); with q, also its l2norm factors
+  // (with the scale): a q row is QPR consecutive lanes
   template <class SM>
-  GDN_DEV void store(SM& sm, int tid) const {
+  GDN_DEV void store(SM& sm, int tid, float scale, int use_l2norm) const {
 #pragma unroll
     for (int p = 0; p < PQ; p++) {
       const int i = tid + NTL * p;
       const int row = i / QPR, vi = i % QPR;
       const int vx = vi ^ ((row >> 3) & 1);  // chunk swizzle of the q / k rows
-      if constexpr (HAS_Q) *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vx * VE) = q[p];
+      if constexpr (HAS_Q) {
+        *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vx * VE) = q[p];
+        const float ss = row_group_sum<QPR>(sum_sq(q[p]));
+        if (vi == 0) sm.rq[row] = use_l2norm ? scale * __builtin_amdgcn_rsqf(ss + 1e-6f) : scale;
+      }
       *reinterpret_cast<V16*>(sm.k + row * SM::LDK + vx * VE) = k[p];
     }
 #pragma unroll
@@ -589,8 +600,72 @@ struct WsLoad {
 #pragma unroll
     for (int p = 0; p < PR; p++) {
       const int i = tid + NTL * p;
-      if (i < RV) *reinterpret_cast<floatx4*>(sm.rec + REC0 + 16 * i) = r[p];
+      if (i < RV) *reinterpret_cast<floatx4*>(sm.rec + 16 * i) = r[p];
     }
+  }
+};
+
+// Hand-off among the consumer waves through an LDS counter, without a
+// workgroup barrier: each wave adds one when its part is stored (arrive) and
+// waits until `target` (NC a chunk so far) is reached.  Every consumer wave
+// runs the same iterations, so the wait ends.
+GDN_DEV void count_arrive(unsigned* count, int lane) {
+  wave_lds_sync();  // this wave's stores are done
+  if (lane == 0) __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+GDN_DEV void count_wait(unsigned* count, unsigned target) {
+  while (__hip_atomic_load(count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+}
+
+// The decayed q k^T of one chunk as the P fragments of the output product:
+// element (tok, tok') = rq_tok rk_tok' e^{G_tok - G_tok'} q_tok . k_tok' for
+// tok' <= tok.  Fragment (mt, s) holds in lane l row tok = 16 mt + l%16 and
+// in its half h (elements 4h .. 4h + 3) the columns tok' = 32 s + 16 h +
+// 4(l/16) + e: exactly the accumulator of the tile k_{j'} q_mt^T, j' = 2s + h.
+// The twelve halves are dealt to the waves that make them in this order (the
+// two that lie above the diagonal, all zero, last but two).
+constexpr int kPHalves = 12;
+__host__ __device__ constexpr int p_half_mt(int u) { return u < 8 ? (u < 4 ? (u == 0 ? 0 : u == 2 ? 1 : 2) : 3) : (u == 8 ? 0 : u == 10 ? 1 : 2); }
+__host__ __device__ constexpr int p_half_s(int u) { return u == 1 || u == 6 || u == 7 || u == 9 ? 1 : 0; }
+__host__ __device__ constexpr int p_half_h(int u) { return u == 5 || u == 7 || u >= 8 ? 1 : 0; }
+
+// One half of P being made: begin() reads the operands and issues the
+// products (no branches, so they interleave with the caller's next
+// products), finish() scales, masks and stores.
+template <int DK>
+struct PHalf {
+  int mt, s, h, jp;
+  floatx4 acc;
+  template <class SM>
+  GDN_DEV void begin(const SM& C, int u, int lane, bool real) {
+    mt = p_half_mt(u);
+    s = p_half_s(u);
+    h = p_half_h(u);
+    jp = 2 * s + h;
+    acc = zero4();
+    if (real) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ks++)
+        Mfma<bf16>::mma(acc, Mfma<bf16>::load_k8_x(C.k, SM::LDK, 16 * jp, 32 * ks, lane),
+                        Mfma<bf16>::load_k8_x(C.q, SM::LDK, 16 * mt, 32 * ks, lane));
+    }
+  }
+  template <class SM>
+  GDN_DEV void finish(SM& C, int lane) const {
+    const int g4 = lane >> 4, ln = lane & 15;
+    const float* Gv = reinterpret_cast<const float*>(C.rec + kRecG);
+    const int tok = 16 * mt + ln, tp0 = 16 * jp + 4 * g4;
+    const float rqt = C.rq[tok], Gt = Gv[tok];
+    const floatx4 rk4 = *reinterpret_cast<const floatx4*>(Gv + 64 + tp0);
+    const floatx4 G4 = *reinterpret_cast<const floatx4*>(Gv + tp0);
+    bf16x4 f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float val = acc[e] * rqt * rk4[e] * __expf(fminf(Gt - G4[e], 0.f));
+      f[e] = (bf16)(tp0 + e <= tok ? val : 0.f);
+    }
+    *reinterpret_cast<bf16x4*>(C.p + p_frag(mt, s) * 1024 + lane * 16 + h * 8) = f;
   }
 };
 
@@ -611,6 +686,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef typename CF::SM SM;
   static_assert(KS == 32, "bf16 fragments");
   __shared__ SM buf[2];
+  __shared__ unsigned p_count;  // consumer waves' P parts, a running count
+  if (OUT) {
+    if (threadIdx.x == 0) p_count = 0u;
+    __syncthreads();
+  }
 
   // Workgroup order: the value heads of one q/k head and segment take ids 8
   // apart, so they run together on one XCD (ids go round-robin over the 8
@@ -634,7 +714,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
 
   if (wave >= NC) {
     // ======================= loaders =======================
-    typedef WsLoad<E, DK, DV, OUT, CF::REC0> LD;
+    typedef WsLoad<E, DK, DV, OUT, SM::REC> LD;
     const int ltid = tid - NC * 64;
     const int qa = h / (Hv / a.Hk);
     const E* qp = (const E*)a.q + (int64_t)qa * DK;
@@ -646,7 +726,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
     for (int it = -1; it < nchunks; it++) {
       const int pc = it + 1;
       if (pc < nchunks) {
-        ld.store(buf[pc & 1], ltid);
+        ld.store(buf[pc & 1], ltid, a.scale, a.use_l2norm);
         if (pc + 1 < nchunks)
           ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (chunk0 + pc + 1) * rstride,
                   tb + (int64_t)(pc + 1) * BT, te, ltid);
@@ -687,6 +767,24 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
     if (it >= 0) {
       SM& C = buf[it & 1];
       const char* R = C.rec;
+      if constexpr (OUT) {
+        // this wave's share of the chunk's P fragments (halves wave,
+        // wave + NC, ...: every product issued before any is finished) and
+        // fo (wave 0); the other waves' shares are awaited before the o
+        // products
+        constexpr int NR = (kPHalves + NC - 1) / NC;
+        PHalf<DK> ph[NR];
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+          const int u = wave + r * NC;
+          if (u < kPHalves) ph[r].begin(C, u, lane, p_half_s(u) * 2 + p_half_h(u) <= p_half_mt(u));
+        }
+#pragma unroll
+        for (int r = 0; r < NR; r++)
+          if (wave + r * NC < kPHalves) ph[r].finish(C, lane);
+        if (wave == 0) C.fo[lane] = __expf(reinterpret_cast<const float*>(R + kRecG)[lane]) * C.rq[lane];
+        count_arrive(&p_count, lane);
+      }
       if constexpr (MODE == kStates) {
         // the state entering this chunk, for the backward
         float* dst = a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
@@ -725,10 +823,9 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           }
         }
       }
-      const float* Fo = reinterpret_cast<const float*>(R + kRecF);
-      const float* Fd = Fo + 64;
-      const float* Fk = Fo + 128;
-      const float eC = Fo[192];
+      const float* Fd = reinterpret_cast<const float*>(R + kRecF);
+      const float* Fk = Fd + 64;
+      const float eC = Fd[128];
       // x = T (v - fk o (k S)): the right side in accumulator layout (token
       // rows), then one lower-triangular product with T's fragments
 #pragma unroll
@@ -765,13 +862,14 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           }
       }
       if constexpr (OUT) {
+        count_wait(&p_count, (unsigned)NC * (unsigned)(it + 1));  // every part of P is in place
         // o^T = fo o (S^T q^T) + x^T P^T.  Tile o[mt][nt] holds value columns
         // c0 + 16 nt + 4(lane/16) + j of token 16 mt + lane%16, so fo is one
-        // factor per lane, x fragments are the A operands and the record's P
-        // fragments (rows = tokens) the B operands.
+        // factor per lane, x fragments are the A operands and the P fragments
+        // (rows = tokens) the B operands.
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const float fo = Fo[16 * mt + ln];
+          const float fo = C.fo[16 * mt + ln];
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) o[mt][nt] *= fo;
         }
@@ -782,7 +880,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           for (int nt = 0; nt < NN; nt++) xs[nt] = acc_as_b<O>(x, s, nt);
 #pragma unroll
           for (int mt = 2 * s; mt < 4; mt++) {
-            const Fr pf = *reinterpret_cast<const Fr*>(R + kRecP + p_frag(mt, s) * 1024 + lane * 16);
+            const Fr pf = *reinterpret_cast<const Fr*>(C.p + p_frag(mt, s) * 1024 + lane * 16);
 #pragma unroll
             for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], xs[nt], pf);
           }
@@ -959,7 +1057,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   if constexpr (PREP) {
     char* rec = ws + pl.off_rec;
     a.rec = rec;
-    PrepArgs pa{a.q, a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.scale, a.use_l2norm, pp.chunk_tab,
+    PrepArgs pa{a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab,
                 pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
   }

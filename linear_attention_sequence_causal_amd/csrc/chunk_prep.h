@@ -4,26 +4,25 @@
 // then consumes).
 //
 // For one chunk of 64 tokens and one value head, with G the in-chunk cumsum
-// of g, Gamma_rc = e^{G_r - G_c}, rk / rq the l2norm factors of k and q (rq
-// includes the q scale) and L = strict-lower(kh kh^T o Gamma), the chunk's
-// corrected values solve (I + diag(beta) L) x = diag(beta)(v - fk o (k S)),
-// fk = e^G rk.  With the lower-triangular
+// of g, Gamma_rc = e^{G_r - G_c}, rk the l2norm factors of k and
+// L = strict-lower(kh kh^T o Gamma), the chunk's corrected values solve
+// (I + diag(beta) L) x = diag(beta)(v - fk o (k S)), fk = e^G rk.  With the
+// lower-triangular
 //   T = (I + diag(beta) L)^-1 diag(beta)
-// that is x = T (v - fk o (k S)), so the state pass needs, besides q, k and
-// v, only T, the decayed q k^T (P, with the q scale) and four row factors:
-//   fo = e^G rq  (o = fo o (q S) + P x),  fk,
-//   fd = rk e^{G_C - G}  (S <- e^{G_C} S + k^T (fd o x)),  eC = e^{G_C}.
+// that is x = T (v - fk o (k S)), so the state passes need, besides k and v,
+// only T and the row factors fk, fd = rk e^{G_C - G} (S <- e^{G_C} S +
+// k^T (fd o x)) and eC = e^{G_C}.  The output pass forms the decayed q k^T
+// (P) and fo = e^G rq itself from its q rows, G and rk.
 //
 // T is formed blockwise over 16-row blocks: D_i = (I + diag(beta_i) L_ii)^-1
 // (a nilpotent series), A_i = D_i diag(beta_i), E_im = A_i L_im, and then
 // T_ii = A_i, T_im = -sum_{m <= j < i} E_ij T_jm: column block m of T only
 // involves column block m, so each wave solves one.
 //
-// One workgroup computes the raw products q k^T and k k^T of a chunk once per
-// q/k head and serves every value head of that head (GQA).  The record of a
-// (chunk, value head) stores P and T as MFMA A fragments in lane order, so
-// the state pass copies it into LDS and reads each lane's fragment with one
-// load.
+// One workgroup computes the raw product k k^T of a chunk once per q/k head
+// and serves every value head of that head (GQA).  The record of a (chunk,
+// value head) stores T as MFMA A fragments in lane order, so the state pass
+// copies it into LDS and reads each lane's fragment with one load.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,15 +34,16 @@
 namespace gdn_chunk {
 
 // Record of one (chunk, value head), bytes:
-//   [kRecP, +6 KiB)  P as six 16x16x32 A fragments (16 B a lane): row block
+//   [kRecT, +6 KiB)  T as six 16x16x32 A fragments (16 B a lane): row block
 //                    mt, contraction half s, for (mt, s) in p_frag order
-//   [kRecT, +6 KiB)  T, same fragments
-//   [kRecF, ...)     fo[64], fd[64], fk[64], eC (fp32)
-constexpr int kRecP = 0;
-constexpr int kRecT = 6 * 1024;
-constexpr int kRecF = 12 * 1024;
-constexpr int kRecBytes = 13 * 1024;
-static_assert(kRecF + 3 * 256 + 16 <= kRecBytes, "record layout");
+//   [kRecF, kRecG)   fd[64], fk[64], eC (fp32)
+//   [kRecG, kRecEnd) G[64], rk[64] (fp32; read by the output pass only)
+constexpr int kRecT = 0;
+constexpr int kRecF = 6 * 1024;
+constexpr int kRecG = kRecF + 2 * 256 + 16;
+constexpr int kRecEnd = kRecG + 2 * 256;
+constexpr int kRecBytes = 7424;  // record stride, a multiple of 256 bytes
+static_assert(kRecEnd <= kRecBytes && kRecG % 16 == 0 && kRecEnd % 16 == 0, "record layout");
 
 // Fragments of a 64 x 64 lower-triangular operator that are not entirely
 // above the diagonal: (row block mt, contraction half s) -> index.
@@ -65,32 +65,24 @@ constexpr int kPrepTiles = 11;
 template <int DK>
 struct PrepSmem {
   static constexpr int LDK = DK + 8;
-  struct Rows {
-    alignas(16) bf16 q[64 * LDK];
-    alignas(16) bf16 k[64 * LDK];
-  };
   struct Stage {
-    alignas(16) bf16 sp[64 * kPrepLd];  // P, C-layout writes
-    alignas(16) bf16 st[64 * kPrepLd];  // T
+    alignas(16) bf16 st[64 * kPrepLd];  // T, C-layout writes
     alignas(16) float sc[kPrepTiles][16 * kPrepScLd];
   };
   union {
-    Rows r;
+    alignas(16) bf16 k[64 * LDK];  // raw rows, dead once k k^T is formed
     Stage s;
   } u;
-  alignas(16) float rq[64];
   alignas(16) float rk[64];
   alignas(16) float wv[4][4][64];  // per wave: G, e^G, beta, e^G rk
 };
 
 struct PrepArgs {
-  const void* q;
   const void* k;
   int64_t ld_qk;
   const float* g;
   const float* beta;
   int Hk, Hv;
-  float scale;
   int use_l2norm;
   const int4* chunk_tab;
   const int32_t* counts;
@@ -132,7 +124,7 @@ GDN_DEV floatx4 prep_invert16(const float* Lt, const float* bb, const floatx4& N
 
 // One (chunk, q/k head) per workgroup of four waves.  Wave w owns the L
 // blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
-// the wave) and the P blocks of row block 3 - w.
+// the wave) and column block w of T.
 template <int DK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void chunk_prep_kernel(PrepArgs a) {
   typedef Mfma<bf16> M;
@@ -155,67 +147,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, ln = lane & 15;
-  const int iq = 3 - w;
   const int GR = a.Hv / a.Hk;
 
-  // raw rows (zero past the sequence end) and the l2norm factors
+  // raw k rows (zero past the sequence end) and their l2norm factors
   {
     typedef bf16x8 V;
     constexpr int QPR = DK / 8;
-    const bf16* qp = (const bf16*)a.q + (int64_t)qa * DK;
     const bf16* kp = (const bf16*)a.k + (int64_t)qa * DK;
 #pragma unroll
     for (int p = 0; p < 64 * QPR / 256; p++) {
       const int i = tid + 256 * p;
       const int row = i / QPR, vi = i % QPR;
       const int64_t t = tc + row;
-      V qv = zero_vec16<bf16>(), kv = zero_vec16<bf16>();
-      if (t < te) {
-        qv = *reinterpret_cast<const V*>(qp + t * a.ld_qk + vi * 8);
-        kv = *reinterpret_cast<const V*>(kp + t * a.ld_qk + vi * 8);
-      }
-      *reinterpret_cast<V*>(sm.u.r.q + row * LDK + vi * 8) = qv;
-      *reinterpret_cast<V*>(sm.u.r.k + row * LDK + vi * 8) = kv;
-      const float qs = row_group_sum<QPR>(sum_sq(qv)), ks = row_group_sum<QPR>(sum_sq(kv));
-      if (vi == 0) {
-        sm.rq[row] = a.use_l2norm ? a.scale * __builtin_amdgcn_rsqf(qs + 1e-6f) : a.scale;
-        sm.rk[row] = a.use_l2norm ? __builtin_amdgcn_rsqf(ks + 1e-6f) : 1.f;
-      }
+      V kv = zero_vec16<bf16>();
+      if (t < te) kv = *reinterpret_cast<const V*>(kp + t * a.ld_qk + vi * 8);
+      *reinterpret_cast<V*>(sm.u.k + row * LDK + vi * 8) = kv;
+      const float ks = row_group_sum<QPR>(sum_sq(kv));
+      if (vi == 0) sm.rk[row] = a.use_l2norm ? __builtin_amdgcn_rsqf(ks + 1e-6f) : 1.f;
     }
   }
   __syncthreads();
 
-  // raw products of this wave's five blocks: k_w k_w^T, q_iq k_iq^T, then the
-  // three below the diagonal: k_w k_t^T (t < w), q_iq k_(t-w)^T
-  floatx4 rD = zero4(), rDP = zero4(), rO[3];
+  // raw products of this wave's blocks: k_w k_w^T and k_w k_t^T (t < w)
+  floatx4 rD = zero4(), rO[3];
 #pragma unroll
   for (int t = 0; t < 3; t++) rO[t] = zero4();
 #pragma unroll
   for (int s = 0; s < NSK; s++) {
-    const Fr ak = M::load(sm.u.r.k, LDK, 16 * w, 32 * s, lane);
-    const Fr aq = M::load(sm.u.r.q, LDK, 16 * iq, 32 * s, lane);
-    M::mma(rD, ak, M::load(sm.u.r.k, LDK, 16 * w, 32 * s, lane));
-    M::mma(rDP, aq, M::load(sm.u.r.k, LDK, 16 * iq, 32 * s, lane));
+    const Fr ak = M::load(sm.u.k, LDK, 16 * w, 32 * s, lane);
+    M::mma(rD, ak, ak);
 #pragma unroll
-    for (int t = 0; t < 3; t++) {
-      const int j = t < w ? t : t - w;
-      M::mma(rO[t], t < w ? ak : aq, M::load(sm.u.r.k, LDK, 16 * j, 32 * s, lane));
-    }
+    for (int t = 0; t < 3; t++)
+      if (t < w) M::mma(rO[t], ak, M::load(sm.u.k, LDK, 16 * t, 32 * s, lane));
   }
-  float rkL[4], rqP[4];
+  float rkL[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; jj++) {
-    rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
-    rqP[jj] = sm.rq[16 * iq + 4 * g4 + jj];
-  }
+  for (int jj = 0; jj < 4; jj++) rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
   __syncthreads();  // every wave's products are formed: the rows' space is reused
   // blocks above the diagonal that the fragments include stay zero
   for (int e = tid; e < 64 * 64; e += 256) {
     const int r = e / 64, c = e % 64;
-    if ((c >> 4) > (r >> 4)) {
-      sm.u.s.sp[r * kPrepLd + c] = (bf16)0.f;
-      sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
-    }
+    if ((c >> 4) > (r >> 4)) sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
   }
   float* const tiles = sm.u.s.sc[prep_tile0(w)];
   float* Lt = tiles;                   // L_ww, then A_w
@@ -256,10 +228,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     fk[lane] = fkv;
     if (w == 0) {
       float* F32 = reinterpret_cast<float*>(rec + kRecF);
-      F32[lane] = egv * sm.rq[lane];                       // fo
-      F32[64 + lane] = sm.rk[lane] * __expf(GC - Gv);      // fd
-      F32[128 + lane] = fkv;                               // fk
-      if (lane == 0) F32[192] = __expf(GC);                // eC
+      F32[lane] = sm.rk[lane] * __expf(GC - Gv);  // fd
+      F32[64 + lane] = fkv;                       // fk
+      if (lane == 0) F32[128] = __expf(GC);       // eC
+      float* G32 = reinterpret_cast<float*>(rec + kRecG);
+      G32[lane] = Gv;
+      G32[64 + lane] = sm.rk[lane];
     }
     wave_lds_sync();
 
@@ -313,30 +287,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
         for (int jj = 0; jj < 4; jj++) et[(4 * g4 + jj) * kPrepScLd + ln] = E[jj];
       }
     }
-    // P blocks of row block iq
-    {
-      const int c = 16 * iq + ln;
-      const float Gc = G[c], fc = sm.rk[c];
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int row = 16 * iq + 4 * g4 + jj;
-        const float e = __expf(fminf(G[row] - Gc, 0.f));
-        sm.u.s.sp[row * kPrepLd + c] = (bf16)(row >= c ? rDP[jj] * rqP[jj] * fc * e : 0.f);
-      }
-      const float G0 = G[16 * iq];
-#pragma unroll
-      for (int t = 0; t < 3; t++) {
-        if (t < w) continue;
-        const int j = t - w;
-        const int cj = 16 * j + ln;
-        const float bcol = sm.rk[cj] * __expf(G0 - G[cj]);
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int row = 16 * iq + 4 * g4 + jj;
-          sm.u.s.sp[row * kPrepLd + cj] = (bf16)(rO[t][jj] * rqP[jj] * __expf(G[row] - G0) * bcol);
-        }
-      }
-    }
     __syncthreads();  // every E block is in place
     // column block m = w of T: T_ww = A_w, T_iw = -sum_{w <= j < i} E_ij T_jw
     {
@@ -366,18 +316,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
       }
     }
     __syncthreads();
-    // copy P and T out as A fragments in lane order
-    for (int i = tid; i < 12 * 64; i += 256) {
-      const int f6 = (i >> 6) % 6, l = i & 63;
-      const bool isT = i >= 6 * 64;
-      const int mt = f6 == 0 ? 0 : f6 == 1 ? 1 : (f6 + 2) >> 1, s = f6 < 2 ? 0 : (f6 & 1);
-      const bf16* src = (isT ? sm.u.s.st : sm.u.s.sp) + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
+    // copy T out as A fragments in lane order
+    for (int i = tid; i < 6 * 64; i += 256) {
+      const int f = i >> 6, l = i & 63;
+      const int mt = f == 0 ? 0 : f == 1 ? 1 : (f + 2) >> 1, s = f < 2 ? 0 : (f & 1);
+      const bf16* src = sm.u.s.st + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
       bf16x8 v;
       const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
       const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
       v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-      *reinterpret_cast<bf16x8*>(rec + (isT ? kRecT : kRecP) + f6 * 1024 + l * 16) = v;
+      *reinterpret_cast<bf16x8*>(rec + kRecT + f * 1024 + l * 16) = v;
     }
     __syncthreads();  // staging is rewritten for the next value head
   }
