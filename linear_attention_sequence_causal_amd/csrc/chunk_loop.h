@@ -964,40 +964,60 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   }
 }
 
-// Scan over segment summaries (fp32): per (sequence, head, 16 columns).
+// Scan over segment summaries (fp32): per (sequence, head, 16 columns),
+// h <- M h + E over the segments of the sequence, with fp32 MFMA products
+// (wave w owns rows 32 w .. 32 w + 31 of h; M's rows are the A operands,
+// read straight from the summaries, h the B operand from LDS).
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ seg_state,
-                                                       float* __restrict__ seg_init,
-                                                       const float* __restrict__ h0,
-                                                       const int32_t* __restrict__ seq_off,
-                                                       const int32_t* __restrict__ seq_nseg, int Hv) {
+__global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restrict__ seg_state,
+                                                          float* __restrict__ seg_init,
+                                                          const float* __restrict__ h0,
+                                                          const int32_t* __restrict__ seq_off,
+                                                          const int32_t* __restrict__ seq_nseg, int Hv) {
+  typedef Mfma<float> M;
+  constexpr int LDX = DK + DV;
+  constexpr int NKT = DK / 16;
+  static_assert(DK % 32 == 0, "two row tiles per wave");
   const int n = blockIdx.x, h = blockIdx.y, cb = blockIdx.z * 16;
   const int nseg = seq_nseg[n];
   if (nseg <= 1) return;
   const int off = seq_off[n];
   __shared__ float hs[DK][16];
-  const int t = threadIdx.x, col = t & 15, r0 = t >> 4;
-  for (int r = r0; r < DK; r += 16)
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g4 = lane >> 4, ln = lane & 15;
+  for (int i = t; i < DK * 16; i += DK * 2) {
+    const int r = i >> 4, col = i & 15;
     hs[r][col] = h0 ? h0[(((int64_t)n * Hv + h) * DK + r) * DV + cb + col] : 0.f;
+  }
   __syncthreads();
   for (int p = 0; p + 1 < nseg; p++) {
-    const float* X = seg_state + ((int64_t)(off + p) * Hv + h) * DK * (DK + DV);
-    float nv[DK / 16];
+    const float* X = seg_state + ((int64_t)(off + p) * Hv + h) * DK * LDX;
+    floatx4 acc[2];
+    floatx4 af[2][NKT];
 #pragma unroll
-    for (int i = 0; i < DK / 16; i++) {
-      const int r = r0 + 16 * i;
-      float acc = X[r * (DK + DV) + DK + cb + col];
-      for (int m = 0; m < DK; m++) acc += X[r * (DK + DV) + m] * hs[m][col];
-      nv[i] = acc;
+    for (int i = 0; i < 2; i++) {
+      const int mt = 2 * w + i;
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = X[(16 * mt + 4 * g4 + j) * LDX + DK + cb + ln];
+#pragma unroll
+      for (int kt = 0; kt < NKT; kt++) af[i][kt] = M::load(X, LDX, 16 * mt, 16 * kt, lane);
     }
-    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++) {
+      const floatx4 bf = M::load_col(&hs[0][0], 16, 0, 16 * kt, lane);
+#pragma unroll
+      for (int i = 0; i < 2; i++) M::mma(acc[i], af[i][kt], bf);
+    }
+    __syncthreads();  // every wave has read h
     float* dst = seg_init + ((int64_t)(off + p + 1) * Hv + h) * DK * DV;
 #pragma unroll
-    for (int i = 0; i < DK / 16; i++) {
-      const int r = r0 + 16 * i;
-      hs[r][col] = nv[i];
-      dst[r * DV + cb + col] = nv[i];
-    }
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int r = 16 * (2 * w + i) + 4 * g4 + j;
+        hs[r][ln] = acc[i][j];
+        dst[r * DV + cb + ln] = acc[i][j];
+      }
     __syncthreads();
   }
 }
@@ -1064,7 +1084,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   if (pl.split) {
     launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(256), 0, stream,
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(DK * 2), 0, stream,
                        a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv);
     if (int rc = gdn::check_launch("chunk scan")) return rc;
   }

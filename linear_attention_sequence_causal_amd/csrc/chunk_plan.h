@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
                                                    int seg_len, int seg_cap, int chunk_cap,
                                                    PlanPtrs pp) {
   __shared__ int buf[256];
+  __shared__ int sc_off[257];     // chunk offsets of this block's sequences (block-local)
+  __shared__ int sc_beg[256], sc_end[256];
   const int t = threadIdx.x;
   int run_seg = 0, run_chunk = 0;
   for (int base = 0; base < N; base += 256) {
@@ -83,9 +85,29 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
             make_int4(n, (int)a, (int)b, (p == 0 ? kFirst : 0) | (p == ns - 1 ? kLast : 0));
         pp.seg_chunk0[off_s + p] = off_c + p * (seg_len / 64);
       }
-      if (pp.chunk_tab)
-        for (int c = 0; c < nc && off_c + c < chunk_cap; c++)
-          pp.chunk_tab[off_c + c] = make_int4((int)(s + 64 * c), (int)e, n, 0);
+    }
+    if (pp.chunk_tab) {
+      // the chunk table of these (up to) 256 sequences, filled by all threads:
+      // entry c of the block belongs to the sequence whose block-local range
+      // [sc_off[i], sc_off[i + 1]) holds it (binary search)
+      sc_off[t] = off_c - run_chunk;
+      sc_beg[t] = (int)s;
+      sc_end[t] = (int)e;
+      if (t == 0) sc_off[256] = tot_c;
+      __syncthreads();
+      const int nseq = N - base < 256 ? N - base : 256;
+      for (int c = t; c < tot_c; c += 256) {
+        int lo = 0, hi = nseq - 1;  // last i with sc_off[i] <= c
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sc_off[mid] <= c) lo = mid;
+          else hi = mid - 1;
+        }
+        const int gc = run_chunk + c;
+        if (gc < chunk_cap)
+          pp.chunk_tab[gc] = make_int4(sc_beg[lo] + 64 * (c - sc_off[lo]), sc_end[lo], base + lo, 0);
+      }
+      __syncthreads();
     }
     run_seg += tot_s;
     run_chunk += tot_c;
