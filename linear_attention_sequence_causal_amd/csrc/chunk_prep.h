@@ -149,6 +149,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   const int g4 = lane >> 4, ln = lane & 15;
   const int GR = a.Hv / a.Hk;
 
+  // gates of the 64 tokens, one per lane (zero past the end), for the first
+  // value head: issued first, so they arrive with the rows; the next value
+  // head's are loaded one head ahead
+  const int64_t tg = tc + lane;
+  float gn = 0.f, bn = 0.f;
+  if (tg < te) {
+    gn = a.g[tg * a.Hv + qa * GR];
+    bn = a.beta[tg * a.Hv + qa * GR];
+  }
+
   // raw k rows (zero past the sequence end) and their l2norm factors
   {
     typedef bf16x8 V;
@@ -197,14 +207,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   float* bt = sm.wv[w][2];
   float* fk = sm.wv[w][3];
 
-  // gates of the 64 tokens, one per lane (zero past the end), loaded one
-  // value head ahead
-  const int64_t tg = tc + lane;
-  float gn = 0.f, bn = 0.f;
-  if (tg < te) {
-    gn = a.g[tg * a.Hv + qa * GR];
-    bn = a.beta[tg * a.Hv + qa * GR];
-  }
   for (int r = 0; r < GR; r++) {
     const int h = qa * GR + r;
     char* rec = a.rec + ((int64_t)chunk * a.Hv + h) * kRecBytes;
