@@ -75,9 +75,12 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
 // bytes of the prepared record per (chunk, value head): bfloat16 only
 size_t chunk_rec_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? (size_t)kRecBytes : 0; }
 
+// the summary pass can run first segments in the output mode (same block shape)
+bool chunk_first_out(int32_t dk, int32_t dv, gdn_dtype dt) { return dt == GDN_BF16 && dk == 128 && dv == 128; }
+
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
   if (T < 0 || N < 0 || Hv < 1) return 0;
-  return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt)).end;
+  return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt), chunk_first_out(dk, dv, dt)).end;
 }
 }  // namespace gdn
 
@@ -93,7 +96,7 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const 
   if (T > 0 && !o) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: o is null");
   if (T > 0 && !gdn::aligned16(o)) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: o must be 16-byte aligned");
   if (N > 0 && ht && !cu_seqlens) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: null cu_seqlens");
-  const Plan pl = make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt));
+  const Plan pl = make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), gdn::chunk_first_out(dk, dv, dt));
   if (!ws || ws_bytes < pl.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_fwd: workspace needs %zu bytes, 256-byte aligned",
                      pl.end);

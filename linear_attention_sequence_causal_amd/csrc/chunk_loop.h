@@ -72,6 +72,8 @@ struct LoopArgs {
   float* states;     // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk
   const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
   int seg_cap;       // capacity of the segment table
+  int first_done;    // the output of every sequence's first segment is already written
+  int seg_base, seg_span;  // the state-pass grid covers segments seg_base .. + seg_span - 1
 };
 
 // LDS of the chunk loop (one chunk of one head at a time; rows padded by
@@ -669,8 +671,13 @@ struct PHalf {
   }
 };
 
+// One (segment, value head) of the state pass in mode MODE, from LDS buffers
+// `buf` and the P hand-off counter (zeroed).  first_summary: the segment is a
+// sequence's first, run in the output mode from h0, and its end state goes to
+// the segment summaries as [0 | S] (for the scan).
 template <typename E, int DK, int DV, int MODE>
-__global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
+GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf, unsigned* p_count_ptr,
+                     int seg, int h, int4 ent, bool first_summary) {
   typedef WsCfg<E, DK, DV, MODE> CF;
   typedef E O;
   typedef Mfma<O> M;
@@ -685,23 +692,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   constexpr bool OUT = CF::OUT;
   typedef typename CF::SM SM;
   static_assert(KS == 32, "bf16 fragments");
-  __shared__ SM buf[2];
-  __shared__ unsigned p_count;  // consumer waves' P parts, a running count
-  if (OUT) {
-    if (threadIdx.x == 0) p_count = 0u;
-    __syncthreads();
-  }
-
-  // Workgroup order: the value heads of one q/k head and segment take ids 8
-  // apart, so they run together on one XCD (ids go round-robin over the 8
-  // XCDs) and share q and k through its L2.
-  const int GR = a.Hv / a.Hk;
-  const int id = blockIdx.x;
-  const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
-  const int seg = grp % a.seg_cap, h = (grp / a.seg_cap) * GR + member;
-  if (grp >= a.seg_cap * a.Hk || seg >= a.counts[0]) return;
-  const int4 ent = a.seg_table[seg];
-  if (MODE == kSummary && (ent.w & kLast)) return;
+  unsigned& p_count = *p_count_ptr;
   const int n = ent.x;
   const int64_t tb = ent.y, te = ent.z;
   const int Hv = a.Hv;
@@ -942,12 +933,17 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
     lds_barrier();
   }
 
-  // final state: ht (output) or the summary X = [M | E]
+  // final state: ht (output), the summary X = [M | E], or for a first segment
+  // run from h0 the summary [0 | S]
   float* dst = nullptr;
   int ld = DV;
-  if (MODE == kSummary) {
+  if (MODE == kSummary || first_summary) {
     dst = a.seg_state + ((int64_t)seg * Hv + h) * DK * (DK + DV);
     ld = DK + DV;
+    if (first_summary) {
+      for (int i = tid; i < DK * DK; i += NC * 64) dst[(i / DK) * (DK + DV) + i % DK] = 0.f;
+      dst += DK;
+    }
   } else if ((ent.w & kLast) && a.ht) {
     dst = a.ht + ((int64_t)n * Hv + h) * DK * DV;
   }
@@ -962,6 +958,55 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
           dst[row * ld + col] = S[mt][nt][j];
         }
   }
+}
+
+template <typename E, int DK, int DV, int MODE>
+__global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
+  typedef typename WsCfg<E, DK, DV, MODE>::SM SM;
+  __shared__ SM buf[2];
+  __shared__ unsigned p_count;  // consumer waves' P parts, a running count
+  if (MODE == kOut) {
+    if (threadIdx.x == 0) p_count = 0u;
+    __syncthreads();
+  }
+  // Workgroup order: the value heads of one q/k head and segment take ids 8
+  // apart, so they run together on one XCD (ids go round-robin over the 8
+  // XCDs) and share q and k through its L2; with a span of 8 segments, XCD x
+  // runs segment seg_base + x of every head.
+  const int GR = a.Hv / a.Hk;
+  const int id = blockIdx.x;
+  const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
+  const int seg = a.seg_base + grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
+  if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
+  const int4 ent = a.seg_table[seg];
+  if (MODE == kSummary && (ent.w & kLast)) return;
+  if (MODE == kOut && a.first_done && (ent.w & kFirst)) return;
+  ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent, false);
+}
+
+// The summary pass when every sequence's first segment runs the output mode
+// there (from h0) instead of a summary: one launch, the mode chosen per
+// workgroup (both modes have the same waves).
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) void chunk_ws_first_kernel(LoopArgs a) {
+  typedef typename WsCfg<E, DK, DV, kOut>::SM SMO;
+  typedef typename WsCfg<E, DK, DV, kSummary>::SM SMS;
+  static_assert(WsCfg<E, DK, DV, kOut>::NT == WsCfg<E, DK, DV, kSummary>::NT, "one block shape");
+  constexpr size_t BYTES = 2 * (sizeof(SMO) > sizeof(SMS) ? sizeof(SMO) : sizeof(SMS));
+  __shared__ __attribute__((aligned(16))) char raw[BYTES];
+  __shared__ unsigned p_count;
+  if (threadIdx.x == 0) p_count = 0u;
+  __syncthreads();
+  const int GR = a.Hv / a.Hk;
+  const int id = blockIdx.x;
+  const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
+  const int seg = a.seg_base + grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
+  if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
+  const int4 ent = a.seg_table[seg];
+  if (ent.w & kFirst)
+    ws_body<E, DK, DV, kOut>(a, reinterpret_cast<SMO*>(raw), &p_count, seg, h, ent, !(ent.w & kLast));
+  else if (!(ent.w & kLast))
+    ws_body<E, DK, DV, kSummary>(a, reinterpret_cast<SMS*>(raw), &p_count, seg, h, ent, false);
 }
 
 // Scan over segment summaries (fp32): per (sequence, head, 16 columns),
@@ -1049,7 +1094,7 @@ void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
   const dim3 grid((unsigned)pl.seg_cap, a.Hv);
   if constexpr (uses_prep<E, DK, DV, MODE>()) {
     const int64_t unit = 8 * (int64_t)(a.Hv / a.Hk);
-    const int64_t n = (pl.seg_cap * a.Hv + unit - 1) / unit * unit;
+    const int64_t n = ((int64_t)a.seg_span * a.Hv + unit - 1) / unit * unit;
     hipLaunchKernelGGL((chunk_ws_kernel<E, DK, DV, MODE>), dim3((unsigned)n),
                        dim3(WsCfg<E, DK, DV, MODE>::NT), 0, stream, a);
   } else {
@@ -1071,7 +1116,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   a.seg_chunk0 = pp.seg_chunk0;
   a.seg_state = pl.split ? reinterpret_cast<float*>(ws + pl.off_state) : nullptr;
   a.seg_init = pl.split ? reinterpret_cast<float*>(ws + pl.off_init) : nullptr;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, (int)pl.seg_len,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, (int)pl.seg_first, (int)pl.seg_len,
                      (int)pl.seg_cap, (int)pl.chunk_cap, pp);
   if (int rc = gdn::check_launch("chunk plan")) return rc;
   if constexpr (PREP) {
@@ -1081,13 +1126,33 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
                 pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
   }
+  a.first_done = 0;
+  a.seg_base = 0;
+  a.seg_span = (int)pl.seg_span;
+  bool first_out = false;
   if (pl.split) {
-    launch_loop<E, DK, DV, kSummary>(a, pl, stream);
+    if constexpr (PREP && FINAL == kOut &&
+                  WsCfg<E, DK, DV, kOut>::NT == WsCfg<E, DK, DV, kSummary>::NT) {
+      if (pl.first_out) {
+        // first segments run the output mode here, from h0
+        const int64_t unit = 8 * (int64_t)(a.Hv / a.Hk);
+        const int64_t n = ((int64_t)a.seg_span * a.Hv + unit - 1) / unit * unit;
+        hipLaunchKernelGGL((chunk_ws_first_kernel<E, DK, DV>), dim3((unsigned)n),
+                           dim3(WsCfg<E, DK, DV, kOut>::NT), 0, stream, a);
+        first_out = true;
+      }
+    }
+    if (!first_out) launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;
     hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(DK * 2), 0, stream,
                        a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv);
     if (int rc = gdn::check_launch("chunk scan")) return rc;
+    a.first_done = first_out ? 1 : 0;
   }
+  // the output pass: segments out_base .. when the first segments are done,
+  // else every segment
+  a.seg_base = first_out ? (int)pl.out_base : 0;
+  a.seg_span = first_out ? (int)pl.seg_span : (int)pl.seg_cap;
   launch_loop<E, DK, DV, FINAL>(a, pl, stream);
   return gdn::check_launch("chunk loop");
 }

@@ -2,7 +2,8 @@
 //
 // From cu_seqlens one workgroup derives, for every sequence n (each chunked
 // in 64-token chunks from its own start):
-//   * its segments: runs of `seg_len` tokens handled by one workgroup each
+//   * its segments: a first run of `seg_first` tokens, then runs of `seg_len`
+//     tokens, each handled by one workgroup
 //     (table[s] = {n, token begin, token end, first/last flags}, seg_chunk0[s]
 //     = global index of the segment's first chunk);
 //   * seq_off[n] / seq_nseg[n]: its first segment and segment count;
@@ -52,8 +53,8 @@ __device__ __forceinline__ int block_excl_scan256(int v, int* buf, int* total) {
 }
 
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int N, int64_t T,
-                                                   int seg_len, int seg_cap, int chunk_cap,
-                                                   PlanPtrs pp) {
+                                                   int seg_first, int seg_len, int seg_cap,
+                                                   int chunk_cap, PlanPtrs pp) {
   __shared__ int buf[256];
   __shared__ int sc_off[257];     // chunk offsets of this block's sequences (block-local)
   __shared__ int sc_beg[256], sc_end[256];
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
       e = cu[n + 1];
       s = s < 0 ? 0 : (s > T ? T : s);
       e = e < s ? s : (e > T ? T : e);
-      ns = (int)((e - s + seg_len - 1) / seg_len);
+      ns = e - s <= seg_first ? (e > s ? 1 : 0) : 1 + (int)((e - s - seg_first + seg_len - 1) / seg_len);
       nc = (int)((e - s + 63) / 64);
     }
     int tot_s = 0, tot_c = 0;
@@ -79,11 +80,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
       pp.seq_nseg[n] = ns;
       pp.seq_chunk_off[n] = off_c;
       for (int p = 0; p < ns && off_s + p < seg_cap; p++) {
-        const int64_t a = s + (int64_t)p * seg_len;
-        const int64_t b = a + seg_len < e ? a + seg_len : e;
+        const int64_t a = p == 0 ? s : s + seg_first + (int64_t)(p - 1) * seg_len;
+        const int64_t len = p == 0 ? seg_first : seg_len;
+        const int64_t b = a + len < e ? a + len : e;
         pp.table[off_s + p] =
             make_int4(n, (int)a, (int)b, (p == 0 ? kFirst : 0) | (p == ns - 1 ? kLast : 0));
-        pp.seg_chunk0[off_s + p] = off_c + p * (seg_len / 64);
+        pp.seg_chunk0[off_s + p] = off_c + (p == 0 ? 0 : (seg_first + (p - 1) * seg_len) / 64);
       }
     }
     if (pp.chunk_tab) {
@@ -122,7 +124,11 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 
 // Host-side layout of the plan inside a workspace.
 struct Plan {
-  int64_t seg_len;
+  int64_t seg_first, seg_len;
+  bool first_out;  // a sequence's first segment runs the output mode in the summary pass
+  // segment indices a state-pass launch covers (its grid): seg_span of them
+  // from 0 (summary pass) or from out_base (output pass)
+  int64_t seg_span, out_base;
   int64_t seg_cap, chunk_cap;
   bool split;  // some sequence may have more than one segment
   size_t off_counts, off_table, off_seg_chunk0, off_seq_off, off_seq_nseg, off_seq_chunk_off,
@@ -141,30 +147,68 @@ struct Plan {
   }
 };
 
-// Segment length from the device size and the number of (sequence, head)
-// chains (GDN_SEG_CHUNKS overrides it for tuning).  rec_bytes: bytes of the
+// Segment lengths from the device size and the number of (sequence, head)
+// chains (GDN_SEG_CHUNKS overrides them for tuning).  rec_bytes: bytes of the
 // prepared record per (chunk, value head), 0 when the state pass takes none.
-inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes) {
+// first_out: the caller can run a sequence's first segment in the output mode
+// during the summary pass (from h0).
+//
+// A state-pass workgroup takes most of a CU's LDS, so one runs per CU.  Each
+// XCD hands its share of a grid (ids x mod 8 go to XCD x) to its CUs in a
+// fixed rotation, also the workgroups that exit at once: more than one
+// workgroup per CU in a grid can put two long-running ones on one CU.  For a
+// single sequence the grids therefore hold exactly CUs / Hv segment indices a
+// head.  With first_out the first segment is shorter (kFirstRatio of the
+// others, about the cost of a summary chunk against an output chunk): the
+// summary pass covers segments 0 .. B-1 (the first in the output mode), the
+// output pass segments 1 .. B, B = CUs / Hv.
+constexpr int kFirstRatioNum = 7, kFirstRatioDen = 10;
+inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes,
+                      bool first_out = false) {
   Plan p{};
   const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
-  int64_t per = 1;
+  int64_t per = 1, first = 1, span = 0;
   const char* env = getenv("GDN_SEG_CHUNKS");
+  p.first_out = false;
+  const int64_t C = (T + 63) / 64 + N - 1;
+  const int64_t cus = gdn::device_cu_count();
   if (env && atoi(env) > 0) {
-    per = atoi(env);
+    per = first = atoi(env);
+  } else if (N == 1) {
+    const int64_t B = cus / Hv > 1 ? cus / Hv : 1;
+    if (first_out && B > 1) {
+      per = (C * kFirstRatioDen + B * kFirstRatioDen + kFirstRatioNum - 1) /
+            (B * kFirstRatioDen + kFirstRatioNum);
+      if (per < 1) per = 1;
+      first = per * kFirstRatioNum / kFirstRatioDen;
+      if (first < 1) first = 1;
+      while (first + B * per < C) per++;
+      p.first_out = true;
+      span = B;
+    } else {
+      per = first = C > B ? (C + B - 1) / B : 1;
+      span = C > 0 ? (C + per - 1) / per : 1;
+    }
   } else {
-    // One workgroup per CU (the chunk loop holds most of a CU's LDS), and a
-    // few CUs may be held back from a queue: plan for 15/16 of them, so every
-    // segment of a pass is resident at once.  Segments per head: with N
-    // sequences of C chunks in all, at most ceil(C / per) + N - 1.
-    const int64_t slots = gdn::device_cu_count() * 15 / 16;
+    // several sequences: segments per head at most ceil(C / per) + N - 1
+    const int64_t slots = cus * 15 / 16;
     const int64_t budget = slots / Hv > 1 ? slots / Hv : 1;
-    const int64_t C = (T + 63) / 64 + N - 1;
     per = budget > N ? (C + (budget - N + 1) - 1) / (budget - N + 1) : C + 1;
     if (per < 1) per = 1;
+    first = per;
   }
+  p.seg_first = first * 64;
   p.seg_len = per * 64;
-  p.split = p.seg_len < T;
-  p.seg_cap = T / p.seg_len + N + 1;
+  p.split = p.seg_first < T;
+  p.first_out = p.first_out && p.split;
+  if (N == 1 && span > 0) {
+    p.seg_cap = p.first_out ? span + 1 : span;
+    p.seg_span = span;
+  } else {
+    p.seg_cap = T / p.seg_len + N + 2;
+    p.seg_span = p.seg_cap;
+  }
+  p.out_base = p.first_out ? 1 : 0;
   p.chunk_cap = chunks + 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {

@@ -120,3 +120,16 @@ def test_workspace_sizes_are_host_only(lib):
     big = lib.gdn_chunk_workspace_size(131072, 1, 16, 32, 128, 128, 1, 0)
     assert 0 < small < big
     assert lib.gdn_conv_bwd_workspace_size(0, 64, 4) == 0
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 300, 4097, 131072])
+@pytest.mark.parametrize("N", [1, 2])
+def test_workspace_size_edge_lengths(lib, T, N):
+    """The host plan (segment lengths, capacities) is total arithmetic for
+    empty, sub-chunk and long inputs, forward and backward, both dtypes."""
+    for dt, d in ((0, 32), (1, 128)):
+        for bwd in (0, 1):
+            size = lib.gdn_chunk_workspace_size(T, N, 2, 4, d, d, dt, bwd)
+            assert size >= 0
+            if T > 0:
+                assert size > 0

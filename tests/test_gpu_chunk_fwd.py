@@ -82,6 +82,20 @@ def test_segmented(seg, dtype):
     assert rel_err(f64(o1), f64(o2)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("length", [2000, 4097])
+def test_single_sequence_default_segments(length):
+    """One bfloat16 sequence at d = 128 under the default plan: its first
+    segment (shorter than the others) runs the output mode in the summary
+    pass from h0 and hands the scan [0 | S]; the rest must still equal the
+    oracle and the unsplit run."""
+    y, g, beta, h0, cu = _inputs(50 + length, [length], 2, 4, 128, 128, torch.bfloat16)
+    g = g * 0.05  # slow decay: the carried state matters across segments
+    o1, h1 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128)
+    o2, h2 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128, seg=100000)
+    assert rel_err(f64(o1), f64(o2)) <= TOL[torch.bfloat16]
+    assert rel_err(f64(h1), f64(h2)) <= TOL[torch.bfloat16]
+
+
 def test_no_l2norm_and_zero_state():
     y, g, beta, _, cu = _inputs(9, [150, 40], 2, 2, 64, 64, torch.float32, h0=False)
     y = y * 0.1  # unnormalised keys: keep |k| small so the recurrence stays contractive
