@@ -159,10 +159,10 @@ struct Plan {
 // workgroup per CU in a grid can put two long-running ones on one CU.  For a
 // single sequence the grids therefore hold exactly CUs / Hv segment indices a
 // head.  With first_out the first segment is shorter (kFirstRatio of the
-// others, about the cost of a summary chunk against an output chunk): the
+// others, the measured cost of a summary chunk against an output chunk): the
 // summary pass covers segments 0 .. B-1 (the first in the output mode), the
 // output pass segments 1 .. B, B = CUs / Hv.
-constexpr int kFirstRatioNum = 7, kFirstRatioDen = 10;
+constexpr int kFirstRatioNum = 77, kFirstRatioDen = 100;
 inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes,
                       bool first_out = false) {
   Plan p{};

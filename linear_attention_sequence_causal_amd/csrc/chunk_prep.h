@@ -61,7 +61,7 @@ __host__ __device__ constexpr int prep_tile0(int w) { return w == 0 ? 0 : w * (w
 constexpr int kPrepTiles = 11;
 
 // The raw rows are dead once the products are formed, so the per-head staging
-// shares their space (four workgroups fit a CU).
+// shares their space (six workgroups fit a CU).
 template <int DK>
 struct PrepSmem {
   static constexpr int LDK = DK + 8;
@@ -74,7 +74,7 @@ struct PrepSmem {
     Stage s;
   } u;
   alignas(16) float rk[64];
-  alignas(16) float wv[4][4][64];  // per wave: G, e^G, beta, e^G rk
+  alignas(16) float wv[4][2][64];  // per wave: G, beta
 };
 
 struct PrepArgs {
@@ -126,7 +126,7 @@ GDN_DEV floatx4 prep_invert16(const float* Lt, const float* bb, const floatx4& N
 // blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
 // the wave) and column block w of T.
 template <int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void chunk_prep_kernel(PrepArgs a) {
   typedef Mfma<bf16> M;
   typedef M::frag Fr;
   typedef Tile16<float> F;
@@ -203,9 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   float* Lt = tiles;                   // L_ww, then A_w
   float* wk = tiles + 16 * kPrepScLd;  // work tile, then E_w0
   float* G = sm.wv[w][0];
-  float* eG = sm.wv[w][1];
-  float* bt = sm.wv[w][2];
-  float* fk = sm.wv[w][3];
+  float* bt = sm.wv[w][1];
 
   for (int r = 0; r < GR; r++) {
     const int h = qa * GR + r;
@@ -225,9 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     const float egv = __expf(Gv);
     const float fkv = egv * sm.rk[lane];
     G[lane] = Gv;
-    eG[lane] = egv;
     bt[lane] = bv;
-    fk[lane] = fkv;
     if (w == 0) {
       float* F32 = reinterpret_cast<float*>(rec + kRecF);
       F32[lane] = sm.rk[lane] * __expf(GC - Gv);  // fd
