@@ -75,6 +75,11 @@ struct BwdArgs {
   const float* states;  // [chunk_cap][Hv][DK][DV]
   float* dstates;       // [chunk_cap][Hv][DK][DV]
   float* dqk;           // [T][Hv][2][DK]
+  // segments of the sequences (the forward plan's), for the dS pass
+  const int4* seg_table;
+  const int32_t* seg_chunk0;
+  float* seg_sum;       // [seg_cap][Hv][DK][DK+DV] reverse summaries [M | E]
+  float* seg_in;        // [seg_cap][Hv][DK][DV] dS leaving each non-last segment
 };
 
 template <typename E, int DK, int DV>
@@ -86,12 +91,31 @@ struct BwdCfg {
   typedef Prefetch<E, DK, DV, NT, true> PF;
 };
 
+// dS pass: 32 state columns a wave; the summary mode carries the extended
+// state [M | E] (DK + DV columns) in one workgroup, so the chunk's shared
+// work (gram, T, w) is formed once for both.
+template <typename E, int DK, int DV, bool SUM>
+struct DsCfg {
+  typedef E O;
+  static constexpr int NW = (SUM ? DK + DV : DV) / 32;
+  static constexpr int NT = NW * 64;
+  typedef Smem<O, DK, DV, true> SM;
+  typedef Prefetch<E, DK, DV, NT, true> PF;
+};
+
 // ---------------------------------------------------------------------------
-// 2. dS pass: reverse over the chunks of one sequence
+// 2. dS pass: reverse over the chunks of one segment
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs a) {
-  typedef BwdCfg<E, DK, DV> CF;
+// Per chunk, dS = (gamma_C I - W^T diag(D) K) dS' + Q^T (gamma o dO) - W^T P^T dO
+// is affine in dS', so the forward's segments serve here too: the summary
+// mode (SUM) runs a segment on the extended state [I | 0] (no dO for the
+// identity columns) from its end back to its start, giving dS_in = M dS_out +
+// E for every segment but a sequence's first; a reverse scan folds them from
+// dht; the final mode runs every segment from its own dS_out, stores dS' of
+// each chunk and writes dh0 in the first segment.
+template <typename E, int DK, int DV, bool SUM>
+__global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(BwdArgs a) {
+  typedef DsCfg<E, DK, DV, SUM> CF;
   typedef typename CF::O O;
   typedef Mfma<O> M;
   typedef typename CF::SM SM;
@@ -99,27 +123,40 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
   constexpr int NSK = DK / KS, NSB = BT / KS, DKT = DK / 16;
   __shared__ SM sm;  // sm.v holds the chunk of dO
 
-  const int n = blockIdx.x, h = blockIdx.y;
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= a.counts[0]) return;
+  const int4 ent = a.seg_table[seg];
+  if (SUM && (ent.w & kFirst)) return;
+  const int n = ent.x;
   const int Hv = a.Hv, qa = h / (Hv / a.Hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c0 = wave * 32;
-  int64_t s0 = a.cu[n], e0 = a.cu[n + 1];
-  s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
-  e0 = e0 < s0 ? s0 : (e0 > a.T ? a.T : e0);
+  const int c0 = wave * 32;                 // first (extended) state column
+  const bool mcol = SUM && c0 < DK;         // columns of M: no dO
+  const int vc0 = SUM ? c0 - DK : c0;       // value column of the first column
+  const int64_t s0 = ent.y, e0 = ent.z;
   const int nch = (int)((e0 - s0 + BT - 1) / BT);
-  const int chunk0 = a.seq_chunk_off[n];
+  const int chunk0 = a.seg_chunk0[seg];
 
   zero_upper<O, true, NT>(sm, tid);
   floatx4 dS[DKT][2];
   {
-    const float* src = a.dht ? a.dht + ((int64_t)n * Hv + h) * DK * DV : nullptr;
+    const float* src = nullptr;
+    if (!SUM) {
+      if (!(ent.w & kLast)) src = a.seg_in + ((int64_t)seg * Hv + h) * DK * DV;
+      else if (a.dht) src = a.dht + ((int64_t)n * Hv + h) * DK * DV;
+    }
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
       for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          dS[mt][nt][j] = src ? src[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] : 0.f;
+        for (int j = 0; j < 4; j++) {
+          const int row = 16 * mt + 4 * (lane >> 4) + j, col = c0 + 16 * nt + (lane & 15);
+          float v = 0.f;
+          if (mcol) v = row == col ? 1.f : 0.f;
+          else if (src) v = src[row * DV + col];
+          dS[mt][nt][j] = v;
+        }
   }
   const E* qp = (const E*)a.q + (int64_t)qa * DK;
   const E* kp = (const E*)a.k + (int64_t)qa * DK;
@@ -134,7 +171,7 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
     __syncthreads();
     stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
     if (c > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, tc - BT, e0, tid);
-    {  // dS' of this chunk for the gradient kernel
+    if (!SUM) {  // dS' of this chunk for the gradient kernel
       float* dst = a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++)
@@ -170,9 +207,13 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
       }
 #pragma unroll
       for (int s = 0; s < NSB; s++) {
+        // the identity columns see no dO: their operand is zero (a select,
+        // not a branch, keeps both modes' registers alike)
         const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
-        M::mma(p0, pt, M::load_col(sm.v, SM::LDV, c0, s * KS, lane));
-        M::mma(p1, pt, M::load_col(sm.v, SM::LDV, c0 + 16, s * KS, lane));
+        const typename M::frag v0 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 0 : vc0, s * KS, lane);
+        const typename M::frag v1 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 16 : vc0 + 16, s * KS, lane);
+        M::mma(p0, pt, mcol ? typename M::frag{} : v0);
+        M::mma(p1, pt, mcol ? typename M::frag{} : v1);
       }
       const int rb = 16 * mt + 4 * (lane >> 4);
 #pragma unroll
@@ -192,7 +233,9 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
 #pragma unroll
       for (int nt = 0; nt < 2; nt++) {
         db[s][nt] = acc_as_b<O>(dvn, s, nt);
-        gb[s][nt] = M::load_col_scaled(sm.v, SM::LDV, c0 + 16 * nt, s * KS, sm.eg, lane);
+        const typename M::frag gv =
+            M::load_col_scaled(sm.v, SM::LDV, (vc0 < 0 ? 0 : vc0) + 16 * nt, s * KS, sm.eg, lane);
+        gb[s][nt] = mcol ? typename M::frag{} : gv;
       }
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++) {
@@ -200,9 +243,9 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
 #pragma unroll
       for (int s = 0; s < NSB; s++) {
         const typename M::frag qt = M::load_col(sm.q, SM::LDK, 16 * mt, s * KS, lane);
-        const typename M::frag wt = M::load_col(sm.w, SM::LDK, 16 * mt, s * KS, lane);
         M::mma(acc0, qt, gb[s][0]);
         M::mma(acc1, qt, gb[s][1]);
+        const typename M::frag wt = M::load_col(sm.w, SM::LDK, 16 * mt, s * KS, lane);
         M::mma(acc0, wt, db[s][0]);
         M::mma(acc1, wt, db[s][1]);
       }
@@ -210,15 +253,23 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void dstate_kernel(BwdArgs
       dS[mt][1] = acc1;
     }
   }
-  if (a.dh0) {
-    float* dst = a.dh0 + ((int64_t)n * Hv + h) * DK * DV;
+  // the summary [M | E] of the segment, or dh0 from a sequence's first segment
+  float* dst = nullptr;
+  int ld = DV;
+  if (SUM) {
+    dst = a.seg_sum + ((int64_t)seg * Hv + h) * DK * (DK + DV);
+    ld = DK + DV;
+  } else if ((ent.w & kFirst) && a.dh0) {
+    dst = a.dh0 + ((int64_t)n * Hv + h) * DK * DV;
+  }
+  if (dst) {
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
       for (int nt = 0; nt < 2; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
+          dst[(16 * mt + 4 * (lane >> 4) + j) * ld + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
   }
 }
 
@@ -722,8 +773,29 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
   LoopArgs la = la_in;
   la.states = reinterpret_cast<float*>(ws + L.off_states);
   if (int rc = run_pipeline<E, DK, DV, kStates>(la, b.cu, N, T, L.plan, ws, true, stream)) return rc;
-  hipLaunchKernelGGL((dstate_kernel<E, DK, DV>), dim3(N, b.Hv), dim3(CF::NT), 0, stream, b);
+  // dS pass over the forward's segments (its summary and initial-state buffers
+  // are free again): reverse summaries, reverse scan from dht, final pass
+  b.seg_table = pp.table;
+  b.seg_chunk0 = pp.seg_chunk0;
+  b.seg_sum = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_state) : nullptr;
+  b.seg_in = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_init) : nullptr;
+  const dim3 sgrid((unsigned)L.plan.seg_cap, b.Hv);
+  if (L.plan.split) {
+    hipLaunchKernelGGL((dstate_kernel<E, DK, DV, true>), sgrid, dim3(DsCfg<E, DK, DV, true>::NT), 0,
+                       stream, b);
+    if (int rc = gdn::check_launch("gdn_chunk_bwd(dS summaries)")) return rc;
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, true>), dim3(N, b.Hv, DV / 16), dim3(DK * 2), 0,
+                       stream, b.seg_sum, b.seg_in, b.dht, pp.seq_off, pp.seq_nseg, b.Hv);
+    if (int rc = gdn::check_launch("gdn_chunk_bwd(dS scan)")) return rc;
+  }
+  hipLaunchKernelGGL((dstate_kernel<E, DK, DV, false>), sgrid, dim3(DsCfg<E, DK, DV, false>::NT), 0,
+                     stream, b);
   if (int rc = gdn::check_launch("gdn_chunk_bwd(dstate)")) return rc;
+  if (b.dh0) {  // empty sequences: dh0 = dht (or zero)
+    hipLaunchKernelGGL(empty_seq_state_kernel, dim3(N, b.Hv), dim3(256), 0, stream, b.cu, b.dht,
+                       b.dh0, b.Hv, DK * DV);
+    if (int rc = gdn::check_launch("gdn_chunk_bwd(empty sequences)")) return rc;
+  }
   hipLaunchKernelGGL((grad_kernel<E, DK, DV>), dim3((unsigned)L.plan.chunk_cap, b.Hv), dim3(CF::NT),
                      0, stream, b);
   if (int rc = gdn::check_launch("gdn_chunk_bwd(grad)")) return rc;

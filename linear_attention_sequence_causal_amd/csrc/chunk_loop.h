@@ -1012,8 +1012,11 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) void chunk_ws_first_k
 // Scan over segment summaries (fp32): per (sequence, head, 16 columns),
 // h <- M h + E over the segments of the sequence, with fp32 MFMA products
 // (wave w owns rows 32 w .. 32 w + 31 of h; M's rows are the A operands,
-// read straight from the summaries, h the B operand from LDS).
-template <int DK, int DV>
+// read straight from the summaries, h the B operand from LDS).  Forward:
+// from h0 over segments 0 .. nseg - 2, giving the initial states of 1 ..
+// nseg - 1.  REV (the backward's dS): from dht over segments nseg - 1 .. 1,
+// giving the state gradient leaving segments nseg - 2 .. 0.
+template <int DK, int DV, bool REV = false>
 __global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restrict__ seg_state,
                                                           float* __restrict__ seg_init,
                                                           const float* __restrict__ h0,
@@ -1035,7 +1038,9 @@ __global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restric
     hs[r][col] = h0 ? h0[(((int64_t)n * Hv + h) * DK + r) * DV + cb + col] : 0.f;
   }
   __syncthreads();
-  for (int p = 0; p + 1 < nseg; p++) {
+  for (int i = 0; i + 1 < nseg; i++) {
+    const int p = REV ? nseg - 1 - i : i;  // the summary applied
+    const int q = REV ? p - 1 : p + 1;     // the segment whose state it gives
     const float* X = seg_state + ((int64_t)(off + p) * Hv + h) * DK * LDX;
     floatx4 acc[2];
     floatx4 af[2][NKT];
@@ -1054,7 +1059,7 @@ __global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restric
       for (int i = 0; i < 2; i++) M::mma(acc[i], af[i][kt], bf);
     }
     __syncthreads();  // every wave has read h
-    float* dst = seg_init + ((int64_t)(off + p + 1) * Hv + h) * DK * DV;
+    float* dst = seg_init + ((int64_t)(off + q) * Hv + h) * DK * DV;
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
