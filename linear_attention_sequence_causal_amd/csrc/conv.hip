@@ -188,7 +188,9 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 // A thread's run covers tokens [t0, t0+R).  It recomputes z and dz for
 // [t0, t0+R+K-1) (the K-1 extra rows feed dx of its last tokens), writes dx
 // for its own tokens, the halo gradient when the run holds the start of
-// sequence 0, and accumulates dw/dbias over its own tokens.  A block loops
+// sequence 0, and accumulates dw/dbias over its own tokens.  The rows stream
+// through windows of the last K x rows, dz rows and sequence ends: dx of
+// token t - (K-1) is formed once dz[t] is known.  A block loops
 // over token tiles with a fixed grid stride; its four runs' sums are added in
 // LDS and written as one partial row, and a second kernel adds the partial
 // rows in a fixed order (deterministic dw).
@@ -199,8 +201,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
     const gdn_cp_meta* __restrict__ meta, const E* __restrict__ dy, E* __restrict__ dx,
     E* __restrict__ dhalo, float* __restrict__ part_w, float* __restrict__ part_b) {
   constexpr int R = kBwdRows;
-  constexpr int XR = R + 2 * (K - 1);  // x rows t0-(K-1) .. t0+R+K-2
-  constexpr int DR = R + K - 1;        // dz rows t0 .. t0+R+K-2
+  constexpr int DR = R + K - 1;  // dz rows t0 .. t0+R+K-2
   __shared__ float red[kLanes][V * (K + 1)];
   const int c0 = (blockIdx.y * kLanes + threadIdx.x) * V;
   const bool active = c0 < C;
@@ -226,40 +227,52 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
   for (int64_t tile = blockIdx.x; active && tile * tile_tokens < T; tile += gridDim.x) {
     const int64_t t0 = tile * tile_tokens + (int64_t)threadIdx.y * R;
     if (t0 >= T) continue;
-    Row<E, V> xr[XR];
-    Row<E, V> gr[DR];
-#pragma unroll
-    for (int i = 0; i < XR; i++) {
-      const int64_t tau = t0 - (K - 1) + i;
-      xr[i] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
-    }
-#pragma unroll
-    for (int i = 0; i < DR; i++) {
-      const int64_t t = t0 + i;
-      gr[i] = (t < T) ? load_row<E, V>(dy + t * C + c0) : zero_row<E, V>();
-    }
     const bool use_halo = n_halo > 0 && t0 - (K - 1) < cu0;
     Row<E, V> hr[K > 1 ? K - 1 : 1];
 #pragma unroll
     for (int i = 0; i < K - 1; i++)
       hr[i] = use_halo ? load_row<E, V>(halo + (int64_t)i * C + c0) : zero_row<E, V>();
+    // windows: xw[j] = x row t-(K-1)+j, dzw[j] = dz row t-(K-1)+j and ew[j]
+    // = the end of that row's sequence, at the current step t
+    Row<E, V> xw[K];
+    float dzw[K][V];
+    int64_t ew[K];
+#pragma unroll
+    for (int j = 0; j < K; j++) {
+      ew[j] = 0;
+#pragma unroll
+      for (int i = 0; i < V; i++) dzw[j][i] = 0.f;
+    }
+    xw[0] = zero_row<E, V>();
+#pragma unroll
+    for (int i = 0; i < K - 1; i++) {
+      const int64_t tau = t0 - (K - 1) + i;
+      xw[i + 1] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
+    }
 
     int n = find_seq(cu, N, t0);
     int64_t s = cu[n], e = cu[n + 1];
     const int n_first = n;
     const int64_t e_first = e, s_first = s;
-    float dz[DR][V];
-    int64_t seq_end[R];
 #pragma unroll
     for (int r = 0; r < DR; r++) {
       const int64_t t = t0 + r;
+#pragma unroll
+      for (int j = 0; j + 1 < K; j++) {
+        xw[j] = xw[j + 1];
+        ew[j] = ew[j + 1];
+#pragma unroll
+        for (int i = 0; i < V; i++) dzw[j][i] = dzw[j + 1][i];
+      }
+      xw[K - 1] = t < T ? load_row<E, V>(x + t * C + c0) : zero_row<E, V>();
+      const Row<E, V> gr = t < T ? load_row<E, V>(dy + t * C + c0) : zero_row<E, V>();
       if (t < T) {
         while (t >= e) {
           n++;
           s = cu[n];
           e = cu[n + 1];
         }
-        if (r < R) seq_end[r] = e;
+        ew[K - 1] = e;
         float xt[K][V];  // the taps x~[t-(K-1)+j]
 #pragma unroll
         for (int j = 0; j < K; j++) {
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
           for (int i = 0; i < V; i++) xt[j][i] = 0.f;
           if (tau >= s) {
 #pragma unroll
-            for (int i = 0; i < V; i++) xt[j][i] = xr[r + j].at(i);
+            for (int i = 0; i < V; i++) xt[j][i] = xw[j].at(i);
           } else if (n == 0 && s - tau <= n_halo) {
             const int hrow = (int)(K - 1 - (s - tau));
 #pragma unroll
@@ -285,8 +298,8 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
 #pragma unroll
           for (int j = 0; j < K; j++) z += wv[j][i] * xt[j][i];
           const float sg = fast_sigmoid(z);
-          const float d = gr[r].at(i) * sg * (1.f + z * (1.f - sg));
-          dz[r][i] = d;
+          const float d = gr.at(i) * sg * (1.f + z * (1.f - sg));
+          dzw[K - 1][i] = d;
           if (r < R) {
             dbacc[i] += d;
 #pragma unroll
@@ -295,50 +308,50 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < V; i++) dz[r][i] = 0.f;
-        if (r < R) seq_end[r] = t;
+        for (int i = 0; i < V; i++) dzw[K - 1][i] = 0.f;
+        ew[K - 1] = t;
       }
-    }
-    // dx[t] = sum_j w[j] dz[t+K-1-j] over taps inside t's sequence
+      // dx[tp] = sum_j w[j] dz[tp+K-1-j] (= dzw[K-1-j]) over taps inside tp's
+      // sequence (whose end is ew[0]), tp = t - (K-1)
+      const int rp = r - (K - 1);
+      if (rp >= 0 && rp < R) {
+        const int64_t tp = t0 + rp;
+        if (tp < T) {
+          float out[V];
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int64_t t = t0 + r;
-      if (t < T) {
-        float out[V];
-#pragma unroll
-        for (int i = 0; i < V; i++) out[i] = 0.f;
-#pragma unroll
-        for (int j = 0; j < K; j++) {
-          const int rr = r + K - 1 - j;
-          if (t0 + rr < seq_end[r]) {
-#pragma unroll
-            for (int i = 0; i < V; i++) out[i] += wv[j][i] * dz[rr][i];
-          }
-        }
-        store_row<E, V>(dx + t * C + c0, out);
-      }
-    }
-    // halo rows (tokens s0 - i, i = 1..K-1, before local sequence 0): the
-    // run starting at cu[0] writes all of them; rows beyond n_halo, or all
-    // rows when sequence 0 is empty, get zero
-    if (dhalo && t0 == cu0) {
-      const bool seq0 = (n_first == 0) && (s_first == t0);
-#pragma unroll
-      for (int i = 1; i < K; i++) {
-        float out[V];
-#pragma unroll
-        for (int v = 0; v < V; v++) out[v] = 0.f;
-        if (seq0 && i <= n_halo) {
+          for (int i = 0; i < V; i++) out[i] = 0.f;
 #pragma unroll
           for (int j = 0; j < K; j++) {
-            const int rr = K - 1 - i - j;  // dz row of token s0 - i + K-1-j
-            if (rr >= 0 && t0 + rr < e_first) {
+            if (t - j < ew[0]) {
 #pragma unroll
-              for (int v = 0; v < V; v++) out[v] += wv[j][v] * dz[rr][v];
+              for (int i = 0; i < V; i++) out[i] += wv[j][i] * dzw[K - 1 - j][i];
             }
           }
+          store_row<E, V>(dx + tp * C + c0, out);
         }
-        store_row<E, V>(dhalo + (int64_t)(K - 1 - i) * C + c0, out);
+      }
+      // halo rows (tokens s0 - i, i = 1..K-1, before local sequence 0) once
+      // dz of rows 0 .. K-2 is known: the run starting at cu[0] writes all of
+      // them; rows beyond n_halo, or all rows when sequence 0 is empty, get 0
+      if (K > 1 && r == K - 2 && dhalo && t0 == cu0) {
+        const bool seq0 = (n_first == 0) && (s_first == t0);
+#pragma unroll
+        for (int i = 1; i < K; i++) {
+          float out[V];
+#pragma unroll
+          for (int v = 0; v < V; v++) out[v] = 0.f;
+          if (seq0 && i <= n_halo) {
+#pragma unroll
+            for (int j = 0; j < K; j++) {
+              const int rr = K - 1 - i - j;  // dz row of token s0 - i + K-1-j
+              if (rr >= 0 && t0 + rr < e_first) {
+#pragma unroll
+                for (int v = 0; v < V; v++) out[v] += wv[j][v] * dzw[rr + 1][v];
+              }
+            }
+          }
+          store_row<E, V>(dhalo + (int64_t)(K - 1 - i) * C + c0, out);
+        }
       }
     }
   }
