@@ -213,13 +213,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void c
       gn = a.g[tg * a.Hv + h + 1];
       bn = a.beta[tg * a.Hv + h + 1];
     }
-    float Gv = gv;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(Gv, off, 64);
-      if (lane >= off) Gv += o;
-    }
-    const float GC = __shfl(Gv, 63, 64);
+    const float Gv = wave_incl_scan(gv);  // in-chunk cumsum of g
+    const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gv), 63));
     const float egv = __expf(Gv);
     const float fkv = egv * sm.rk[lane];
     G[lane] = Gv;

@@ -315,6 +315,23 @@ template <int W> GDN_DEV float row_group_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves: shifts
+// by 1, 2, 4, 8 within each row of 16 lanes (lanes without a source add 0),
+// then lane 15 of each row added to the next row and lane 31 to rows 2 and 3.
+template <int CTRL, int ROWS, bool BOUND>
+GDN_DEV float dpp_upd(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, BOUND));
+}
+GDN_DEV float wave_incl_scan(float v) {
+  v += dpp_upd<0x111, 0xF, true>(v);  // row_shr:1
+  v += dpp_upd<0x112, 0xF, true>(v);  // row_shr:2
+  v += dpp_upd<0x114, 0xF, true>(v);  // row_shr:4
+  v += dpp_upd<0x118, 0xF, true>(v);  // row_shr:8
+  v += dpp_upd<0x142, 0xA, false>(v); // row_bcast:15 into rows 1, 3
+  v += dpp_upd<0x143, 0xC, false>(v); // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Sum of squares of a 16-byte activation vector (bf16: pairwise dot
 // products accumulated in fp32).
 GDN_DEV float sum_sq(const floatx4& v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
