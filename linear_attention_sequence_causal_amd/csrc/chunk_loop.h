@@ -607,9 +607,9 @@ struct WsLoad {
   }
 };
 
-// Hand-off among the consumer waves through an LDS counter, without a
-// workgroup barrier: each wave adds one when its part is stored (arrive) and
-// waits until `target` (NC a chunk so far) is reached.  Every consumer wave
+// Hand-off among the loader waves through an LDS counter, without a
+// workgroup barrier: each wave adds one when its rows are stored (arrive) and
+// waits until `target` (NL a chunk so far) is reached.  Every loader wave
 // runs the same iterations, so the wait ends.
 GDN_DEV void count_arrive(unsigned* count, int lane) {
   wave_lds_sync();  // this wave's stores are done
@@ -683,6 +683,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
   typedef Mfma<O> M;
   typedef typename M::frag Fr;
   constexpr int NC = CF::NC;
+  constexpr int NL = CF::NL;
   constexpr int CW = CF::CW;
   constexpr int NN = CW / 16;   // 16-column tiles per consumer wave
   constexpr int KS = M::KSTEP;  // 32
@@ -717,12 +718,32 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     for (int it = -1; it < nchunks; it++) {
       const int pc = it + 1;
       if (pc < nchunks) {
-        ld.store(buf[pc & 1], ltid, a.scale, a.use_l2norm);
+        SM& B = buf[pc & 1];
+        ld.store(B, ltid, a.scale, a.use_l2norm);
         if (pc + 1 < nchunks)
           ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (chunk0 + pc + 1) * rstride,
                   tb + (int64_t)(pc + 1) * BT, te, ltid);
+        if constexpr (OUT) {
+          // P and fo of the chunk just stored, made here while the consumers
+          // run the previous chunk: once every loader wave's rows are in
+          // place (LDS counter among the loader waves), each makes its
+          // three halves of P (all products issued before any is finished)
+          const int lw = wave - NC;
+          count_arrive(&p_count, lane);
+          count_wait(&p_count, (unsigned)NL * (unsigned)(pc + 1));
+          constexpr int NR = kPHalves / NL;
+          PHalf<DK> ph[NR];
+#pragma unroll
+          for (int r = 0; r < NR; r++) {
+            const int u = lw + r * NL;
+            ph[r].begin(B, u, lane, p_half_s(u) * 2 + p_half_h(u) <= p_half_mt(u));
+          }
+#pragma unroll
+          for (int r = 0; r < NR; r++) ph[r].finish(B, lane);
+          if (lw == 0) B.fo[lane] = __expf(reinterpret_cast<const float*>(B.rec + kRecG)[lane]) * B.rq[lane];
+        }
       }
-      lds_barrier();
+      lds_barrier();  // the chunk (with P and fo) is published
     }
     return;
   }
@@ -758,24 +779,6 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     if (it >= 0) {
       SM& C = buf[it & 1];
       const char* R = C.rec;
-      if constexpr (OUT) {
-        // this wave's share of the chunk's P fragments (halves wave,
-        // wave + NC, ...: every product issued before any is finished) and
-        // fo (wave 0); the other waves' shares are awaited before the o
-        // products
-        constexpr int NR = (kPHalves + NC - 1) / NC;
-        PHalf<DK> ph[NR];
-#pragma unroll
-        for (int r = 0; r < NR; r++) {
-          const int u = wave + r * NC;
-          if (u < kPHalves) ph[r].begin(C, u, lane, p_half_s(u) * 2 + p_half_h(u) <= p_half_mt(u));
-        }
-#pragma unroll
-        for (int r = 0; r < NR; r++)
-          if (wave + r * NC < kPHalves) ph[r].finish(C, lane);
-        if (wave == 0) C.fo[lane] = __expf(reinterpret_cast<const float*>(R + kRecG)[lane]) * C.rq[lane];
-        count_arrive(&p_count, lane);
-      }
       if constexpr (MODE == kStates) {
         // the state entering this chunk, for the backward
         float* dst = a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
@@ -853,7 +856,6 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
           }
       }
       if constexpr (OUT) {
-        count_wait(&p_count, (unsigned)NC * (unsigned)(it + 1));  // every part of P is in place
         // o^T = fo o (S^T q^T) + x^T P^T.  Tile o[mt][nt] holds value columns
         // c0 + 16 nt + 4(lane/16) + j of token 16 mt + lane%16, so fo is one
         // factor per lane, x fragments are the A operands and the P fragments
@@ -964,7 +966,7 @@ template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
   typedef typename WsCfg<E, DK, DV, MODE>::SM SM;
   __shared__ SM buf[2];
-  __shared__ unsigned p_count;  // consumer waves' P parts, a running count
+  __shared__ unsigned p_count;  // loader waves' stored chunks, a running count (P hand-off)
   if (MODE == kOut) {
     if (threadIdx.x == 0) p_count = 0u;
     __syncthreads();
