@@ -296,7 +296,7 @@ enum { kRB = 0, kRYKS = 1, kRDOQS = 2, kRKDSVN = 3 };
 enum { kRowP = 0, kColP = 1, kRowKK = 2, kRowL = 3, kColL = 4 };
 
 // sum over the 16 lanes of each lane group (one C-tile row)
-GDN_DEV float row16_sum(float v) { return group_sum<16>(v); }
+GDN_DEV float row16_sum(float v) { return row_group_sum<16>(v); }
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a) {
@@ -404,10 +404,12 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     ks[mt][1] = k1;
     kds[mt][0] = d0;
     kds[mt][1] = d1;
+    {
+      // dO tiles (mt, this wave's columns) in C layout
+      const floatx4 o0 = lds_tile_c(gs.dO, LDV, 16 * mt, c0, lane);
+      const floatx4 o1 = lds_tile_c(gs.dO, LDV, 16 * mt, c0 + 16, lane);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int row = 16 * mt + 4 * g4 + j;
-      r_doqs[mt][j] = to_f(gs.dO[row * LDV + c0 + ln]) * q0[j] + to_f(gs.dO[row * LDV + c0 + 16 + ln]) * q1[j];
+      for (int j = 0; j < 4; j++) r_doqs[mt][j] = o0[j] * q0[j] + o1[j] * q1[j];
     }
   }
   // dVn = P^T dO + D o K dS'
@@ -448,11 +450,13 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     }
     y[mt][0] = y0;
     y[mt][1] = y1;
+    const floatx4 v0 = lds_tile_c(sm.v, LDV, 16 * mt, c0, lane);
+    const floatx4 v1 = lds_tile_c(sm.v, LDV, 16 * mt, c0 + 16, lane);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int row = 16 * mt + 4 * g4 + j;
       const float bt = sm.beta[row];
-      r_b[mt][j] = y0[j] * to_f(sm.v[row * LDV + c0 + ln]) + y1[j] * to_f(sm.v[row * LDV + c0 + 16 + ln]);
+      r_b[mt][j] = y0[j] * v0[j] + y1[j] * v1[j];
       r_yks[mt][j] = y0[j] * ks[mt][0][j] + y1[j] * ks[mt][1][j];
       const int64_t t = tc + row;
       if (t < te) {

@@ -59,6 +59,24 @@ template <typename E> GDN_DEV typename Vec16<E>::type zero_vec16() {
 // ---------------------------------------------------------------------------
 // MFMA policy: operand type O of the contractions.
 // ---------------------------------------------------------------------------
+// Transposed LDS read (ds_read_b64_tr_b16): from a row-major [rows][ld] bf16
+// array, lane l (group g = l/16, index i = l%16) receives the four elements
+// of column c0 + i in rows r0 + 4g + j, j = 0..3 -- a C-layout tile, or
+// half of an A fragment whose contraction index runs down the rows.  Within
+// each 16-lane group the instruction returns to lane i element i%4 of the
+// 8-byte vector read by lane 4j + i/4, so lane i points at row r0 + 4g +
+// i/4, columns c0 + 4(i%4) .. +3.  Addresses must be 8-byte aligned.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+// With cs = 8 the four column blocks are c0, c0 + 8, c0 + 16, c0 + 24, and lane
+// i receives column c0 + 8(i/4) + i%4 (the permuted dk order of the state).
+GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane, int cs = 4) {
+  const int i = lane & 15, g = lane >> 4;
+  const bf16* p = base + ((4 * g + (i >> 2)) * ld + cs * (i & 3)) + (r0 * ld + c0);
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 template <typename O> struct Mfma;
 
 template <> struct Mfma<bf16> {
@@ -116,17 +134,13 @@ template <> struct Mfma<bf16> {
     }
     return f;
   }
-  // column access: element (k, c0 + l%16) of a [K][ld] array, k in the
-  // convention's order -- an operand whose contraction index runs down rows
+  // column access: element (k, c0 + l%16) of a [K][ld] array in LDS, k in
+  // the convention's order -- an operand whose contraction index runs down
+  // rows; two transposing reads (ld and c0 multiples of 4 elements)
   GDN_DEV static frag load_col(const bf16* base, int ld, int c0, int k0, int lane) {
-    const bf16* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
-    frag f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      f[j] = p[j * ld];
-      f[4 + j] = p[(16 + j) * ld];
-    }
-    return f;
+    const bf16x4 lo = lds_rows4_tr(base, ld, k0, c0, lane);
+    const bf16x4 hi = lds_rows4_tr(base, ld, k0 + 16, c0, lane);
+    return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   GDN_DEV static frag load_col_f32(const float* base, int ld, int c0, int k0, const float* sc,
                                    int lane) {
@@ -140,16 +154,17 @@ template <> struct Mfma<bf16> {
     }
     return f;
   }
-  // column access with element k scaled by sc[k]
+  // column access (LDS, as load_col) with element k scaled by sc[k]
   GDN_DEV static frag load_col_scaled(const bf16* base, int ld, int c0, int k0, const float* sc,
                                       int lane) {
     const int kk = k0 + 4 * (lane >> 4);
-    const bf16* p = base + (4 * (lane >> 4) * ld + (lane & 15)) + (k0 * ld + c0);
+    const bf16x4 lo = lds_rows4_tr(base, ld, k0, c0, lane);
+    const bf16x4 hi = lds_rows4_tr(base, ld, k0 + 16, c0, lane);
     frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      f[j] = (bf16)((float)p[j * ld] * sc[kk + j]);
-      f[4 + j] = (bf16)((float)p[(16 + j) * ld] * sc[kk + 16 + j]);
+      f[j] = (bf16)((float)lo[j] * sc[kk + j]);
+      f[4 + j] = (bf16)((float)hi[j] * sc[kk + 16 + j]);
     }
     return f;
   }
@@ -249,22 +264,16 @@ template <> struct Tile16<float> {
   GDN_DEV static void mma(floatx4& acc, const frag& a, const frag& b) { Mfma<float>::mma(acc, a, b); }
 };
 
-// Transposed LDS read (ds_read_b64_tr_b16): from a row-major [rows][ld] bf16
-// array, lane l (group g = l/16, index i = l%16) receives the four elements
-// of column c0 + i in rows r0 + 4g + j, j = 0..3 -- a C-layout tile, or
-// half of an A fragment whose contraction index runs down the rows.  Within
-// each 16-lane group the instruction returns to lane i element i%4 of the
-// 8-byte vector read by lane 4j + i/4, so lane i points at row r0 + 4g +
-// i/4, columns c0 + 4(i%4) .. +3.  Addresses must be 8-byte aligned.
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-// With cs = 8 the four column blocks are c0, c0 + 8, c0 + 16, c0 + 24, and lane
-// i receives column c0 + 8(i/4) + i%4 (the permuted dk order of the state).
-GDN_DEV bf16x4 lds_rows4_tr(const bf16* base, int ld, int r0, int c0, int lane, int cs = 4) {
-  const int i = lane & 15, g = lane >> 4;
-  const bf16* p = base + ((4 * g + (i >> 2)) * ld + cs * (i & 3)) + (r0 * ld + c0);
-  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+// The C-layout 16x16 tile at (r0, c0) of a row-major [rows][ld] LDS array,
+// as fp32: lane l receives rows r0 + 4(l/16) + j (j = 0..3) of column
+// c0 + l%16 (bf16: one transposing read, ld and c0 multiples of 4).
+GDN_DEV floatx4 lds_tile_c(const bf16* base, int ld, int r0, int c0, int lane) {
+  const bf16x4 v = lds_rows4_tr(base, ld, r0, c0, lane);
+  return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+GDN_DEV floatx4 lds_tile_c(const float* base, int ld, int r0, int c0, int lane) {
+  const float* p = base + (r0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+  return floatx4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
 // lds_rows4_tr with cs = 8 from an array stored like load_k8_x's (16-byte
