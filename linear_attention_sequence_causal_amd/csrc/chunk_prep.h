@@ -194,10 +194,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void c
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
   __syncthreads();  // every wave's products are formed: the rows' space is reused
-  // blocks above the diagonal that the fragments include stay zero
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e / 64, c = e % 64;
-    if ((c >> 4) > (r >> 4)) sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
+  // the two blocks above the diagonal that the fragments include, (0, 1) and
+  // (2, 3), stay zero: 2 x 256 elements, two a thread
+  {
+    const int blk = tid >> 7, e = (tid & 127) * 2;  // block 0: rows 0-15, block 1: rows 32-47
+    const int r = 32 * blk + (e >> 4), c = 16 + 32 * blk + (e & 15);
+    sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
+    sm.u.s.st[r * kPrepLd + c + 1] = (bf16)0.f;
   }
   float* const tiles = sm.u.s.sc[prep_tile0(w)];
   float* Lt = tiles;                   // L_ww, then A_w
