@@ -537,8 +537,28 @@ struct WsCfg {
   static constexpr bool FITS = 2 * sizeof(SM) <= 160 * 1024;
 };
 
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0): loads at
+// offsets past the end return zero, so rows past a sequence end need no
+// predicate and nothing outside the range is ever read.
+GDN_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename V>
+GDN_DEV V buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// 8-byte store; past the end of the range it is dropped
+template <typename V>
+GDN_DEV void buffer_store8(const V& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+}
+
 // Loader registers: one chunk's rows and the first RECB bytes of its record,
-// 16-byte vectors.
+// 16-byte vectors.  The loads go through buffer resources
+// based at the chunk's first row, so a thread's byte offsets are the same for
+// every chunk (made once by `offsets`) and the per-chunk address work is
+// scalar.
 template <typename E, int DK, int DV, bool HAS_Q, int RECB>
 struct WsLoad {
   typedef typename Vec16<E>::type V16;
@@ -553,29 +573,38 @@ struct WsLoad {
   V16 q[HAS_Q ? PQ : 1], k[PQ], v[PV];
   floatx4 r[PR];
 
+  // this thread's byte offsets within a chunk (row tid / QPR, piece tid % QPR,
+  // then NTL / QPR rows further per step p)
+  struct Off {
+    uint32_t qk, v, qk_step, v_step;
+  };
+  GDN_DEV static Off offsets(int64_t ld_qk, int64_t ld_v, int tid) {
+    Off o;
+    o.qk = (uint32_t)((tid / QPR) * ld_qk * (int64_t)sizeof(E) + (tid % QPR) * 16);
+    o.v = (uint32_t)((tid / VPR) * ld_v * (int64_t)sizeof(E) + (tid % VPR) * 16);
+    o.qk_step = (uint32_t)((NTL / QPR) * ld_qk * (int64_t)sizeof(E));
+    o.v_step = (uint32_t)((NTL / VPR) * ld_v * (int64_t)sizeof(E));
+    return o;
+  }
+
   GDN_DEV void load(const E* qp, const E* kp, int64_t ld_qk, const E* vp, int64_t ld_v,
-                    const char* rec, int64_t tc, int64_t te, int tid) {
+                    const char* rec, int64_t tc, int64_t te, const Off& off, int tid) {
+    const int64_t rows = te - tc < BT ? te - tc : BT;  // rows of the chunk in its sequence (>= 1)
+    // the last valid row ends its head slice inside the range; row `rows` starts past it
+    const uint32_t qk_bytes = (uint32_t)(((rows - 1) * ld_qk + DK) * (int64_t)sizeof(E));
+    const uint32_t v_bytes = (uint32_t)(((rows - 1) * ld_v + DV) * (int64_t)sizeof(E));
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp + tc * ld_qk, qk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp + tc * ld_v, v_bytes);
 #pragma unroll
     for (int p = 0; p < PQ; p++) {
-      const int i = tid + NTL * p;
-      const int row = i / QPR, vi = i % QPR;
-      const int64_t t = tc + row;
-      const bool ok = t < te;
-      if constexpr (HAS_Q) q[p] = ok ? *reinterpret_cast<const V16*>(qp + t * ld_qk + vi * VE) : zero_vec16<E>();
-      k[p] = ok ? *reinterpret_cast<const V16*>(kp + t * ld_qk + vi * VE) : zero_vec16<E>();
+      if constexpr (HAS_Q) q[p] = buffer_load16<V16>(buffer_rsrc(qp + tc * ld_qk, qk_bytes), off.qk, p * off.qk_step);
+      k[p] = buffer_load16<V16>(rk, off.qk, p * off.qk_step);
     }
 #pragma unroll
-    for (int p = 0; p < PV; p++) {
-      const int i = tid + NTL * p;
-      const int row = i / VPR, vi = i % VPR;
-      const int64_t t = tc + row;
-      v[p] = t < te ? *reinterpret_cast<const V16*>(vp + t * ld_v + vi * VE) : zero_vec16<E>();
-    }
+    for (int p = 0; p < PV; p++) v[p] = buffer_load16<V16>(rv, off.v, p * off.v_step);
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(rec, (uint32_t)RECB);
 #pragma unroll
-    for (int p = 0; p < PR; p++) {
-      const int i = tid + NTL * p;
-      if (i < RV) r[p] = *reinterpret_cast<const floatx4*>(rec + 16 * i);
-    }
+    for (int p = 0; p < PR; p++) r[p] = buffer_load16<floatx4>(rr, 16u * tid, 16u * NTL * p);
   }
   // rows into LDS (q and k chunk-swizzled); with q, also its l2norm factors
   // (with the scale): a q row is QPR consecutive lanes
@@ -713,8 +742,9 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     const E* kp = (const E*)a.k + (int64_t)qa * DK;
     const E* vp = (const E*)a.v + (int64_t)h * DV;
     const int64_t rstride = (int64_t)Hv * kRecBytes;
+    const typename LD::Off off = LD::offsets(a.ld_qk, a.ld_v, ltid);
     LD ld;
-    if (nchunks > 0) ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + chunk0 * rstride, tb, te, ltid);
+    if (nchunks > 0) ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + chunk0 * rstride, tb, te, off, ltid);
     for (int it = -1; it < nchunks; it++) {
       const int pc = it + 1;
       if (pc < nchunks) {
@@ -722,7 +752,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
         ld.store(B, ltid, a.scale, a.use_l2norm);
         if (pc + 1 < nchunks)
           ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (chunk0 + pc + 1) * rstride,
-                  tb + (int64_t)(pc + 1) * BT, te, ltid);
+                  tb + (int64_t)(pc + 1) * BT, te, off, ltid);
         if constexpr (OUT) {
           // P and fo of the chunk just stored, made here while the consumers
           // run the previous chunk: once every loader wave's rows are in
@@ -914,20 +944,25 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
         // o, after the state update's products (which hide the latency of
         // the last o products): four consecutive value columns of one token
         // per lane, one 8-byte (bf16) store per tile, straight to HBM
+        // (a buffer resource over the chunk's rows of this head: the
+        // lane's byte offset is fixed, rows past the sequence end fall
+        // outside the range and their stores are dropped)
         typedef E E4 __attribute__((ext_vector_type(4)));
+        static_assert(sizeof(E4) == 8, "8-byte o stores");
         const int64_t tc = tb + (int64_t)it * BT;
-        E* op = (E*)a.o + (tc * o_ld + (int64_t)h * DV + c0 + 4 * g4);
+        const int64_t rows = te - tc < BT ? te - tc : BT;
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc((E*)a.o + (tc * o_ld + (int64_t)h * DV),
+                        (uint32_t)(((rows - 1) * o_ld + DV) * (int64_t)sizeof(E)));
+        const uint32_t ooff = (uint32_t)((ln * o_ld + c0 + 4 * g4) * (int64_t)sizeof(E));
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const int row = 16 * mt + ln;
-          if (tc + row < te) {
 #pragma unroll
-            for (int nt = 0; nt < NN; nt++) {
-              E4 v4;
+          for (int nt = 0; nt < NN; nt++) {
+            E4 v4;
 #pragma unroll
-              for (int j = 0; j < 4; j++) v4[j] = from_f<E>(o[mt][nt][j]);
-              *reinterpret_cast<E4*>(op + row * o_ld + 16 * nt) = v4;
-            }
+            for (int j = 0; j < 4; j++) v4[j] = from_f<E>(o[mt][nt][j]);
+            buffer_store8(v4, ro, ooff, (uint32_t)((16 * mt * o_ld + 16 * nt) * (int64_t)sizeof(E)));
           }
         }
       }
