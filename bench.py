@@ -48,6 +48,10 @@ def conv_bytes_per_token(C, s):
     return 2 * C * s  # read x, write y
 
 
+def conv_bwd_bytes_per_token(C, s):
+    return 3 * C * s  # read x and dy, write dx
+
+
 def chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s):
     """Algorithmic HBM bytes of one chunk forward: read q, k, v, g, beta;
     write o; read h0 and write ht once per sequence."""
@@ -164,6 +168,20 @@ def main():
         "conv_fwd": {"bound": "hbm", "achieved": conv_b / t_conv / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": conv_b / t_conv / HBM_PEAK},
     }
+    if spec.backward:
+        # the backward dominates such a step: its call is the roofline line,
+        # the forward's moves to the other entries
+        t_bwd = per_call["chunk_bwd"] * 1e-3
+        bwd_flops = 2 * flops  # reverse mode of the chunk algorithm: twice the forward's products
+        extra["chunk_fwd"] = dict(roofline, kernel="gdn_chunk_fwd call")
+        roofline = {"bound": "mfma", "achieved": bwd_flops / t_bwd / 1e12, "peak": peak / 1e12,
+                    "unit": "TFLOP/s", "frac": bwd_flops / t_bwd / peak,
+                    "traffic": measured_traffic("chunk_bwd", spec.name),
+                    "kernel": "gdn_chunk_bwd call: per-chunk states, dS passes, gradients, finalize"}
+        t_cbwd = per_call["conv_bwd"] * 1e-3
+        cbwd_b = conv_bwd_bytes_per_token(C, s_bytes) * T + C * K * (s_bytes + 4)
+        extra["conv_bwd"] = {"bound": "hbm", "achieved": cbwd_b / t_cbwd / 1e9, "peak": HBM_PEAK / 1e9,
+                             "unit": "GB/s", "frac": cbwd_b / t_cbwd / HBM_PEAK}
 
     cpu = None
     if not args.no_cpu_baseline:
