@@ -51,22 +51,22 @@ __host__ __device__ constexpr int p_frag(int mt, int s) { return mt == 0 ? 0 : m
 
 namespace {
 
-constexpr int kPrepLd = 64 + 8;  // bf16 staging tiles [64][kPrepLd]
 constexpr int kPrepScLd = 20;    // fp32 16 x 16 scratch rows (16 + 4)
 
 // fp32 16 x 16 tiles of the staging area, per wave w from prep_tile0(w):
 // wave 0: L_00 and a work tile; wave w > 0: L_ww and the work tile of its
-// inversion, which then hold A_w and E_w0, followed by E_w1 .. E_w,w-1.
+// inversion, which then hold A_w and E_w0, followed by E_w1 .. E_w,w-1.  The
+// first tile of a wave is read by that wave only; it finally turns T's tiles
+// into fragment lane order.
 __host__ __device__ constexpr int prep_tile0(int w) { return w == 0 ? 0 : w * (w + 1) / 2 + 1; }
 constexpr int kPrepTiles = 11;
 
 // The raw rows are dead once the products are formed, so the per-head staging
-// shares their space (six workgroups fit a CU).
+// shares their space (19.7 KB a workgroup; seven a CU, held by registers).
 template <int DK>
 struct PrepSmem {
   static constexpr int LDK = DK + 8;
   struct Stage {
-    alignas(16) bf16 st[64 * kPrepLd];  // T, C-layout writes
     alignas(16) float sc[kPrepTiles][16 * kPrepScLd];
   };
   union {
@@ -194,14 +194,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void c
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) rkL[jj] = sm.rk[16 * w + 4 * g4 + jj];
   __syncthreads();  // every wave's products are formed: the rows' space is reused
-  // the two blocks above the diagonal that the fragments include, (0, 1) and
-  // (2, 3), stay zero: 2 x 256 elements, two a thread
-  {
-    const int blk = tid >> 7, e = (tid & 127) * 2;  // block 0: rows 0-15, block 1: rows 32-47
-    const int r = 32 * blk + (e >> 4), c = 16 + 32 * blk + (e & 15);
-    sm.u.s.st[r * kPrepLd + c] = (bf16)0.f;
-    sm.u.s.st[r * kPrepLd + c + 1] = (bf16)0.f;
-  }
   float* const tiles = sm.u.s.sc[prep_tile0(w)];
   float* Lt = tiles;                   // L_ww, then A_w
   float* wk = tiles + 16 * kPrepScLd;  // work tile, then E_w0
@@ -303,26 +295,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void c
         }
         Tc[i] = -acc;
       }
+      // column block w is half w % 2 (bytes 8(w % 2) .. + 7 of each lane's
+      // 16) of the fragments of contraction slab w / 2: lane l holds row l%16
+      // and columns 4(l/16) .. + 3 of the block, so each tile is turned from C
+      // layout through this wave's own tile (A_w is no longer read) and its
+      // half stored straight to the record
+      char* tdst = rec + kRecT + 8 * (w & 1) + 16 * lane;
+      if (w & 1)  // the zero block above the diagonal in row block w - 1
+        *reinterpret_cast<bf16x4*>(tdst + p_frag(w - 1, w >> 1) * 1024) = bf16x4{};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (i < w) continue;
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++)
-          sm.u.s.st[(16 * i + 4 * g4 + jj) * kPrepLd + 16 * w + ln] = (bf16)Tc[i][jj];
+        for (int jj = 0; jj < 4; jj++) Lt[(4 * g4 + jj) * kPrepScLd + ln] = Tc[i][jj];
+        wave_lds_sync();
+        const floatx4 tv = *reinterpret_cast<const floatx4*>(Lt + ln * kPrepScLd + 4 * g4);
+        bf16x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; e++) b[e] = (bf16)tv[e];
+        *reinterpret_cast<bf16x4*>(tdst + p_frag(i, w >> 1) * 1024) = b;
+        wave_lds_sync();  // read before the next tile overwrites
       }
-    }
-    __syncthreads();
-    // copy T out as A fragments in lane order
-    for (int i = tid; i < 6 * 64; i += 256) {
-      const int f = i >> 6, l = i & 63;
-      const int mt = f == 0 ? 0 : f == 1 ? 1 : (f + 2) >> 1, s = f < 2 ? 0 : (f & 1);
-      const bf16* src = sm.u.s.st + (16 * mt + (l & 15)) * kPrepLd + 32 * s + 4 * (l >> 4);
-      bf16x8 v;
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
-      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-      *reinterpret_cast<bf16x8*>(rec + kRecT + f * 1024 + l * 16) = v;
     }
     __syncthreads();  // staging is rewritten for the next value head
   }
