@@ -122,11 +122,48 @@ GDN_DEV floatx4 prep_invert16(const float* Lt, const float* bb, const floatx4& N
   return R2 - t;
 }
 
+// Column block W of T: T_WW = A_W (Ai), T_iW = -sum_{W <= j < i} E_ij T_jW
+// for i > W (E_ij from wave i's tiles).  Block W is half W % 2 (bytes
+// 8(W % 2) .. + 7 of each lane's 16) of the fragments of contraction slab
+// W / 2, where lane l holds row l%16 and columns 4(l/16) .. + 3 of the block:
+// each tile goes from C layout through this wave's own tile Lt (A_W is no
+// longer read) and its half is stored straight to the record.
+template <int W, class SM>
+GDN_DEV void prep_column(SM& sm, const floatx4& Ai, float* Lt, char* rec, int lane) {
+  typedef Tile16<float> F;
+  const int g4 = lane >> 4, ln = lane & 15;
+  floatx4 Tc[4];
+  Tc[W] = Ai;
+#pragma unroll
+  for (int i = W + 1; i < 4; i++) {
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int j = W; j < i; j++)
+      F::mma(acc, F::load(sm.u.s.sc[prep_tile0(i) + 1 + j], kPrepScLd, 0, 0, lane), Tc[j]);
+    Tc[i] = -acc;
+  }
+  char* tdst = rec + kRecT + 8 * (W & 1) + 16 * lane;
+  if constexpr (W & 1)  // the zero block above the diagonal in row block W - 1
+    *reinterpret_cast<bf16x4*>(tdst + p_frag(W - 1, W >> 1) * 1024) = bf16x4{};
+#pragma unroll
+  for (int i = W; i < 4; i++) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) Lt[(4 * g4 + jj) * kPrepScLd + ln] = Tc[i][jj];
+    wave_lds_sync();
+    const floatx4 tv = *reinterpret_cast<const floatx4*>(Lt + ln * kPrepScLd + 4 * g4);
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; e++) b[e] = (bf16)tv[e];
+    *reinterpret_cast<bf16x4*>(tdst + p_frag(i, W >> 1) * 1024) = b;
+    wave_lds_sync();  // read before the next tile overwrites
+  }
+}
+
 // One (chunk, q/k head) per workgroup of four waves.  Wave w owns the L
 // blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
 // the wave) and column block w of T.
 template <int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void chunk_prep_kernel(PrepArgs a) {
   typedef Mfma<bf16> M;
   typedef M::frag Fr;
   typedef Tile16<float> F;
@@ -276,46 +313,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void c
       }
     }
     __syncthreads();  // every E block is in place
-    // column block m = w of T: T_ww = A_w, T_iw = -sum_{w <= j < i} E_ij T_jw
-    {
-      floatx4 Tc[4];  // static indices only (w is a runtime value)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (i <= w) {
-          Tc[i] = i == w ? Ai : zero4();
-          continue;
-        }
-        floatx4 acc = zero4();
-#pragma unroll
-        for (int j = 0; j < 3; j++) {
-          if (j < w || j >= i) continue;
-          // E_ij: tile j + 1 of wave i (tile 0 holds A_i)
-          const float* et = sm.u.s.sc[prep_tile0(i) + 1 + j];
-          F::mma(acc, F::load(et, kPrepScLd, 0, 0, lane), Tc[j]);
-        }
-        Tc[i] = -acc;
-      }
-      // column block w is half w % 2 (bytes 8(w % 2) .. + 7 of each lane's
-      // 16) of the fragments of contraction slab w / 2: lane l holds row l%16
-      // and columns 4(l/16) .. + 3 of the block, so each tile is turned from C
-      // layout through this wave's own tile (A_w is no longer read) and its
-      // half stored straight to the record
-      char* tdst = rec + kRecT + 8 * (w & 1) + 16 * lane;
-      if (w & 1)  // the zero block above the diagonal in row block w - 1
-        *reinterpret_cast<bf16x4*>(tdst + p_frag(w - 1, w >> 1) * 1024) = bf16x4{};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (i < w) continue;
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) Lt[(4 * g4 + jj) * kPrepScLd + ln] = Tc[i][jj];
-        wave_lds_sync();
-        const floatx4 tv = *reinterpret_cast<const floatx4*>(Lt + ln * kPrepScLd + 4 * g4);
-        bf16x4 b;
-#pragma unroll
-        for (int e = 0; e < 4; e++) b[e] = (bf16)tv[e];
-        *reinterpret_cast<bf16x4*>(tdst + p_frag(i, w >> 1) * 1024) = b;
-        wave_lds_sync();  // read before the next tile overwrites
-      }
+    // column block m = w of T (the wave index fixed at compile time, so the
+    // products that do not wait on the block above interleave)
+    switch (w) {
+      case 0: prep_column<0>(sm, Ai, Lt, rec, lane); break;
+      case 1: prep_column<1>(sm, Ai, Lt, rec, lane); break;
+      case 2: prep_column<2>(sm, Ai, Lt, rec, lane); break;
+      default: prep_column<3>(sm, Ai, Lt, rec, lane); break;
     }
     __syncthreads();  // staging is rewritten for the next value head
   }
