@@ -502,11 +502,11 @@ void chunk_loop_kernel(LoopArgs a) {
 GDN_DEV int dk_of_row(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3); }
 
 // One LDS buffer: raw rows and the record.  Rows are padded by 32 bytes
-// (288-byte rows for 128 bf16), and the 16-byte chunks of a q or k row are
-// stored with the chunk index XOR-ed with bit 3 of the row.  Over 64 banks of
-// 4 bytes the 16-byte row reads of q and k, the loaders' stores and v's
-// transposing reads are then free of bank conflicts, and k's transposing
-// reads (one 8-byte half of each chunk) two-way instead of four-way.
+// (288-byte rows for 128 bf16): the 16-byte row reads of q and k (rows
+// l%16 of a fragment) then meet no bank conflict, and the transposing reads
+// of k and v two-way ones (both measured with the SQ_LDS_BANK_CONFLICT
+// counter on gfx950; 256- or 272-byte rows, or the 16-byte pieces of a row
+// XOR-ed with a row bit, conflict on the row reads).
 template <typename O, int DK, int DV, bool OUT>
 struct WsSmem {
   static constexpr int PAD = 32 / (int)sizeof(O);
@@ -606,7 +606,7 @@ struct WsLoad {
 #pragma unroll
     for (int p = 0; p < PR; p++) r[p] = buffer_load16<floatx4>(rr, 16u * tid, 16u * NTL * p);
   }
-  // rows into LDS (q and k chunk-swizzled); with q, also its l2norm factors
+  // rows into LDS; with q, also its l2norm factors
   // (with the scale): a q row is QPR consecutive lanes
   template <class SM>
   GDN_DEV void store(SM& sm, int tid, float scale, int use_l2norm) const {
@@ -614,7 +614,7 @@ struct WsLoad {
     for (int p = 0; p < PQ; p++) {
       const int i = tid + NTL * p;
       const int row = i / QPR, vi = i % QPR;
-      const int vx = vi ^ ((row >> 3) & 1);  // chunk swizzle of the q / k rows
+      const int vx = vi;
       if constexpr (HAS_Q) {
         *reinterpret_cast<V16*>(sm.q + row * SM::LDK + vx * VE) = q[p];
         const float ss = row_group_sum<QPR>(sum_sq(q[p]));
@@ -678,8 +678,8 @@ struct PHalf {
     if (real) {
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ks++)
-        Mfma<bf16>::mma(acc, Mfma<bf16>::load_k8_x(C.k, SM::LDK, 16 * jp, 32 * ks, lane),
-                        Mfma<bf16>::load_k8_x(C.q, SM::LDK, 16 * mt, 32 * ks, lane));
+        Mfma<bf16>::mma(acc, Mfma<bf16>::load_k8(C.k, SM::LDK, 16 * jp, 32 * ks, lane),
+                        Mfma<bf16>::load_k8(C.q, SM::LDK, 16 * mt, 32 * ks, lane));
     }
   }
   template <class SM>
@@ -835,13 +835,13 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
         for (int nt = 0; nt < NN; nt++) b[nt] = acc_as_b<O>(S, s, nt);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-          const Fr kf = M::load_k8_x(C.k, SM::LDK, 16 * mt, s * KS, lane);
+          const Fr kf = M::load_k8(C.k, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
           if constexpr (OUT) {
             // o^T = S^T q^T: the state fragment is the A operand (its column
             // index is the row of the product), q rows the B operand
-            const Fr qf = M::load_k8_x(C.q, SM::LDK, 16 * mt, s * KS, lane);
+            const Fr qf = M::load_k8(C.q, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
             for (int nt = 0; nt < NN; nt++) M::mma(o[mt][nt], b[nt], qf);
           }
@@ -931,8 +931,8 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
           // A = k^T: the dk rows of tile mt (permuted), tokens s KS.. down the
           // stored rows
           const int cdk = 32 * (mt >> 1) + 4 * (mt & 1);
-          const bf16x4 lo = lds_rows4_tr_x(C.k, SM::LDK, s * KS, cdk, lane);
-          const bf16x4 hi = lds_rows4_tr_x(C.k, SM::LDK, s * KS + 16, cdk, lane);
+          const bf16x4 lo = lds_rows4_tr(C.k, SM::LDK, s * KS, cdk, lane, 8);
+          const bf16x4 hi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, cdk, lane, 8);
           const Fr kf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], kf, xv[s][nt]);

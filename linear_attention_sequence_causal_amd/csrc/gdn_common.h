@@ -98,12 +98,6 @@ template <> struct Mfma<bf16> {
   GDN_DEV static frag load_k8(const bf16* base, int ld, int row0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8*>(base + ((lane & 15) * ld + 8 * (lane >> 4)) + (row0 * ld + k0));
   }
-  // load_k8 from a [rows][ld] array whose 16-byte chunks are stored with the
-  // chunk index XOR-ed with bit 3 of the row (row0 and k0 multiples of 16)
-  GDN_DEV static frag load_k8_x(const bf16* base, int ld, int row0, int k0, int lane) {
-    const int ln = lane & 15, g = lane >> 4;
-    return *reinterpret_cast<const bf16x8*>(base + (ln * ld + 8 * (g ^ (ln >> 3))) + (row0 * ld + k0));
-  }
   // same from an fp32 [rows][ld] array, element k scaled by sc[k]
   GDN_DEV static frag load_scaled(const float* base, int ld, int row0, int k0, const float* sc,
                                   int lane) {
@@ -274,17 +268,6 @@ GDN_DEV floatx4 lds_tile_c(const bf16* base, int ld, int r0, int c0, int lane) {
 GDN_DEV floatx4 lds_tile_c(const float* base, int ld, int r0, int c0, int lane) {
   const float* p = base + (r0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
   return floatx4{p[0], p[ld], p[2 * ld], p[3 * ld]};
-}
-
-// lds_rows4_tr with cs = 8 from an array stored like load_k8_x's (16-byte
-// chunk index XOR-ed with bit 3 of the row; r0 a multiple of 16, c0 / 8 a
-// multiple of 4): lane i still receives column c0 + 8(i/4) + i%4.
-GDN_DEV bf16x4 lds_rows4_tr_x(const bf16* base, int ld, int r0, int c0, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const bf16* p = base + ((4 * g + (i >> 2)) * ld + 8 * ((i & 3) ^ (g >> 1))) + (r0 * ld + c0);
-  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
 }
 
 GDN_DEV floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
