@@ -179,7 +179,9 @@ size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, in
  *   ws       workspace of gdn_chunk_workspace_size(..., 0) bytes (256-byte
  *            aligned) or NULL when that size is 0.
  * Errors: GDN_EINVAL for negative sizes, Hk < 1, Hv % Hk != 0, ld_qk smaller
- * than Hk*dk, ld_v smaller than Hv*dv, null required pointers;
+ * than Hk*dk, ld_v smaller than Hv*dv, row strides that are not multiples of
+ * 16 bytes or whose 64 rows (of q/k, v or o) span 4 GiB or more, null or
+ * misaligned required pointers;
  * GDN_EUNSUPPORTED unless dk, dv in {32, 64, 128} (bfloat16) or in {32, 64}
  * (float32, whose chunk tiles would not fit in LDS at 128); GDN_EWORKSPACE.
  */

@@ -63,6 +63,10 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
   const int es = dt == GDN_BF16 ? 2 : 4;
   if ((ld_qk * es) % 16 || (ld_v * es) % 16)
     return fail(GDN_EINVAL, "%s: row strides must be multiples of 16 bytes", fn);
+  // a chunk's 64 rows (q, k, v and o) are addressed with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if (64 * ld_qk * es >= lim || 64 * ld_v * es >= lim || 64 * (int64_t)Hv * dv * es >= lim)
+    return fail(GDN_EINVAL, "%s: 64 rows of q, k, v or o must span less than 4 GiB", fn);
   if (T > 0) {
     if (N < 1) return fail(GDN_EINVAL, "%s: T > 0 needs N >= 1 sequences", fn);
     if (!q || !k || !v || !g || !beta || !cu) return fail(GDN_EINVAL, "%s: null pointer", fn);

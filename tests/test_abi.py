@@ -108,6 +108,7 @@ def test_chunk_rejects_bad_arguments(lib):
     assert _chunk(lib, q=None) == gdn.GDN_EINVAL
     assert _chunk(lib, q=ctypes.c_void_p(0x1002)) == gdn.GDN_EINVAL     # misaligned
     assert _chunk(lib, T=-1) == gdn.GDN_EINVAL
+    assert _chunk(lib, ld_qk=1 << 25, ld_v=6144) == gdn.GDN_EINVAL  # 64 rows past 32-bit offsets
     assert _chunk(lib, ws=None, ws_bytes=0) == gdn.GDN_EWORKSPACE
     assert _chunk(lib, ws=ctypes.c_void_p(0x1010)) == gdn.GDN_EWORKSPACE  # not 256-aligned
     assert _chunk(lib, ws_bytes=16) == gdn.GDN_EWORKSPACE
