@@ -51,14 +51,19 @@ __device__ __forceinline__ Row<E, V> load_row(const E* p) {
   return r;
 }
 
-template <typename E, int V>
+// NT: a non-temporal store (streamed past the caches; the conv forward's
+// output is not read again before it leaves them)
+template <typename E, int V, bool NT = false>
 __device__ __forceinline__ void store_row(E* p, const float* f) {
   if constexpr (V * sizeof(E) == 16) {
     typedef typename Vec16<E>::type VT;
     VT t;
 #pragma unroll
     for (int i = 0; i < V; i++) t[i] = from_f<E>(f[i]);
-    *reinterpret_cast<VT*>(p) = t;
+    if constexpr (NT)
+      __builtin_nontemporal_store(t, reinterpret_cast<VT*>(p));
+    else
+      *reinterpret_cast<VT*>(p) = t;
   } else {
 #pragma unroll
     for (int i = 0; i < V; i++) p[i] = from_f<E>(f[i]);
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
         for (int j = 0; j < K; j++) z += wv[j][i] * xr[r + j].at(i);
         out[i] = z * fast_sigmoid(z);
       }
-      store_row<E, V>(y + (t0 + r) * C + c0, out);
+      store_row<E, V, true>(y + (t0 + r) * C + c0, out);
     }
     return;
   }
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
       float out[V];
 #pragma unroll
       for (int i = 0; i < V; i++) out[i] = z[i] * fast_sigmoid(z[i]);
-      store_row<E, V>(y + t * C + c0, out);
+      store_row<E, V, true>(y + t * C + c0, out);
     }
   }
 }
