@@ -51,8 +51,8 @@ __device__ __forceinline__ Row<E, V> load_row(const E* p) {
   return r;
 }
 
-// NT: a non-temporal store (streamed past the caches; the conv forward's
-// output is not read again before it leaves them)
+// NT: a non-temporal store (streamed past the caches; the conv's outputs, y
+// and dx, are not read again before they would leave them)
 template <typename E, int V, bool NT = false>
 __device__ __forceinline__ void store_row(E* p, const float* f) {
   if constexpr (V * sizeof(E) == 16) {
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
               for (int i = 0; i < V; i++) out[i] += wv[j][i] * dzw[K - 1 - j][i];
             }
           }
-          store_row<E, V>(dx + tp * C + c0, out);
+          store_row<E, V, true>(dx + tp * C + c0, out);
         }
       }
       // halo rows (tokens s0 - i, i = 1..K-1, before local sequence 0) once
