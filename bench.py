@@ -160,7 +160,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic("chunk_fwd", spec.name),
-                "kernel": "gdn_chunk_fwd call: plan, segment summaries, scan, output pass"}
+                "kernel": "gdn_chunk_fwd call: plan, prep, segment summaries, scan, output pass"}
     chunk_hbm = chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
     extra = {
         "chunk_fwd_hbm": {"achieved": chunk_hbm / t_chunk / 1e9, "peak": HBM_PEAK / 1e9,
