@@ -694,24 +694,31 @@ __global__ __launch_bounds__(256) void finalize_qk_kernel(BwdArgs a, int64_t uni
   const int64_t t = u / a.Hk;
   const int qa = (int)(u % a.Hk);
   const int grp = a.Hv / a.Hk;
+  // lane owns the PER consecutive elements d = PER lane .. + PER - 1
   constexpr int PER = (DK + 63) / 64;
   float dq[PER], dk[PER], q[PER], k[PER];
   float qs = 0.f, ks = 0.f, qd = 0.f, kd = 0.f;
   const E* qp = (const E*)a.q + t * a.ld_qk + (int64_t)qa * DK;
   const E* kp = (const E*)a.k + t * a.ld_qk + (int64_t)qa * DK;
 #pragma unroll
-  for (int e = 0; e < PER; e++) {
-    const int d = lane + 64 * e;
-    dq[e] = dk[e] = q[e] = k[e] = 0.f;
-    if (d < DK) {
-      for (int hh = qa * grp; hh < (qa + 1) * grp; hh++) {
-        const float* src = a.dqk + (t * a.Hv + hh) * 2 * DK;
-        dq[e] += src[d];
-        dk[e] += src[DK + d];
+  for (int e = 0; e < PER; e++) dq[e] = dk[e] = q[e] = k[e] = 0.f;
+  if (PER * lane < DK) {
+    for (int hh = qa * grp; hh < (qa + 1) * grp; hh++) {
+      const float* src = a.dqk + (t * a.Hv + hh) * 2 * DK + PER * lane;
+#pragma unroll
+      for (int e = 0; e < PER; e++) {
+        dq[e] += src[e];
+        dk[e] += src[DK + e];
       }
-      q[e] = to_f(qp[d]);
-      k[e] = to_f(kp[d]);
     }
+#pragma unroll
+    for (int e = 0; e < PER; e++) {
+      q[e] = to_f(qp[PER * lane + e]);
+      k[e] = to_f(kp[PER * lane + e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; e++) {
     qs += q[e] * q[e];
     ks += k[e] * k[e];
     qd += q[e] * dq[e];
@@ -725,10 +732,10 @@ __global__ __launch_bounds__(256) void finalize_qk_kernel(BwdArgs a, int64_t uni
   E* dkp = (E*)a.dk + t * a.ld_dqk + (int64_t)qa * DK;
   const float rq = a.use_l2norm ? 1.f / sqrtf(qs + 1e-6f) : 1.f;
   const float rk = a.use_l2norm ? 1.f / sqrtf(ks + 1e-6f) : 1.f;
+  if (PER * lane < DK) {
 #pragma unroll
-  for (int e = 0; e < PER; e++) {
-    const int d = lane + 64 * e;
-    if (d < DK) {
+    for (int e = 0; e < PER; e++) {
+      const int d = PER * lane + e;
       float gq = a.scale * dq[e], gk = dk[e];
       if (a.use_l2norm) {
         gq = a.scale * rq * (dq[e] - q[e] * rq * rq * qd);
