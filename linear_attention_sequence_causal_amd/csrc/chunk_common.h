@@ -307,12 +307,20 @@ GDN_DEV void compute_w(SM& sm, int wave, int lane) {
   typedef Mfma<O> M;
   constexpr int NS = BT / M::KSTEP;
   constexpr int NTILE = 4 * (DK / 16);
+  // with NW a multiple of 4 every tile of a wave lies in row block wave % 4:
+  // its scaled T fragments are formed once
+  constexpr bool ONE_ROW = NW % 4 == 0;
+  typename M::frag af[NS];
+  if constexpr (ONE_ROW) {
+#pragma unroll
+    for (int s = 0; s < NS; s++) af[s] = M::load_scaled(sm.Tm, SM::LDF, 16 * (wave % 4), s * M::KSTEP, sm.bg, lane);
+  }
   for (int tt = wave; tt < NTILE; tt += NW) {
     const int mt = tt % 4, nt = tt / 4;
     floatx4 acc = zero4();
 #pragma unroll
     for (int s = 0; s < NS; s++)
-      M::mma(acc, M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.bg, lane),
+      M::mma(acc, ONE_ROW ? af[s] : M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.bg, lane),
              M::load_col(sm.k, SM::LDK, 16 * nt, s * M::KSTEP, lane));
     const int rb = 16 * mt + 4 * (lane >> 4), c = 16 * nt + (lane & 15);
 #pragma unroll
