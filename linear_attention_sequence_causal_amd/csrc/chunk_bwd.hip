@@ -196,6 +196,16 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 #pragma unroll
       for (int nt = 0; nt < 2; nt++) sb[s][nt] = acc_as_b<O>(dS, s, nt);
     floatx4 dvn[4][2];
+    // this wave's dO columns (the identity columns see no dO: their operand
+    // is zero -- a select, not a branch, keeps both modes' registers alike)
+    typename M::frag dof[NSB][2];
+#pragma unroll
+    for (int s = 0; s < NSB; s++) {
+      const typename M::frag v0 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 0 : vc0, s * KS, lane);
+      const typename M::frag v1 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 16 : vc0 + 16, s * KS, lane);
+      dof[s][0] = mcol ? typename M::frag{} : v0;
+      dof[s][1] = mcol ? typename M::frag{} : v1;
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
       floatx4 k0 = zero4(), k1 = zero4(), p0 = zero4(), p1 = zero4();
@@ -207,13 +217,9 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
       }
 #pragma unroll
       for (int s = 0; s < NSB; s++) {
-        // the identity columns see no dO: their operand is zero (a select,
-        // not a branch, keeps both modes' registers alike)
         const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
-        const typename M::frag v0 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 0 : vc0, s * KS, lane);
-        const typename M::frag v1 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 16 : vc0 + 16, s * KS, lane);
-        M::mma(p0, pt, mcol ? typename M::frag{} : v0);
-        M::mma(p1, pt, mcol ? typename M::frag{} : v1);
+        M::mma(p0, pt, dof[s][0]);
+        M::mma(p1, pt, dof[s][1]);
       }
       const int rb = 16 * mt + 4 * (lane >> 4);
 #pragma unroll
