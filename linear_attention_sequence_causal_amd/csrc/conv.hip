@@ -25,6 +25,7 @@ constexpr int kRunsPerBlock = 4;   // blockDim.y
 constexpr int kLanes = 64;         // blockDim.x: channel vectors per block
 constexpr int kFwdRows = 8;        // tokens per thread run, forward
 constexpr int kBwdRows = 16;       // tokens per thread run, backward
+constexpr int kBwdPrefetch = 3;    // rows in flight ahead of the one formed, backward
 constexpr int kBwdMaxSplits = 64;  // token splits of the backward grid (dw partial rows)
 
 // V channels of one row: a packed 16-byte vector when V*sizeof(E) == 16
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
     E* __restrict__ dhalo, float* __restrict__ part_w, float* __restrict__ part_b) {
   constexpr int R = kBwdRows;
   constexpr int DR = R + K - 1;  // dz rows t0 .. t0+R+K-2
+  constexpr int PD = kBwdPrefetch < DR ? kBwdPrefetch : DR;
   __shared__ float red[kLanes][V * (K + 1)];
   const int c0 = (blockIdx.y * kLanes + threadIdx.x) * V;
   const bool active = c0 < C;
@@ -219,12 +221,14 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < K; j++) dwacc[j][i] = 0.f;
   }
-  float wv[K][V], bv[V];
+  // taps and bias kept in the activation type (exact: they are read from it),
+  // which leaves registers for the rows in flight
+  Row<E, V> wv[K], bv;
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    bv[i] = (active && bias) ? to_f(bias[c0 + i]) : 0.f;
+    bv.v[i] = (active && bias) ? bias[c0 + i] : from_f<E>(0.f);
 #pragma unroll
-    for (int j = 0; j < K; j++) wv[j][i] = active ? to_f(w[(c0 + i) * K + j]) : 0.f;
+    for (int j = 0; j < K; j++) wv[j].v[i] = active ? w[(c0 + i) * K + j] : from_f<E>(0.f);
   }
   const int64_t cu0 = cu[0];
 
@@ -232,11 +236,6 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
   for (int64_t tile = blockIdx.x; active && tile * tile_tokens < T; tile += gridDim.x) {
     const int64_t t0 = tile * tile_tokens + (int64_t)threadIdx.y * R;
     if (t0 >= T) continue;
-    const bool use_halo = n_halo > 0 && t0 - (K - 1) < cu0;
-    Row<E, V> hr[K > 1 ? K - 1 : 1];
-#pragma unroll
-    for (int i = 0; i < K - 1; i++)
-      hr[i] = use_halo ? load_row<E, V>(halo + (int64_t)i * C + c0) : zero_row<E, V>();
     // windows: xw[j] = x row t-(K-1)+j, dzw[j] = dz row t-(K-1)+j and ew[j]
     // = the end of that row's sequence, at the current step t
     Row<E, V> xw[K];
@@ -255,6 +254,16 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
       xw[i + 1] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
     }
 
+    // the x and dy rows of the next PD tokens are in flight while a row is
+    // formed (one row at a time leaves too few bytes in flight per CU)
+    Row<E, V> px[PD], pg[PD];
+#pragma unroll
+    for (int d = 0; d < PD; d++) {
+      const int64_t t = t0 + d;
+      px[d] = t < T ? load_row<E, V>(x + t * C + c0) : zero_row<E, V>();
+      pg[d] = t < T ? load_row<E, V>(dy + t * C + c0) : zero_row<E, V>();
+    }
+
     int n = find_seq(cu, N, t0);
     int64_t s = cu[n], e = cu[n + 1];
     const int n_first = n;
@@ -269,8 +278,13 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < V; i++) dzw[j][i] = dzw[j + 1][i];
       }
-      xw[K - 1] = t < T ? load_row<E, V>(x + t * C + c0) : zero_row<E, V>();
-      const Row<E, V> gr = t < T ? load_row<E, V>(dy + t * C + c0) : zero_row<E, V>();
+      xw[K - 1] = px[r % PD];
+      const Row<E, V> gr = pg[r % PD];
+      if (r + PD < DR) {
+        const int64_t tn = t + PD;
+        px[r % PD] = tn < T ? load_row<E, V>(x + tn * C + c0) : zero_row<E, V>();
+        pg[r % PD] = tn < T ? load_row<E, V>(dy + tn * C + c0) : zero_row<E, V>();
+      }
       if (t < T) {
         while (t >= e) {
           n++;
@@ -288,20 +302,18 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
 #pragma unroll
             for (int i = 0; i < V; i++) xt[j][i] = xw[j].at(i);
           } else if (n == 0 && s - tau <= n_halo) {
-            const int hrow = (int)(K - 1 - (s - tau));
+            // a valid halo row (only before local sequence 0; n_halo > 0
+            // implies a halo)
+            const Row<E, V> hv = load_row<E, V>(halo + (int64_t)(K - 1 - (s - tau)) * C + c0);
 #pragma unroll
-            for (int hi = 0; hi < K - 1; hi++)
-              if (hi == hrow) {
-#pragma unroll
-                for (int i = 0; i < V; i++) xt[j][i] = hr[hi].at(i);
-              }
+            for (int i = 0; i < V; i++) xt[j][i] = hv.at(i);
           }
         }
 #pragma unroll
         for (int i = 0; i < V; i++) {
-          float z = bv[i];
+          float z = bv.at(i);
 #pragma unroll
-          for (int j = 0; j < K; j++) z += wv[j][i] * xt[j][i];
+          for (int j = 0; j < K; j++) z += wv[j].at(i) * xt[j][i];
           const float sg = fast_sigmoid(z);
           const float d = gr.at(i) * sg * (1.f + z * (1.f - sg));
           dzw[K - 1][i] = d;
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
           for (int j = 0; j < K; j++) {
             if (t - j < ew[0]) {
 #pragma unroll
-              for (int i = 0; i < V; i++) out[i] += wv[j][i] * dzw[K - 1 - j][i];
+              for (int i = 0; i < V; i++) out[i] += wv[j].at(i) * dzw[K - 1 - j][i];
             }
           }
           store_row<E, V, true>(dx + tp * C + c0, out);
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
               const int rr = K - 1 - i - j;  // dz row of token s0 - i + K-1-j
               if (rr >= 0 && t0 + rr < e_first) {
 #pragma unroll
-                for (int v = 0; v < V; v++) out[v] += wv[j][v] * dzw[rr + 1][v];
+                for (int v = 0; v < V; v++) out[v] += wv[j].at(v) * dzw[rr + 1][v];
               }
             }
           }
