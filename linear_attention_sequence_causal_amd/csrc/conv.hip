@@ -474,10 +474,20 @@ int launch_fwd(const ConvArgs& a, void* y, hipStream_t stream) {
   return gdn::fail(GDN_EINVAL, "conv: K must be in [1, 8]");
 }
 
+// token splits of the backward grid: an upper bound, which sizes the workspace
 int bwd_splits(int64_t T) {
   const int64_t tile = (int64_t)kBwdRows * kRunsPerBlock;
   int64_t tiles = (T + tile - 1) / tile;
   return (int)(tiles < kBwdMaxSplits ? (tiles < 1 ? 1 : tiles) : kBwdMaxSplits);
+}
+
+// the splits a launch uses: no more blocks than run at once (two four-wave
+// blocks a CU at two waves a SIMD), since a second, partial round of these
+// long-running blocks would keep part of the chip idle
+int bwd_launch_splits(int64_t T, int cgroups) {
+  const int cap = bwd_splits(T);
+  const int64_t fit = 2 * (int64_t)gdn::device_cu_count() / (cgroups > 0 ? cgroups : 1);
+  return (int)(fit < 1 ? 1 : (fit < cap ? fit : cap));
 }
 
 template <typename E, int K>
@@ -489,11 +499,11 @@ int launch_bwd_k(const ConvArgs& a, const void* dy, void* dx, float* dw, float* 
                    (dhalo == nullptr || gdn::aligned16(dhalo));
   const int V = vec ? VE : 1;
   const int cvec = (a.C + V - 1) / V;
-  const int P = a.T > 0 ? bwd_splits(a.T) : 0;
-  float* part_w = (float*)ws;
-  float* part_b = part_w + (size_t)P * a.C * K;
   const int cgroups = (cvec + kLanes - 1) / kLanes;
   if (cgroups > 65535) return gdn::fail(GDN_EINVAL, "conv: C too large");
+  const int P = a.T > 0 ? bwd_launch_splits(a.T, cgroups) : 0;
+  float* part_w = (float*)ws;
+  float* part_b = part_w + (size_t)P * a.C * K;
   dim3 block(kLanes, kRunsPerBlock);
   dim3 grid(P, cgroups);
   if (P > 0) {
