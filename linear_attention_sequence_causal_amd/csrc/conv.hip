@@ -26,7 +26,7 @@ constexpr int kLanes = 64;         // blockDim.x: channel vectors per block
 constexpr int kFwdRows = 8;        // tokens per thread run, forward
 constexpr int kBwdRows = 16;       // tokens per thread run, backward
 constexpr int kBwdPrefetch = 3;    // rows in flight ahead of the one formed, backward
-constexpr int kBwdMaxSplits = 64;  // token splits of the backward grid (dw partial rows)
+constexpr int kBwdMaxSplits = 64;  // most token splits of the backward grid (dw partial rows)
 
 // V channels of one row: a packed 16-byte vector when V*sizeof(E) == 16
 // (bf16 stays two to a register), else V scalars.
@@ -196,10 +196,12 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 // for its own tokens, the halo gradient when the run holds the start of
 // sequence 0, and accumulates dw/dbias over its own tokens.  The rows stream
 // through windows of the last K x rows, dz rows and sequence ends: dx of
-// token t - (K-1) is formed once dz[t] is known.  A block loops
-// over token tiles with a fixed grid stride; its four runs' sums are added in
-// LDS and written as one partial row, and a second kernel adds the partial
-// rows in a fixed order (deterministic dw).
+// token t - (K-1) is formed once dz[t] is known, while the x and dy rows of
+// the next kBwdPrefetch tokens are already being read.  A block loops over
+// token tiles with a fixed grid stride (the grid is at most one round of
+// blocks); its four runs' sums are added in LDS and written as one partial
+// row, and a second kernel adds the partial rows in a fixed order
+// (deterministic dw).
 template <typename E, int K, int V>
 __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
     const E* __restrict__ x, const E* __restrict__ w, const E* __restrict__ bias,
