@@ -69,6 +69,28 @@ def test_conv_bwd_deterministic():
     assert torch.equal(r1[1], r2[1]) and torch.equal(r1[0], r2[0])
 
 
+def test_conv_bwd_many_tiles_ragged():
+    """Fewer blocks than token tiles (each block takes several, the last tile
+    ragged), a last channel group with one active lane (C = 8200), short and
+    empty sequences and a halo: dx, dw, dbias and dhalo on sampled channels,
+    the first and last ones included (channels are independent)."""
+    cu = [0, 5, 5, 3000, 3001, 9000, 12345]
+    C, K, hr = 8200, 4, 3
+    x, w, b, halo, dy = _case(11, cu, C, K, torch.bfloat16, bias=True, halo_rows=hr)
+    meta = gdn.make_meta("cuda", n_halo=hr)
+    dx, dw, db, dh = gdn.gdn_conv1d_silu_halo_bwd(x.cuda(), w.cuda(), cu_tensor(cu), dy.cuda(),
+                                                  bias=b.cuda(), halo=halo.cuda(), meta=meta)
+    rng = np.random.default_rng(3)
+    cols = np.sort(np.concatenate([np.arange(8), 8 + rng.choice(C - 16, 80, replace=False),
+                                   np.arange(C - 8, C)]))
+    rdx, rdw, rdb, rdh = capi.conv1d_silu_bwd(f64(x[:, cols]), f64(w[cols]), f64(b[cols]),
+                                              f64(halo[:, cols]), hr, cu, f64(dy[:, cols]))
+    assert_close("dx", f64(dx[:, cols]), rdx, torch.bfloat16)
+    assert_close("dw", f64(dw[cols]), rdw, torch.bfloat16)
+    assert_close("dbias", f64(db[cols]), rdb, torch.bfloat16)
+    assert_close("dhalo", f64(dh[:, cols]), rdh, torch.bfloat16)
+
+
 def test_conv_empty_batch():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
     w = torch.randn(64, 4, device="cuda").to(torch.bfloat16)
