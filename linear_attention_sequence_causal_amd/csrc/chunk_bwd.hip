@@ -694,61 +694,66 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 // ---------------------------------------------------------------------------
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void finalize_qk_kernel(BwdArgs a, int64_t units) {
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (u >= units) return;
-  const int64_t t = u / a.Hk;
-  const int qa = (int)(u % a.Hk);
+  // a lane owns 4 consecutive elements (one 16-byte read of each fp32 partial
+  // row), DK / 4 lanes a (token, q/k head) unit, 64 / (DK / 4) units a wave
+  constexpr int LPU = DK / 4, UPW = 64 / LPU;
+  static_assert(DK % 4 == 0 && LPU <= 64 && 64 % LPU == 0, "dk / 4 must divide 64");
+  const int lane = threadIdx.x & 63, d0 = 4 * (lane % LPU);
+  const int64_t u = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * UPW + lane / LPU;
+  // a whole lane group is in or out of range: no lane leaves before the
+  // group sums below
+  const bool valid = u < units;
+  const int64_t t = valid ? u / a.Hk : 0;
+  const int qa = valid ? (int)(u % a.Hk) : 0;
   const int grp = a.Hv / a.Hk;
-  // lane owns the PER consecutive elements d = PER lane .. + PER - 1
-  constexpr int PER = (DK + 63) / 64;
-  float dq[PER], dk[PER], q[PER], k[PER];
+  float dq[4], dk[4], q[4], k[4];
   float qs = 0.f, ks = 0.f, qd = 0.f, kd = 0.f;
-  const E* qp = (const E*)a.q + t * a.ld_qk + (int64_t)qa * DK;
-  const E* kp = (const E*)a.k + t * a.ld_qk + (int64_t)qa * DK;
+  const E* qp = (const E*)a.q + t * a.ld_qk + (int64_t)qa * DK + d0;
+  const E* kp = (const E*)a.k + t * a.ld_qk + (int64_t)qa * DK + d0;
 #pragma unroll
-  for (int e = 0; e < PER; e++) dq[e] = dk[e] = q[e] = k[e] = 0.f;
-  if (PER * lane < DK) {
+  for (int e = 0; e < 4; e++) dq[e] = dk[e] = q[e] = k[e] = 0.f;
+  if (valid) {
     for (int hh = qa * grp; hh < (qa + 1) * grp; hh++) {
-      const float* src = a.dqk + (t * a.Hv + hh) * 2 * DK + PER * lane;
+      const float* src = a.dqk + (t * a.Hv + hh) * 2 * DK + d0;
+      const floatx4 vq = *reinterpret_cast<const floatx4*>(src);
+      const floatx4 vk = *reinterpret_cast<const floatx4*>(src + DK);
 #pragma unroll
-      for (int e = 0; e < PER; e++) {
-        dq[e] += src[e];
-        dk[e] += src[DK + e];
+      for (int e = 0; e < 4; e++) {
+        dq[e] += vq[e];
+        dk[e] += vk[e];
       }
     }
 #pragma unroll
-    for (int e = 0; e < PER; e++) {
-      q[e] = to_f(qp[PER * lane + e]);
-      k[e] = to_f(kp[PER * lane + e]);
+    for (int e = 0; e < 4; e++) {
+      q[e] = to_f(qp[e]);
+      k[e] = to_f(kp[e]);
     }
   }
 #pragma unroll
-  for (int e = 0; e < PER; e++) {
+  for (int e = 0; e < 4; e++) {
     qs += q[e] * q[e];
     ks += k[e] * k[e];
     qd += q[e] * dq[e];
     kd += k[e] * dk[e];
   }
-  qs = group_sum<64>(qs);
-  ks = group_sum<64>(ks);
-  qd = group_sum<64>(qd);
-  kd = group_sum<64>(kd);
-  E* dqp = (E*)a.dq + t * a.ld_dqk + (int64_t)qa * DK;
-  E* dkp = (E*)a.dk + t * a.ld_dqk + (int64_t)qa * DK;
+  qs = group_sum<LPU>(qs);
+  ks = group_sum<LPU>(ks);
+  qd = group_sum<LPU>(qd);
+  kd = group_sum<LPU>(kd);
+  E* dqp = (E*)a.dq + t * a.ld_dqk + (int64_t)qa * DK + d0;
+  E* dkp = (E*)a.dk + t * a.ld_dqk + (int64_t)qa * DK + d0;
   const float rq = a.use_l2norm ? 1.f / sqrtf(qs + 1e-6f) : 1.f;
   const float rk = a.use_l2norm ? 1.f / sqrtf(ks + 1e-6f) : 1.f;
-  if (PER * lane < DK) {
+  if (valid) {
 #pragma unroll
-    for (int e = 0; e < PER; e++) {
-      const int d = PER * lane + e;
+    for (int e = 0; e < 4; e++) {
       float gq = a.scale * dq[e], gk = dk[e];
       if (a.use_l2norm) {
         gq = a.scale * rq * (dq[e] - q[e] * rq * rq * qd);
         gk = rk * (dk[e] - k[e] * rk * rk * kd);
       }
-      dqp[d] = from_f<E>(gq);
-      dkp[d] = from_f<E>(gk);
+      dqp[e] = from_f<E>(gq);
+      dkp[e] = from_f<E>(gk);
     }
   }
 }
@@ -817,7 +822,9 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
                      0, stream, b);
   if (int rc = gdn::check_launch("gdn_chunk_bwd(grad)")) return rc;
   const int64_t units = T * b.Hk;
-  hipLaunchKernelGGL((finalize_qk_kernel<E, DK>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0,
+  constexpr int64_t kUnitsPerBlock = 4 * (64 / (DK / 4));  // four waves
+  hipLaunchKernelGGL((finalize_qk_kernel<E, DK>),
+                     dim3((unsigned)((units + kUnitsPerBlock - 1) / kUnitsPerBlock)), dim3(256), 0,
                      stream, b, units);
   return gdn::check_launch("gdn_chunk_bwd(finalize)");
 }
