@@ -119,15 +119,19 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < K; j++) wv[j][i] = to_f(w[(c0 + i) * K + j]);
   }
+  // rows t0-(K-1) .. t0+R-1 (those inside [0, T)) go out before the sequence
+  // search, so the two latencies overlap
+  Row<E, V> xr[R + K - 1];
+#pragma unroll
+  for (int i = 0; i < R + K - 1; i++) {
+    const int64_t tau = t0 - (K - 1) + i;
+    xr[i] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
+  }
   int n = find_seq(cu, N, t0);
   int64_t s = cu[n], e = cu[n + 1];
 
   if (t0 - (K - 1) >= s && t0 + R <= e && t0 + R <= T) {
-    // the run and its K-1 predecessors lie inside one sequence: no masking;
-    // rows t0-(K-1) .. t0+R-1 are loaded up front
-    Row<E, V> xr[R + K - 1];
-#pragma unroll
-    for (int i = 0; i < R + K - 1; i++) xr[i] = load_row<E, V>(x + (t0 - (K - 1) + i) * C + c0);
+    // the run and its K-1 predecessors lie inside one sequence: no masking
 #pragma unroll
     for (int r = 0; r < R; r++) {
       float out[V];
