@@ -113,6 +113,17 @@ def main():
 
     local_buf = torch.empty(N + 1, dtype=torch.int32, device=dev)
     meta_buf = torch.empty(gdn.META_BYTES, dtype=torch.uint8, device=dev)
+    bwd_out = conv_out = ws_b = ws_cb = None
+    if spec.backward:
+        bwd_out = (torch.empty_like(x), torch.empty((T, Hv), dtype=torch.float32, device=dev),
+                   torch.empty((T, Hv), dtype=torch.float32, device=dev),
+                   torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev))
+        conv_out = (torch.empty_like(x), torch.empty((C, K), dtype=torch.float32, device=dev), None,
+                    None if halo is None else torch.empty_like(halo))
+        ws_b = torch.empty(max(gdn.chunk_workspace_size(T, N, Hk, Hv, dk, dv, dtype, bwd=True), 1),
+                           dtype=torch.uint8, device=dev)
+        ws_cb = torch.empty(max(gdn.conv_bwd_workspace_size(T, C, K), 1), dtype=torch.uint8,
+                            device=dev)
 
     def step(ev=None):
         def mark(i):
@@ -128,9 +139,11 @@ def main():
         gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht, ws=ws_f)
         mark(3)
         if spec.backward:
-            gr = gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht)
+            gr = gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht, ws=ws_b,
+                                   out=bwd_out)
             mark(4)
-            gdn.gdn_conv1d_silu_halo_bwd(x, w, local, gr["dy"], halo=halo, meta=m)
+            gdn.gdn_conv1d_silu_halo_bwd(x, w, local, gr["dy"], halo=halo, meta=m, out=conv_out,
+                                         ws=ws_cb)
             mark(5)
 
     names = ["localize", "conv_fwd", "chunk_fwd"] + (["chunk_bwd", "conv_bwd"] if spec.backward else [])
@@ -145,7 +158,8 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_call = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+    # per call: the median over the timed steps of its HIP-event interval
+    per_call = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, n in enumerate(names)}
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
@@ -220,32 +234,39 @@ def measured_traffic(call, workload):
 
 def cpu_baseline(spec, inp, sample_tokens):
     """The fp64 oracle (conv + token recurrence forward) on the first
-    `sample_tokens` tokens of the first sequence(s), all heads; tokens/s of
-    the sample."""
+    `sample_tokens` tokens of the workload, all heads: tokens/s of the whole
+    sample, with each leg (conv, recurrence) timed and its thread count
+    reported on its own."""
     from oracle import capi
     T = inp["T"]
+    thr = capi.max_threads()
+    rec_threads = min(thr, spec.Hv)  # the recurrence runs its (sequence, head) chains in parallel
     if sample_tokens <= 0:
         # ~7*dk*dv fp64 FLOP per token and head; aim for ~15 s at ~2.5 GFLOP/s/thread
-        thr = capi.max_threads()
         per_tok = 7.0 * spec.dk * spec.dv * spec.Hv
-        sample_tokens = int(min(T, max(256, 15 * 2.5e9 * min(thr, spec.Hv) / per_tok)))
+        sample_tokens = int(min(T, max(256, 15 * 2.5e9 * rec_threads / per_tok)))
     n = min(sample_tokens, T)
     x = inp["x"][:n].double().numpy()
     w = inp["w"].double().numpy()
     cu = [0, n]
     Hk, Hv, dk, dv = spec.Hk, spec.Hv, spec.dk, spec.dv
-    threads = min(capi.max_threads(), Hv)
     t0 = time.perf_counter()
     yv = capi.conv1d_silu(x, w, None, None, 0, cu)
+    t1 = time.perf_counter()
     q = yv[:, :Hk * dk].reshape(n, Hk, dk)
     k = yv[:, Hk * dk:2 * Hk * dk].reshape(n, Hk, dk)
     v = yv[:, 2 * Hk * dk:].reshape(n, Hv, dv)
     capi.gdn_fwd(q, k, v, inp["g"][:n].double().numpy(), inp["beta"][:n].double().numpy(), None,
-                 cu, dk ** -0.5, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                 cu, dk ** -0.5, nthreads=rec_threads)
+    t2 = time.perf_counter()
+    dt = t2 - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": max(thr, rec_threads), "kind": "oracle",
             "sample": "first %d tokens of the workload, all %d value heads, conv + gated delta "
                       "rule forward in fp64 (%.1f s)" % (n, Hv, dt),
+            "legs": {"conv": {"seconds": t1 - t0, "threads": thr,
+                              "tokens_per_s": n / (t1 - t0)},
+                     "recurrence": {"seconds": t2 - t1, "threads": rec_threads,
+                                    "tokens_per_s": n / (t2 - t1)}},
             "host_cpus": len(os.sched_getaffinity(0))}
 
 

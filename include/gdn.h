@@ -204,7 +204,11 @@ int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const void* v, in
  *   dv_      [T, Hv, dv] view with token stride ld_dv.
  *   dg, dbeta float32 [T, Hv];  dh0 float32 [N, Hv, dk, dv] or NULL.
  * Forward arguments as in gdn_chunk_fwd.  ws: gdn_chunk_workspace_size(...,1).
- * Errors: as gdn_chunk_fwd.
+ * Errors: the argument checks of gdn_chunk_fwd (GDN_EINVAL, GDN_EWORKSPACE);
+ * GDN_EINVAL also for null gradient pointers (d_o, dq, dk_, dv_, dg, dbeta
+ * when T > 0) and for ld_dqk < Hk*dk or ld_dv < Hv*dv.  The backward has
+ * kernels for fewer shapes than the forward: GDN_EUNSUPPORTED unless
+ * dk == dv and d is 64 or 128 (bfloat16) or 32 or 64 (float32).
  */
 int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
                   const float* g, const float* beta, const float* h0, const int32_t* cu_seqlens,

@@ -8,6 +8,9 @@
 namespace gdn {
 
 static thread_local char g_last_error[512] = "";
+static thread_local int g_seg_chunks = 0;
+
+int segment_chunks_override() { return g_seg_chunks; }
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -35,3 +38,13 @@ int device_cu_count() {
 }  // namespace gdn
 
 extern "C" const char* gdn_last_error(void) { return gdn::g_last_error; }
+
+// Test hook, deliberately absent from gdn.h: forces the segment length of the
+// chunk plans made on the calling thread (workspace queries included) to
+// `chunks` 64-token chunks; 0 restores the default plan.  Returns the
+// previous value.
+extern "C" int gdn_testing_set_segment_chunks(int chunks) {
+  const int prev = gdn::g_seg_chunks;
+  gdn::g_seg_chunks = chunks > 0 ? chunks : 0;
+  return prev;
+}

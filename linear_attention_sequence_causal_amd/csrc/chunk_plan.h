@@ -148,7 +148,7 @@ struct Plan {
 };
 
 // Segment lengths from the device size and the number of (sequence, head)
-// chains (GDN_SEG_CHUNKS overrides them for tuning).  rec_bytes: bytes of the
+// chains (a test hook on the calling thread can force them).  rec_bytes: bytes of the
 // prepared record per (chunk, value head), 0 when the state pass takes none.
 // first_out: the caller can run a sequence's first segment in the output mode
 // during the summary pass (from h0).
@@ -168,12 +168,12 @@ inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, 
   Plan p{};
   const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
   int64_t per = 1, first = 1, span = 0;
-  const char* env = getenv("GDN_SEG_CHUNKS");
+  const int forced = gdn::segment_chunks_override();
   p.first_out = false;
   const int64_t C = (T + 63) / 64 + N - 1;
   const int64_t cus = gdn::device_cu_count();
-  if (env && atoi(env) > 0) {
-    per = first = atoi(env);
+  if (forced > 0) {
+    per = first = forced;
   } else if (N == 1) {
     const int64_t B = cus / Hv > 1 ? cus / Hv : 1;
     if (first_out && B > 1) {

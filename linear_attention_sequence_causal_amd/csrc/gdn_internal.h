@@ -27,4 +27,10 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Segment length (in 64-token chunks) forced on the chunk plans of the
+// calling thread, 0 for the plan's own choice.  Set only through
+// gdn_testing_set_segment_chunks, which the public header does not declare:
+// it exists so that tests can run the segment machinery on small inputs.
+int segment_chunks_override();
+
 }  // namespace gdn

@@ -101,21 +101,36 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError("activations must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def _req(t, name, dtype=None, dev=None, contiguous=True):
+def _req(t, name, dtype=None, shape=None, contiguous=True, device=None):
+    """Checks a tensor argument (None passes): on the GPU, of ``dtype``, of
+    ``shape`` (a tuple, None entries free) and contiguous; ``device`` (a
+    tensor) must hold it on the same device."""
     if t is None:
         return
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device.device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device.device))
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(w is None or int(w) == d for w, d in zip(shape, t.shape))
+        if not ok:
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     if contiguous and not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
 
 
-def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
+def _workspace(ws, nbytes: int, like: torch.Tensor) -> Optional[torch.Tensor]:
+    """The caller's workspace if it is large enough (uint8, contiguous, on
+    the device of ``like``), else a new one; None when none is needed."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws is not None:
+        _req(ws, "ws", torch.uint8, (None,), device=like)
+        if ws.numel() >= nbytes:
+            return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
 
 
 # --------------------------------------------------------------------------
@@ -141,11 +156,12 @@ def gdn_localize_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, world_s
     device of cu_seqlens; no host synchronisation.  ``out`` may supply both
     buffers."""
     load_library()
-    _req(cu_seqlens, "cu_seqlens", torch.int32)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,))
     n = cu_seqlens.numel() - 1
     if out is not None:
         local, meta = out
-        _req(local, "local_cu_seqlens", torch.int32)
+        _req(local, "local_cu_seqlens", torch.int32, (None,), device=cu_seqlens)
+        _req(meta, "meta", torch.uint8, (None,), device=cu_seqlens)
         if local.numel() < n + 1 or meta.numel() < META_BYTES:
             raise ValueError("output buffers too small")
     else:
@@ -163,11 +179,15 @@ def gdn_localize_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, world_s
 def gdn_conv1d_silu_halo(x, w, cu_seqlens, bias=None, halo=None, meta=None, out=None):
     """y [T, C] = SiLU(causal depthwise conv(x)) with the halo rows of meta."""
     load_library()
+    _req(x, "x", shape=(None, None))
     T, C = x.shape
+    _req(w, "w", x.dtype, (C, None), device=x)
     K = w.shape[1]
-    for t, nm in ((x, "x"), (w, "w"), (bias, "bias"), (halo, "halo")):
-        _req(t, nm, x.dtype)
-    _req(cu_seqlens, "cu_seqlens", torch.int32)
+    _req(bias, "bias", x.dtype, (C,), device=x)
+    _req(halo, "halo", x.dtype, (K - 1, C), device=x)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=x)
+    _req(meta, "meta", torch.uint8, (META_BYTES,), device=x)
+    _req(out, "out", x.dtype, (T, C), device=x)
     y = torch.empty_like(x) if out is None else out
     rc = _lib.gdn_conv1d_silu_halo(_ptr(x), _ptr(w), _ptr(bias), _ptr(halo), _ptr(cu_seqlens),
                                    cu_seqlens.numel() - 1, T, C, K, _ptr(meta), _ptr(y), _dt(x),
@@ -176,20 +196,41 @@ def gdn_conv1d_silu_halo(x, w, cu_seqlens, bias=None, halo=None, meta=None, out=
     return y
 
 
-def gdn_conv1d_silu_halo_bwd(x, w, cu_seqlens, dy, bias=None, halo=None, meta=None):
-    """Returns dx [T,C] (act), dw [C,K] fp32, dbias [C] fp32 (or None),
-    dhalo [K-1,C] (act, or None)."""
+def conv_bwd_workspace_size(T, C, K) -> int:
     load_library()
+    return int(_lib.gdn_conv_bwd_workspace_size(T, C, K))
+
+
+def gdn_conv1d_silu_halo_bwd(x, w, cu_seqlens, dy, bias=None, halo=None, meta=None, out=None,
+                             ws=None):
+    """Returns dx [T,C] (act), dw [C,K] fp32, dbias [C] fp32 (or None),
+    dhalo [K-1,C] (act, or None).  ``out`` may supply (dx, dw, dbias, dhalo)
+    and ``ws`` the workspace, so that the call allocates nothing."""
+    load_library()
+    _req(x, "x", shape=(None, None))
     T, C = x.shape
+    _req(w, "w", x.dtype, (C, None), device=x)
     K = w.shape[1]
-    for t, nm in ((x, "x"), (w, "w"), (bias, "bias"), (halo, "halo"), (dy, "dy")):
-        _req(t, nm, x.dtype)
-    dx = torch.empty_like(x)
-    dw = torch.empty((C, K), dtype=torch.float32, device=x.device)
-    dbias = torch.empty(C, dtype=torch.float32, device=x.device) if bias is not None else None
-    dhalo = torch.empty((K - 1, C), dtype=x.dtype, device=x.device) if halo is not None else None
-    nbytes = _lib.gdn_conv_bwd_workspace_size(T, C, K)
-    ws = _ws(nbytes, x.device)
+    _req(bias, "bias", x.dtype, (C,), device=x)
+    _req(halo, "halo", x.dtype, (K - 1, C), device=x)
+    _req(dy, "dy", x.dtype, (T, C), device=x)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=x)
+    _req(meta, "meta", torch.uint8, (META_BYTES,), device=x)
+    if out is not None:
+        dx, dw, dbias, dhalo = out
+        if (dbias is None) != (bias is None) or (dhalo is None) != (halo is None):
+            raise ValueError("out must hold dbias / dhalo exactly when bias / halo are given")
+    else:
+        dx = torch.empty_like(x)
+        dw = torch.empty((C, K), dtype=torch.float32, device=x.device)
+        dbias = torch.empty(C, dtype=torch.float32, device=x.device) if bias is not None else None
+        dhalo = torch.empty((K - 1, C), dtype=x.dtype, device=x.device) if halo is not None else None
+    _req(dx, "dx", x.dtype, (T, C), device=x)
+    _req(dw, "dw", torch.float32, (C, K), device=x)
+    _req(dbias, "dbias", torch.float32, (C,), device=x)
+    _req(dhalo, "dhalo", x.dtype, (K - 1, C), device=x)
+    nbytes = conv_bwd_workspace_size(T, C, K)
+    ws = _workspace(ws, nbytes, x)
     rc = _lib.gdn_conv1d_silu_halo_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(halo), _ptr(cu_seqlens),
                                        cu_seqlens.numel() - 1, T, C, K, _ptr(meta), _ptr(dy),
                                        _ptr(dx), _ptr(dw), _ptr(dbias), _ptr(dhalo), _ptr(ws),
@@ -215,32 +256,35 @@ def chunk_workspace_size(T, N, Hk, Hv, dk, dv, dtype, bwd=False) -> int:
     return int(_lib.gdn_chunk_workspace_size(T, N, Hk, Hv, dk, dv, dt, int(bwd)))
 
 
+def _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv):
+    _req(y, "y", shape=(None, None))
+    T = y.shape[0]
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=y)
+    N = cu_seqlens.numel() - 1
+    _req(g, "g", torch.float32, (T, Hv), device=y)
+    _req(beta, "beta", torch.float32, (T, Hv), device=y)
+    _req(h0, "h0", torch.float32, (N, Hv, dk, dv), device=y)
+    return T, N
+
+
 def gdn_chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0=None, scale=None,
                   use_qk_l2norm=True, want_ht=True, out=None, ht_out=None, ws=None):
     """Chunked gated delta rule on the q/k/v channel blocks of y [T, C].
 
     Returns (o [T, Hv, dv] act, ht [N, Hv, dk, dv] fp32 or None)."""
     load_library()
-    T, C = y.shape
-    N = cu_seqlens.numel() - 1
-    _req(y, "y")
-    _req(g, "g", torch.float32)
-    _req(beta, "beta", torch.float32)
-    _req(h0, "h0", torch.float32)
-    _req(cu_seqlens, "cu_seqlens", torch.int32)
-    if g.shape != (T, Hv) or beta.shape != (T, Hv):
-        raise ValueError("g and beta must be [T, Hv]")
-    if h0 is not None and h0.shape != (N, Hv, dk, dv):
-        raise ValueError("h0 must be [N, Hv, dk, dv]")
+    T, N = _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv)
+    C = y.shape[1]
     q, k, v = _qkv_views(y, Hk, Hv, dk, dv)
+    _req(out, "out", y.dtype, (T, Hv, dv), device=y)
+    _req(ht_out, "ht_out", torch.float32, (N, Hv, dk, dv), device=y)
     o = out if out is not None else torch.empty((T, Hv, dv), dtype=y.dtype, device=y.device)
     ht = None
     if want_ht:
         ht = ht_out if ht_out is not None else torch.empty((N, Hv, dk, dv), dtype=torch.float32,
                                                            device=y.device)
     nbytes = chunk_workspace_size(T, N, Hk, Hv, dk, dv, y.dtype)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, y.device)
+    ws = _workspace(ws, nbytes, y)
     scale = dk ** -0.5 if scale is None else scale
     rc = _lib.gdn_chunk_fwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
                             _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
@@ -251,26 +295,31 @@ def gdn_chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0=None, scale=None,
 
 
 def gdn_chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0=None, dht=None, scale=None,
-                  use_qk_l2norm=True, ws=None):
+                  use_qk_l2norm=True, ws=None, out=None):
     """Reverse mode of gdn_chunk_fwd.  Returns dict with dy [T, C] (act: the
     gradients w.r.t. the q, k, v channel blocks of y), dg, dbeta [T, Hv] fp32
-    and dh0 [N, Hv, dk, dv] fp32."""
+    and dh0 [N, Hv, dk, dv] fp32.  ``out`` may supply (dy, dg, dbeta, dh0)
+    and ``ws`` the workspace, so that the call allocates nothing."""
     load_library()
-    T, C = y.shape
-    N = cu_seqlens.numel() - 1
-    _req(y, "y")
-    _req(d_o, "d_o", y.dtype)
-    _req(dht, "dht", torch.float32)
-    _req(h0, "h0", torch.float32)
+    T, N = _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv)
+    C = y.shape[1]
+    _req(d_o, "d_o", y.dtype, (T, Hv, dv), device=y)
+    _req(dht, "dht", torch.float32, (N, Hv, dk, dv), device=y)
     q, k, v = _qkv_views(y, Hk, Hv, dk, dv)
-    dy = torch.empty_like(y)
+    if out is not None:
+        dy, dg, dbeta, dh0 = out
+    else:
+        dy = torch.empty_like(y)
+        dg = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
+        dbeta = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
+        dh0 = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=y.device)
+    _req(dy, "dy", y.dtype, (T, C), device=y)
+    _req(dg, "dg", torch.float32, (T, Hv), device=y)
+    _req(dbeta, "dbeta", torch.float32, (T, Hv), device=y)
+    _req(dh0, "dh0", torch.float32, (N, Hv, dk, dv), device=y)
     dq, dk_, dv_ = _qkv_views(dy, Hk, Hv, dk, dv)
-    dg = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
-    dbeta = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
-    dh0 = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=y.device)
     nbytes = chunk_workspace_size(T, N, Hk, Hv, dk, dv, y.dtype, bwd=True)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, y.device)
+    ws = _workspace(ws, nbytes, y)
     scale = dk ** -0.5 if scale is None else scale
     rc = _lib.gdn_chunk_bwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
                             _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),

@@ -146,8 +146,11 @@ void oracle_conv1d_silu(const double *x, const double *w, const double *bias, co
                         int64_t n_halo, const int64_t *cu, int64_t N, int64_t T, int64_t C, int64_t K,
                         double *y, double *z_out) {
   (void)T;
+  /* every output element is independent: the tokens of a sequence are shared
+   * among the threads (rows stay contiguous in memory) */
   for (int64_t n = 0; n < N; n++) {
     int64_t s = cu[n], e = cu[n + 1];
+#pragma omp parallel for schedule(static)
     for (int64_t t = s; t < e; t++) {
       for (int64_t c = 0; c < C; c++) {
         double z = bias ? bias[c] : 0.0;
@@ -170,10 +173,14 @@ void oracle_conv1d_silu_bwd(const double *x, const double *w, const double *bias
   memset(dw, 0, sizeof(double) * (size_t)(C * K));
   if (dbias) memset(dbias, 0, sizeof(double) * (size_t)C);
   if (dhalo && K > 1) memset(dhalo, 0, sizeof(double) * (size_t)((K - 1) * C));
+  /* channels are independent (each writes its own column of dx, dhalo and
+   * its own dw row): they are shared among the threads */
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < C; c++) {
   for (int64_t n = 0; n < N; n++) {
     int64_t s = cu[n], e = cu[n + 1];
     for (int64_t t = s; t < e; t++) {
-      for (int64_t c = 0; c < C; c++) {
+      {
         double z = bias ? bias[c] : 0.0;
         for (int64_t j = 0; j < K; j++)
           z += w[c * K + j] * xtilde(x, halo, n_halo, n, s, t - (K - 1) + j, c, C, K);
@@ -193,6 +200,7 @@ void oracle_conv1d_silu_bwd(const double *x, const double *w, const double *bias
         }
       }
     }
+  }
   }
 }
 

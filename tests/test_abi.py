@@ -134,3 +134,53 @@ def test_workspace_size_edge_lengths(lib, T, N):
             assert size >= 0
             if T > 0:
                 assert size > 0
+
+
+def _chunk_bwd(lib, **kw):
+    f = ctypes.c_void_p(0x1000)
+    a = dict(q=f, k=f, ld_qk=6144, v=f, ld_v=6144, g=f, beta=f, h0=None, cu=f, N=1, T=64, Hk=16,
+             Hv=16, dk=128, dv=128, scale=0.1, l2=1, do=f, dht=None, dq=f, dk_=f, ld_dqk=6144,
+             dv_=f, ld_dv=6144, dg=f, dbeta=f, dh0=None, ws=f, ws_bytes=1 << 40, dt=1)
+    a.update(kw)
+    return lib.gdn_chunk_bwd(a["q"], a["k"], a["ld_qk"], a["v"], a["ld_v"], a["g"], a["beta"],
+                             a["h0"], a["cu"], a["N"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                             a["scale"], a["l2"], a["do"], a["dht"], a["dq"], a["dk_"], a["ld_dqk"],
+                             a["dv_"], a["ld_dv"], a["dg"], a["dbeta"], a["dh0"], a["ws"],
+                             a["ws_bytes"], a["dt"], None)
+
+
+def test_chunk_bwd_rejects_shapes_it_has_no_kernel_for(lib):
+    """The backward's kernels cover dk == dv with d in {64, 128} (bfloat16)
+    or {32, 64} (float32); shapes the forward accepts beyond that are
+    reported as unsupported, not run."""
+    assert _chunk_bwd(lib, dk=128, dv=64, ld_qk=4096, ld_v=4096) == gdn.GDN_EUNSUPPORTED
+    assert _chunk_bwd(lib, dk=64, dv=128, ld_qk=2048, ld_v=4096) == gdn.GDN_EUNSUPPORTED
+    assert _chunk_bwd(lib, dk=32, dv=32, ld_qk=1024, ld_v=1024) == gdn.GDN_EUNSUPPORTED  # bf16 d=32
+    assert b"dk == dv" in lib.gdn_last_error()
+    assert _chunk_bwd(lib, dk=128, dv=128, dt=0) == gdn.GDN_EUNSUPPORTED  # fp32 d=128
+    assert _chunk_bwd(lib, dq=None) == gdn.GDN_EINVAL
+    assert _chunk_bwd(lib, dg=None) == gdn.GDN_EINVAL
+    assert _chunk_bwd(lib, ld_dqk=100) == gdn.GDN_EINVAL
+    assert _chunk_bwd(lib, ws_bytes=16) == gdn.GDN_EWORKSPACE
+
+
+def test_segment_hook_is_thread_local_and_not_public(lib):
+    """Forcing the segment length is a test hook that the public header does
+    not declare; it changes only the calling thread's plans and is undone by
+    setting 0."""
+    import threading
+    assert "gdn_testing_set_segment_chunks" not in declared_functions()
+    fn = lib.gdn_testing_set_segment_chunks
+    fn.argtypes = [ctypes.c_int]
+    fn.restype = ctypes.c_int
+    base = lib.gdn_chunk_workspace_size(4096, 1, 2, 4, 128, 128, 1, 0)
+    assert fn(1) == 0
+    forced = lib.gdn_chunk_workspace_size(4096, 1, 2, 4, 128, 128, 1, 0)
+    other = []
+    t = threading.Thread(target=lambda: other.append(
+        lib.gdn_chunk_workspace_size(4096, 1, 2, 4, 128, 128, 1, 0)))
+    t.start()
+    t.join()
+    assert fn(0) == 1
+    assert forced != base and other == [base]
+    assert lib.gdn_chunk_workspace_size(4096, 1, 2, 4, 128, 128, 1, 0) == base

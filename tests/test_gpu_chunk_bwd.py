@@ -6,7 +6,6 @@ over the value heads of a q/k head), random initial state and final-state
 gradient, l2norm on/off, the segmented state pass.  Workloads: the float32
 single sequence and the 4 x 4096 bfloat16 batch end to end (conv forward,
 chunk forward, chunk backward, conv backward) at full size."""
-import os
 
 import numpy as np
 import pytest
@@ -14,7 +13,7 @@ import torch
 
 from linear_attention_sequence_causal_amd import gdn, workloads
 from oracle import capi
-from tests.helpers import TOL, assert_close, cu_tensor, f64, split_qkv
+from tests.helpers import forced_segments, TOL, assert_close, cu_tensor, f64, split_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -36,15 +35,11 @@ def _inputs(seed, lengths, Hk, Hv, d, dtype, h0=True):
 
 def _check_bwd(y, g, beta, h0, do, dht, cu, Hk, Hv, d, use_l2norm=True, seg=None):
     dtype = y.dtype
-    if seg is not None:
-        os.environ["GDN_SEG_CHUNKS"] = str(seg)
-    try:
+    with forced_segments(seg or 0):
         r = gdn.gdn_chunk_bwd(y.cuda(), g.cuda(), beta.cuda(), cu_tensor(cu), Hk, Hv, d, d,
                               do.cuda(), h0=None if h0 is None else h0.cuda(),
                               dht=None if dht is None else dht.cuda(), use_qk_l2norm=use_l2norm)
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("GDN_SEG_CHUNKS", None)
     q, k, v = split_qkv(f64(y), Hk, Hv, d, d)
     ref = capi.gdn_bwd(q, k, v, f64(g), f64(beta), f64(h0), cu, d ** -0.5, f64(do), f64(dht),
                        use_l2norm)
