@@ -9,6 +9,8 @@
  *             _causal_conv1d_with_cp_halo, _l2norm_torch,
  *             _prepare_gdn_chunks_for_summary, _run_prepared_gdn_chunks,
  *             _RecvInitialStateP2PFunction, _SendFinalStateP2PFunction,
+ *             _compute_gdn_state_summary_from_prepared,
+ *             _merge_gdn_prefix_state_summaries_torch, _apply_gdn_state_summary,
  *             LinearAttentionP2PCPWrapper.forward (the data flow conv ->
  *             split -> GQA expansion -> gated delta rule).
  *
@@ -216,6 +218,54 @@ int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v, in
                   int use_qk_l2norm, const void* d_o, const float* dht, void* dq, void* dk_,
                   int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta, float* dh0,
                   void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace gdn_chunk_summary needs for these sizes. */
+size_t gdn_chunk_summary_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                                        int32_t dv, gdn_dtype dt);
+
+/*
+ * Affine state summary of every local sequence of a shard.  [HP-CP]
+ * _compute_gdn_state_summary_from_prepared: the gated delta rule of
+ * gdn_chunk_fwd is affine in its initial state, so for each sequence n and
+ * value head h the state leaving it is
+ *     S_out = M[n,h] S_in + E[n,h],
+ * M [dk, dk] the product of the chunk transitions e^{G_C} I - (kh o
+ * e^{G_C - G})^T w and E [dk, dv] the state reached from S_in = 0.  This is
+ * what a rank computes before it knows its carried-in state (the page's P2P
+ * wavefront and all-gather modes exchange it).  An empty sequence gives
+ * M = I, E = 0.  q plays no part; scale is irrelevant.
+ *
+ *   k, v, g, beta, cu_seqlens, N, T, Hk, Hv, dk, dv, use_qk_l2norm, dt: as
+ *            in gdn_chunk_fwd (k with token stride ld_k).
+ *   M        float32 [N, Hv, dk, dk] or NULL (not written).
+ *   E        float32 [N, Hv, dk, dv] or NULL (not written).
+ *   ws       gdn_chunk_summary_workspace_size(...) bytes, 256-byte aligned.
+ * Errors: as gdn_chunk_fwd (shapes, strides, dtypes, workspace); GDN_EINVAL
+ * also for M or E not 16-byte aligned.
+ */
+int gdn_chunk_summary(const void* k, int64_t ld_k, const void* v, int64_t ld_v, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, int32_t N, int64_t T,
+                      int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, int use_qk_l2norm, float* M,
+                      float* E, void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/*
+ * Prefix merge of affine summaries.  [HP-CP]
+ * _merge_gdn_prefix_state_summaries_torch (fold the summaries of the ranks
+ * before this one from a zero state) and _apply_gdn_state_summary (one
+ * summary applied to a received state): for every state slot s (e.g. a
+ * (sequence, value head) pair),
+ *     h = h_in[s] (zero if h_in is NULL);  h <- M[r,s] h + E[r,s] for r = 0 .. R-1;
+ *     h_out[s] = h.
+ *
+ *   M      float32 [R, S, dk, dk];  E float32 [R, S, dk, dv]  (R >= 0).
+ *   h_in   float32 [S, dk, dv] or NULL;  h_out float32 [S, dk, dv] (may be
+ *          h_in: each workgroup reads its columns before it writes them).
+ * fp32 arithmetic (MFMA).  Errors: GDN_EINVAL for negative R or S, null or
+ * non-16-byte-aligned pointers; GDN_EUNSUPPORTED unless dk, dv in
+ * {32, 64, 128}.
+ */
+int gdn_merge_summaries(const float* M, const float* E, int32_t R, int32_t S, int32_t dk,
+                        int32_t dv, const float* h_in, float* h_out, hipStream_t stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* gdn_last_error(void);

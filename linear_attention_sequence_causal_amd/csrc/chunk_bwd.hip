@@ -36,13 +36,6 @@
 
 using namespace gdn_chunk;
 
-namespace gdn {
-int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, const void* v,
-                   int64_t ld_v, const float* g, const float* beta, const int32_t* cu, int32_t N,
-                   int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
-size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
-size_t chunk_rec_bytes(gdn_dtype dt);
-}  // namespace gdn
 
 namespace {
 

@@ -74,6 +74,7 @@ struct LoopArgs {
   int seg_cap;       // capacity of the segment table
   int first_done;    // the output of every sequence's first segment is already written
   int seg_base, seg_span;  // the state-pass grid covers segments seg_base .. + seg_span - 1
+  int summary_all;         // kSummary: summarise a sequence's last segment too
 };
 
 // LDS of the chunk loop (one chunk of one head at a time; rows padded by
@@ -232,7 +233,7 @@ void chunk_loop_kernel(LoopArgs a) {
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
-  if (MODE == kSummary && (ent.w & kLast)) return;
+  if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
   const int n = ent.x;
   const int64_t tb = ent.y, te = ent.z;
   const int Hv = a.Hv;
@@ -1016,7 +1017,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   const int seg = a.seg_base + grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
   if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
-  if (MODE == kSummary && (ent.w & kLast)) return;
+  if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
   if (MODE == kOut && a.first_done && (ent.w & kFirst)) return;
   ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent, false);
 }
@@ -1197,6 +1198,143 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   a.seg_span = first_out ? (int)pl.seg_span : (int)pl.seg_cap;
   launch_loop<E, DK, DV, FINAL>(a, pl, stream);
   return gdn::check_launch("chunk loop");
+}
+
+// Composition of a sequence's segment summaries into the summary of the whole
+// sequence (hyper-parallel _compute_gdn_state_summary_from_prepared, folded
+// over segments instead of chunks): per (sequence, head, 16 columns of
+// [M | E]), X <- M_p X + [0 | E_p] over its segments from X = [I | 0]; an
+// empty sequence gives [I | 0].  fp32 MFMA tiles as in seg_scan_kernel.
+template <int DK, int DV>
+__global__ __launch_bounds__(DK * 2) void seg_compose_kernel(const float* __restrict__ seg_state,
+                                                             const int32_t* __restrict__ seq_off,
+                                                             const int32_t* __restrict__ seq_nseg,
+                                                             int Hv, float* __restrict__ Mout,
+                                                             float* __restrict__ Eout) {
+  typedef Mfma<float> M;
+  constexpr int LDX = DK + DV;
+  constexpr int NKT = DK / 16;
+  static_assert(DK % 32 == 0, "two row tiles per wave");
+  const int n = blockIdx.x, h = blockIdx.y, cb = blockIdx.z * 16;
+  const bool ecol = cb >= DK;  // the block holds columns of E
+  float* dst = ecol ? Eout : Mout;
+  if (!dst) return;
+  const int nseg = seq_nseg[n], off = seq_off[n];
+  __shared__ float hs[DK][16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g4 = lane >> 4, ln = lane & 15;
+  for (int i = t; i < DK * 16; i += DK * 2) {
+    const int r = i >> 4, col = i & 15;
+    hs[r][col] = (!ecol && r == cb + col) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  for (int p = 0; p < nseg; p++) {
+    const float* X = seg_state + ((int64_t)(off + p) * Hv + h) * DK * LDX;
+    floatx4 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int mt = 2 * w + i;
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = ecol ? X[(16 * mt + 4 * g4 + j) * LDX + cb + ln] : 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; kt++)
+        M::mma(acc[i], M::load(X, LDX, 16 * mt, 16 * kt, lane), M::load_col(&hs[0][0], 16, 0, 16 * kt, lane));
+    }
+    __syncthreads();  // every wave has read the running summary
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) hs[16 * (2 * w + i) + 4 * g4 + j][ln] = acc[i][j];
+    __syncthreads();
+  }
+  const int ld = ecol ? DV : DK, c0 = ecol ? cb - DK : cb;
+  float* out = dst + ((int64_t)n * Hv + h) * DK * ld;
+  for (int i = t; i < DK * 16; i += DK * 2) {
+    const int r = i >> 4, col = i & 15;
+    out[r * ld + c0 + col] = hs[r][col];
+  }
+}
+
+// Prefix merge of affine summaries (hyper-parallel
+// _merge_gdn_prefix_state_summaries_torch, and _apply_gdn_state_summary for
+// one summary): per (state slot, 16 columns), h <- M_r h + E_r for
+// r = 0 .. R-1 from h_in (zero if null).  M [R][S][DK][DK], E [R][S][DK][DV].
+template <int DK, int DV>
+__global__ __launch_bounds__(DK * 2) void merge_summaries_kernel(const float* __restrict__ Ms,
+                                                                 const float* __restrict__ Es,
+                                                                 int R, int S,
+                                                                 const float* __restrict__ h_in,
+                                                                 float* __restrict__ h_out) {
+  typedef Mfma<float> M;
+  constexpr int NKT = DK / 16;
+  static_assert(DK % 32 == 0, "two row tiles per wave");
+  const int sl = blockIdx.x, cb = blockIdx.y * 16;
+  __shared__ float hs[DK][16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g4 = lane >> 4, ln = lane & 15;
+  for (int i = t; i < DK * 16; i += DK * 2) {
+    const int r = i >> 4, col = i & 15;
+    hs[r][col] = h_in ? h_in[((int64_t)sl * DK + r) * DV + cb + col] : 0.f;
+  }
+  __syncthreads();
+  for (int p = 0; p < R; p++) {
+    const float* Mp = Ms + ((int64_t)p * S + sl) * DK * DK;
+    const float* Ep = Es + ((int64_t)p * S + sl) * DK * DV;
+    floatx4 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int mt = 2 * w + i;
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = Ep[(16 * mt + 4 * g4 + j) * DV + cb + ln];
+#pragma unroll
+      for (int kt = 0; kt < NKT; kt++)
+        M::mma(acc[i], M::load(Mp, DK, 16 * mt, 16 * kt, lane), M::load_col(&hs[0][0], 16, 0, 16 * kt, lane));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) hs[16 * (2 * w + i) + 4 * g4 + j][ln] = acc[i][j];
+    __syncthreads();
+  }
+  for (int i = t; i < DK * 16; i += DK * 2) {
+    const int r = i >> 4, col = i & 15;
+    h_out[((int64_t)sl * DK + r) * DV + cb + col] = hs[r][col];
+  }
+}
+
+// A shard's affine summary per local sequence: plan, prep (bf16), the
+// summary pass over every segment (last ones included), then the
+// composition over each sequence's segments into M and E.
+template <typename E, int DK, int DV>
+int run_summary(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl, char* ws,
+                float* Mout, float* Eout, hipStream_t stream) {
+  constexpr bool PREP = uses_prep<E, DK, DV, kSummary>();
+  PlanPtrs pp = pl.ptrs(ws, PREP);
+  a.seg_cap = (int)pl.seg_cap;
+  a.seg_table = pp.table;
+  a.counts = pp.counts;
+  a.seg_chunk0 = pp.seg_chunk0;
+  a.seg_state = reinterpret_cast<float*>(ws + pl.off_state);
+  a.seg_init = nullptr;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, (int)pl.seg_first, (int)pl.seg_len,
+                     (int)pl.seg_cap, (int)pl.chunk_cap, pp);
+  if (int rc = gdn::check_launch("chunk plan")) return rc;
+  if constexpr (PREP) {
+    char* rec = ws + pl.off_rec;
+    a.rec = rec;
+    PrepArgs pa{a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab, pp.counts, rec};
+    if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
+  }
+  a.first_done = 0;
+  a.seg_base = 0;
+  a.seg_span = (int)pl.seg_span;
+  a.summary_all = 1;
+  launch_loop<E, DK, DV, kSummary>(a, pl, stream);
+  if (int rc = gdn::check_launch("chunk summary")) return rc;
+  hipLaunchKernelGGL((seg_compose_kernel<DK, DV>), dim3(N, a.Hv, (DK + DV) / 16), dim3(DK * 2), 0,
+                     stream, a.seg_state, pp.seq_off, pp.seq_nseg, a.Hv, Mout, Eout);
+  return gdn::check_launch("chunk summary compose");
 }
 
 }  // namespace

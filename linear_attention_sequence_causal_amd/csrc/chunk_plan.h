@@ -151,7 +151,8 @@ struct Plan {
 // chains (a test hook on the calling thread can force them).  rec_bytes: bytes of the
 // prepared record per (chunk, value head), 0 when the state pass takes none.
 // first_out: the caller can run a sequence's first segment in the output mode
-// during the summary pass (from h0).
+// during the summary pass (from h0).  summaries: the plan of a shard summary,
+// which keeps every segment's [M | E].
 //
 // A state-pass workgroup takes most of a CU's LDS, so one runs per CU.  Each
 // XCD hands its share of a grid (ids x mod 8 go to XCD x) to its CUs in a
@@ -164,7 +165,7 @@ struct Plan {
 // output pass segments 1 .. B, B = CUs / Hv.
 constexpr int kFirstRatioNum = 77, kFirstRatioDen = 100;
 inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes,
-                      bool first_out = false) {
+                      bool first_out = false, bool summaries = false) {
   Plan p{};
   const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
   int64_t per = 1, first = 1, span = 0;
@@ -223,7 +224,8 @@ inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, 
   p.off_seq_nseg = take(4 * (size_t)N);
   p.off_seq_chunk_off = take(4 * (size_t)N);
   p.off_chunk_tab = take(sizeof(int4) * (size_t)p.chunk_cap);
-  p.off_state = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * (dk + dv) : 0);
+  // summaries: every segment's [M | E] is kept (a shard's summary), split or not
+  p.off_state = take(p.split || summaries ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * (dk + dv) : 0);
   p.off_init = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * dv : 0);
   p.off_rec = take(rec_bytes * (size_t)p.chunk_cap * Hv);
   p.end = o;

@@ -35,8 +35,11 @@ META_BYTES = struct.calcsize(META_FORMAT)
 ENTRY_POINTS = (
     "gdn_localize_cu_seqlens", "gdn_conv1d_silu_halo", "gdn_conv_bwd_workspace_size",
     "gdn_conv1d_silu_halo_bwd", "gdn_chunk_workspace_size", "gdn_chunk_fwd", "gdn_chunk_bwd",
+    "gdn_chunk_summary_workspace_size", "gdn_chunk_summary", "gdn_merge_summaries",
     "gdn_last_error",
 )
+_SIZE_QUERIES = ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size",
+                 "gdn_chunk_summary_workspace_size")
 
 
 class GdnError(RuntimeError):
@@ -71,9 +74,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   INT, P, P, P, SZ, INT, P]
     lib.gdn_chunk_bwd.argtypes = [P, P, I64, P, I64, P, P, P, P, I32, I64, I32, I32, I32, I32, F,
                                   INT, P, P, P, P, I64, P, I64, P, P, P, P, SZ, INT, P]
+    lib.gdn_chunk_summary_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, INT]
+    lib.gdn_chunk_summary_workspace_size.restype = SZ
+    lib.gdn_chunk_summary.argtypes = [P, I64, P, I64, P, P, P, I32, I64, I32, I32, I32, I32, INT,
+                                      P, P, P, SZ, INT, P]
+    lib.gdn_merge_summaries.argtypes = [P, P, I32, I32, I32, I32, P, P, P]
     lib.gdn_last_error.restype = ctypes.c_char_p
     for name in ENTRY_POINTS:
-        if name not in ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size", "gdn_last_error"):
+        if name not in _SIZE_QUERIES + ("gdn_last_error",):
             getattr(lib, name).restype = INT
     if path == LIB_PATH:
         _lib = lib
@@ -328,3 +336,51 @@ def gdn_chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0=None, dht=None
                             _dt(y), _stream())
     _check("gdn_chunk_bwd", rc)
     return dict(dy=dy, dg=dg, dbeta=dbeta, dh0=dh0)
+
+
+# --------------------------------------------------------------------------
+# affine state summaries (a shard's [M | E]) and their prefix merge
+# --------------------------------------------------------------------------
+def gdn_chunk_summary(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, use_qk_l2norm=True, want_m=True,
+                      want_e=True, ws=None):
+    """Per local sequence n and value head h: S_out = M S_in + E.  Returns
+    (M [N, Hv, dk, dk] fp32 or None, E [N, Hv, dk, dv] fp32 or None)."""
+    load_library()
+    T, N = _chunk_common(y, g, beta, cu_seqlens, None, Hk, Hv, dk, dv)
+    C = y.shape[1]
+    _, k, v = _qkv_views(y, Hk, Hv, dk, dv)
+    M = torch.empty((N, Hv, dk, dk), dtype=torch.float32, device=y.device) if want_m else None
+    E = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=y.device) if want_e else None
+    dt = GDN_BF16 if y.dtype == torch.bfloat16 else GDN_F32
+    nbytes = int(_lib.gdn_chunk_summary_workspace_size(T, N, Hk, Hv, dk, dv, dt))
+    ws = _workspace(ws, nbytes, y)
+    rc = _lib.gdn_chunk_summary(_ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(cu_seqlens), N,
+                                T, Hk, Hv, dk, dv, int(bool(use_qk_l2norm)), _ptr(M), _ptr(E),
+                                _ptr(ws), nbytes, _dt(y), _stream())
+    _check("gdn_chunk_summary", rc)
+    return M, E
+
+
+def gdn_merge_summaries(M, E, h_in=None, out=None):
+    """M [R, ..., dk, dk], E [R, ..., dk, dv] (the same middle dimensions, the
+    state slots); h = h_in (or zero), then h <- M[r] h + E[r] for r < R.
+    Returns h [..., dk, dv] fp32."""
+    load_library()
+    _req(M, "M", torch.float32)
+    if M.dim() < 3:
+        raise ValueError("M must be [R, ..., dk, dk]")
+    R, dk = M.shape[0], M.shape[-1]
+    slots = tuple(M.shape[1:-2])
+    _req(M, "M", torch.float32, (R,) + slots + (dk, dk))
+    _req(E, "E", torch.float32, (R,) + slots + (dk, None), device=M)
+    dv = E.shape[-1]
+    _req(h_in, "h_in", torch.float32, slots + (dk, dv), device=M)
+    h = out if out is not None else torch.empty(slots + (dk, dv), dtype=torch.float32,
+                                                device=M.device)
+    _req(h, "out", torch.float32, slots + (dk, dv), device=M)
+    S = 1
+    for d in slots:
+        S *= int(d)
+    rc = _lib.gdn_merge_summaries(_ptr(M), _ptr(E), R, S, dk, dv, _ptr(h_in), _ptr(h), _stream())
+    _check("gdn_merge_summaries", rc)
+    return h

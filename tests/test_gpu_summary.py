@@ -1,0 +1,161 @@
+"""GPU affine state summaries (gdn_chunk_summary) and their prefix merge
+(gdn_merge_summaries) against the oracle.
+
+hyper-parallel "linear_attention_context_parallel.py":
+_compute_gdn_state_summary_from_prepared gives S_out = M S_in + E per
+sequence; the oracle's M is its token recurrence run from S_in = I with v = 0
+(then S_out = M), its E the recurrence from S_in = 0.
+_merge_gdn_prefix_state_summaries_torch / _apply_gdn_state_summary fold
+summaries from a state; the oracle is the page's fold written out in numpy
+(oracle/ref.py merge_prefix_summaries), and, composed, the summaries of the
+shards of a sequence must reproduce the final state of the unsplit run."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_sequence_causal_amd import gdn, workloads
+from oracle import capi, ref
+from tests.helpers import assert_close, cu_tensor, f64, forced_segments, split_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, lengths, Hk, Hv, dk, dv, dtype, g_scale=1.0):
+    gen = torch.Generator().manual_seed(seed)
+    T = sum(lengths)
+    C = 2 * Hk * dk + Hv * dv
+    y = torch.nn.functional.silu(torch.randn(T, C, generator=gen)).to(dtype)
+    beta = torch.sigmoid(torch.randn(T, Hv, generator=gen))
+    g = -torch.nn.functional.softplus(torch.randn(T, Hv, generator=gen)) * g_scale
+    cu = [0] + list(np.cumsum(lengths))
+    return y, g, beta, cu
+
+
+def oracle_summary(y, g, beta, cu, Hk, Hv, dk, dv):
+    """M from the recurrence started at I with v = 0, E from 0 with v."""
+    q, k, v = split_qkv(f64(y), Hk, Hv, dk, dv)
+    N = len(cu) - 1
+    eye = np.broadcast_to(np.eye(dk), (N, Hv, dk, dk)).copy()
+    _, M = capi.gdn_fwd(k, k, np.zeros((v.shape[0], Hv, dk)), f64(g), f64(beta), eye, cu, 1.0)
+    _, E = capi.gdn_fwd(k, k, v, f64(g), f64(beta), None, cu, 1.0)
+    return M, E
+
+
+def _check(y, g, beta, cu, Hk, Hv, dk, dv, seg=None):
+    dtype = y.dtype
+    with forced_segments(seg or 0):
+        M, E = gdn.gdn_chunk_summary(y.cuda(), g.cuda(), beta.cuda(), cu_tensor(cu), Hk, Hv, dk, dv)
+        torch.cuda.synchronize()
+    rM, rE = oracle_summary(y, g, beta, cu, Hk, Hv, dk, dv)
+    # per sequence: the transitions of long sequences are small next to the
+    # identity of an empty one
+    for n in range(len(cu) - 1):
+        assert_close("M[%d]" % n, f64(M[n]), rM[n], dtype)
+        assert_close("E[%d]" % n, f64(E[n]), rE[n], dtype)
+
+
+SMALL = [
+    # lengths, Hk, Hv, dk, dv, dtype, g_scale
+    ([256], 2, 2, 32, 32, torch.float32, 1.0),
+    ([1, 63, 64, 65, 0, 200], 1, 2, 32, 32, torch.float32, 0.1),
+    ([130, 70], 2, 2, 64, 64, torch.float32, 0.1),
+    ([300, 0, 2600], 2, 4, 128, 128, torch.bfloat16, 0.02),
+    ([1, 129, 700], 2, 2, 128, 64, torch.bfloat16, 0.05),
+    ([190, 65], 1, 2, 64, 128, torch.bfloat16, 0.05),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_summary_small(ci):
+    lengths, Hk, Hv, dk, dv, dtype, gs = SMALL[ci]
+    print("case", SMALL[ci], flush=True)
+    y, g, beta, cu = _inputs(70 + ci, lengths, Hk, Hv, dk, dv, dtype, gs)
+    _check(y, g, beta, cu, Hk, Hv, dk, dv)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 5])
+def test_summary_segments(seg):
+    """Sequences cut into segments of `seg` chunks: each segment's [M | E]
+    is composed over the sequence's segments."""
+    y, g, beta, cu = _inputs(80 + seg, [1, 64, 650, 0, 333], 2, 4, 128, 128, torch.bfloat16, 0.02)
+    _check(y, g, beta, cu, 2, 4, 128, 128, seg=seg)
+
+
+def test_summary_sharded_workload():
+    """The summary a rank of the sharded workload sends: its shard's local
+    sequences (localised cu_seqlens), every head, at full size."""
+    spec = workloads.config("shard3of8_32k_h16_d128_bf16")
+    inp = workloads.make(spec)
+    cu_glob = torch.tensor(inp["cu_global"], dtype=torch.int32, device="cuda")
+    local, meta = gdn.gdn_localize_cu_seqlens(cu_glob, int(inp["cu_global"][-1]), spec.world_size,
+                                              spec.rank, spec.K)
+    n = gdn.read_meta(meta)["num_local_seqs"]
+    lc = local[:n + 1].contiguous()
+    halo = inp["halo"].cuda()
+    y = gdn.gdn_conv1d_silu_halo(inp["x"].cuda(), inp["w"].cuda(), lc, halo=halo, meta=meta)
+    g = inp["g"] * 0.05
+    _check(y.cpu(), g, inp["beta"], lc.cpu().numpy(), spec.Hk, spec.Hv, spec.dk, spec.dv)
+
+
+@pytest.mark.parametrize("R", [0, 1, 5])
+@pytest.mark.parametrize("with_h", [False, True])
+def test_merge_matches_page_fold(R, with_h):
+    rng = np.random.default_rng(R + 10 * with_h)
+    d, dv = 128, 64
+    S = (2, 3)
+    M = rng.standard_normal((R,) + S + (d, d)) / np.sqrt(d)
+    E = rng.standard_normal((R,) + S + (d, dv))
+    h_in = rng.standard_normal(S + (d, dv)) if with_h else None
+    Mt = torch.tensor(M, dtype=torch.float32)
+    Et = torch.tensor(E, dtype=torch.float32)
+    ht = None if h_in is None else torch.tensor(h_in, dtype=torch.float32)
+    out = gdn.gdn_merge_summaries(Mt.cuda(), Et.cuda(), None if ht is None else ht.cuda())
+    torch.cuda.synchronize()
+    want = np.zeros(S + (d, dv))
+    for i in np.ndindex(*S):
+        Ms = [f64(Mt)[(r,) + i] for r in range(R)]
+        Es = [f64(Et)[(r,) + i] for r in range(R)]
+        h = ref.merge_prefix_summaries(Ms, Es, R) if R else np.zeros((d, dv))
+        if h_in is not None:
+            # the page's fold starts from zero; from a state h0 it is the same
+            # fold with h0 carried through every transition
+            h0 = f64(ht)[i]
+            for r in range(R):
+                h0 = Ms[r] @ h0
+            h = h + h0
+        want[i] = h
+    assert_close("h", f64(out), want, torch.float32)
+    if with_h and R:
+        # in place: h_out aliases h_in
+        hh = ht.cuda()
+        gdn.gdn_merge_summaries(Mt.cuda(), Et.cuda(), hh, out=hh)
+        torch.cuda.synchronize()
+        assert torch.equal(hh, out)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_shard_summaries_compose_to_the_final_state(dtype):
+    """The all-gather mode on one GPU: a sequence cut into four shards, each
+    shard's summary computed on its own, folded from h0 with
+    gdn_merge_summaries, equals ht of gdn_chunk_fwd on the whole sequence;
+    and so does the wavefront (one summary applied at a time)."""
+    d = 32 if dtype == torch.float32 else 128
+    Hk, Hv = 1, 2
+    y, g, beta, cu = _inputs(90, [1000], Hk, Hv, d, d, dtype, 0.02)
+    h0 = torch.randn(1, Hv, d, d, generator=torch.Generator().manual_seed(5)) * 0.05
+    yc, gc, bc = y.cuda(), g.cuda(), beta.cuda()
+    _, ht = gdn.gdn_chunk_fwd(yc, gc, bc, cu_tensor(cu), Hk, Hv, d, d, h0=h0.cuda())
+    cuts = [0, 130, 500, 501, 1000]
+    Ms, Es = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        M, E = gdn.gdn_chunk_summary(yc[a:b], gc[a:b].contiguous(), bc[a:b].contiguous(),
+                                     cu_tensor([0, b - a]), Hk, Hv, d, d)
+        Ms.append(M)
+        Es.append(E)
+    h = gdn.gdn_merge_summaries(torch.stack(Ms), torch.stack(Es), h0.cuda())
+    wave = h0.cuda()
+    for M, E in zip(Ms, Es):
+        wave = gdn.gdn_merge_summaries(M[None], E[None], wave)
+    torch.cuda.synchronize()
+    assert_close("merged", f64(h), f64(ht), dtype)
+    assert_close("wavefront", f64(wave), f64(ht), dtype)
