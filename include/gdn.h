@@ -152,6 +152,35 @@ int gdn_conv1d_silu_halo_bwd(const void* x, const void* w, const void* bias, con
                              float* dbias, void* dhalo, void* ws, size_t ws_bytes, gdn_dtype dt,
                              hipStream_t stream);
 
+/* Size of the library's own scratch array used by
+ * gdn_conv1d_silu_halo_bwd_noalloc (one per GPU). */
+#define GDN_CONV_BWD_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * gdn_conv1d_silu_halo_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the dw / dbias partial rows
+ * in a static device array of GDN_CONV_BWD_SCRATCH_BYTES owned by the
+ * library (each GPU the library runs on holds its own copy until the process
+ * ends) instead of a caller workspace.  The call allocates nothing; the
+ * caller still passes every input and output.  The array's device address is
+ * looked up once per device, on the first call with that device current.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads without ordering) race and
+ * must not be issued; calls ordered on a stream are safe.  Nothing in the
+ * array needs to start at zero (each call overwrites the partial rows it
+ * reads).
+ * Errors: as gdn_conv1d_silu_halo_bwd; GDN_EWORKSPACE when
+ * gdn_conv_bwd_workspace_size(T, C, K) exceeds GDN_CONV_BWD_SCRATCH_BYTES
+ * (e.g. C above about 13000 channels at K = 4 for long inputs); GDN_EHIP if
+ * the array's address cannot be obtained.
+ */
+int gdn_conv1d_silu_halo_bwd_noalloc(const void* x, const void* w, const void* bias,
+                                     const void* halo, const int32_t* cu_seqlens, int32_t N,
+                                     int64_t T, int32_t C, int32_t K, const gdn_cp_meta* meta,
+                                     const void* dy, void* dx, float* dw, float* dbias,
+                                     void* dhalo, gdn_dtype dt, hipStream_t stream);
+
 /* Bytes of workspace gdn_chunk_fwd (bwd = 0) or gdn_chunk_bwd (bwd = 1)
  * needs for these sizes; 0 means none. */
 size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,

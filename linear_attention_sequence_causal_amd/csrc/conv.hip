@@ -16,6 +16,8 @@
 // masked, so the unrolled loop keeps every row in registers.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -593,4 +595,61 @@ extern "C" int gdn_conv1d_silu_halo_bwd(const void* x, const void* w, const void
   ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta};
   return dt == GDN_BF16 ? launch_bwd<bf16>(a, dy, dx, dw, dbias, dhalo, ws, stream)
                         : launch_bwd<float>(a, dy, dx, dw, dbias, dhalo, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The same backward for callers that cannot allocate: the dw / dbias partial
+// rows live in a file-scope device array (one copy per GPU, held until the
+// process ends) instead of a caller workspace.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = GDN_CONV_BWD_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch array, looked up once per device
+// with that device current.  In host code the array's name is only a
+// stand-in for it, never a device address.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return gdn::fail(GDN_EHIP, "gdn_conv1d_silu_halo_bwd_noalloc: no current device below %d",
+                     kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return gdn::fail(GDN_EHIP, "gdn_conv1d_silu_halo_bwd_noalloc: hipGetSymbolAddress: %s",
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" int gdn_conv1d_silu_halo_bwd_noalloc(const void* x, const void* w, const void* bias,
+                                                const void* halo, const int32_t* cu_seqlens,
+                                                int32_t N, int64_t T, int32_t C, int32_t K,
+                                                const gdn_cp_meta* meta, const void* dy, void* dx,
+                                                float* dw, float* dbias, void* dhalo, gdn_dtype dt,
+                                                hipStream_t stream) {
+  int rc = validate("gdn_conv1d_silu_halo_bwd_noalloc", x, w, cu_seqlens, N, T, C, K, dx, dt);
+  if (rc != GDN_OK) return rc;
+  const size_t need = gdn_conv_bwd_workspace_size(T, C, K);
+  if (need > kScratchBytes)
+    return gdn::fail(GDN_EWORKSPACE,
+                     "gdn_conv1d_silu_halo_bwd_noalloc: T=%lld C=%d K=%d need %zu bytes of scratch, "
+                     "above its fixed %zu; call gdn_conv1d_silu_halo_bwd with a workspace",
+                     (long long)T, C, K, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws)) != GDN_OK) return rc;
+  return gdn_conv1d_silu_halo_bwd(x, w, bias, halo, cu_seqlens, N, T, C, K, meta, dy, dx, dw, dbias,
+                                  dhalo, ws, kScratchBytes, dt, stream);
 }

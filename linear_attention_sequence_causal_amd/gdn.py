@@ -36,8 +36,9 @@ ENTRY_POINTS = (
     "gdn_localize_cu_seqlens", "gdn_conv1d_silu_halo", "gdn_conv_bwd_workspace_size",
     "gdn_conv1d_silu_halo_bwd", "gdn_chunk_workspace_size", "gdn_chunk_fwd", "gdn_chunk_bwd",
     "gdn_chunk_summary_workspace_size", "gdn_chunk_summary", "gdn_merge_summaries",
-    "gdn_last_error",
+    "gdn_conv1d_silu_halo_bwd_noalloc", "gdn_last_error",
 )
+CONV_BWD_SCRATCH_BYTES = 16 << 20  # GDN_CONV_BWD_SCRATCH_BYTES
 _SIZE_QUERIES = ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size",
                  "gdn_chunk_summary_workspace_size")
 
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_conv_bwd_workspace_size.restype = SZ
     lib.gdn_conv1d_silu_halo_bwd.argtypes = [P, P, P, P, P, I32, I64, I32, I32, P, P, P, P, P, P,
                                              P, SZ, INT, P]
+    lib.gdn_conv1d_silu_halo_bwd_noalloc.argtypes = [P, P, P, P, P, I32, I64, I32, I32, P, P, P,
+                                                     P, P, P, INT, P]
     lib.gdn_chunk_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, INT, INT]
     lib.gdn_chunk_workspace_size.restype = SZ
     lib.gdn_chunk_fwd.argtypes = [P, P, I64, P, I64, P, P, P, P, I32, I64, I32, I32, I32, I32, F,
@@ -244,6 +247,36 @@ def gdn_conv1d_silu_halo_bwd(x, w, cu_seqlens, dy, bias=None, halo=None, meta=No
                                        _ptr(dx), _ptr(dw), _ptr(dbias), _ptr(dhalo), _ptr(ws),
                                        nbytes, _dt(x), _stream())
     _check("gdn_conv1d_silu_halo_bwd", rc)
+    return dx, dw, dbias, dhalo
+
+
+def gdn_conv1d_silu_halo_bwd_noalloc(x, w, cu_seqlens, dy, out, bias=None, halo=None,
+                                     meta=None):
+    """gdn_conv1d_silu_halo_bwd into the caller's ``out`` = (dx, dw, dbias,
+    dhalo) with the library's static scratch: neither this function nor the
+    library allocates device memory."""
+    load_library()
+    _req(x, "x", shape=(None, None))
+    T, C = x.shape
+    _req(w, "w", x.dtype, (C, None), device=x)
+    K = w.shape[1]
+    _req(bias, "bias", x.dtype, (C,), device=x)
+    _req(halo, "halo", x.dtype, (K - 1, C), device=x)
+    _req(dy, "dy", x.dtype, (T, C), device=x)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=x)
+    _req(meta, "meta", torch.uint8, (META_BYTES,), device=x)
+    dx, dw, dbias, dhalo = out
+    if (dbias is None) != (bias is None) or (dhalo is None) != (halo is None):
+        raise ValueError("out must hold dbias / dhalo exactly when bias / halo are given")
+    _req(dx, "dx", x.dtype, (T, C), device=x)
+    _req(dw, "dw", torch.float32, (C, K), device=x)
+    _req(dbias, "dbias", torch.float32, (C,), device=x)
+    _req(dhalo, "dhalo", x.dtype, (K - 1, C), device=x)
+    rc = _lib.gdn_conv1d_silu_halo_bwd_noalloc(_ptr(x), _ptr(w), _ptr(bias), _ptr(halo),
+                                               _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, C, K,
+                                               _ptr(meta), _ptr(dy), _ptr(dx), _ptr(dw),
+                                               _ptr(dbias), _ptr(dhalo), _dt(x), _stream())
+    _check("gdn_conv1d_silu_halo_bwd_noalloc", rc)
     return dx, dw, dbias, dhalo
 
 

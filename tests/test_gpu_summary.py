@@ -54,9 +54,12 @@ def _check(y, g, beta, cu, Hk, Hv, dk, dv, seg=None):
         assert_close("E[%d]" % n, f64(E[n]), rE[n], dtype)
 
 
+# Gates are scaled so that M stays within float32 range: at the workloads'
+# gate strength (sum of g about -0.8 a token) the transition of a 256-token
+# sequence is about e^-205, which float32 flushes to zero.
 SMALL = [
     # lengths, Hk, Hv, dk, dv, dtype, g_scale
-    ([256], 2, 2, 32, 32, torch.float32, 1.0),
+    ([256], 2, 2, 32, 32, torch.float32, 0.1),
     ([1, 63, 64, 65, 0, 200], 1, 2, 32, 32, torch.float32, 0.1),
     ([130, 70], 2, 2, 64, 64, torch.float32, 0.1),
     ([300, 0, 2600], 2, 4, 128, 128, torch.bfloat16, 0.02),
@@ -93,7 +96,7 @@ def test_summary_sharded_workload():
     lc = local[:n + 1].contiguous()
     halo = inp["halo"].cuda()
     y = gdn.gdn_conv1d_silu_halo(inp["x"].cuda(), inp["w"].cuda(), lc, halo=halo, meta=meta)
-    g = inp["g"] * 0.05
+    g = inp["g"] * 0.01  # M of a 4096-token sequence stays within float32 range
     _check(y.cpu(), g, inp["beta"], lc.cpu().numpy(), spec.Hk, spec.Hv, spec.dk, spec.dv)
 
 
