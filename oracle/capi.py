@@ -60,6 +60,10 @@ def _load():
                                        ctypes.c_double, ctypes.c_int, P, P, P, P, P, P, P, P,
                                        ctypes.c_int]
         lib.oracle_gdn_bwd.restype = None
+        lib.oracle_gating_fwd.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+        lib.oracle_gating_fwd.restype = None
+        lib.oracle_gating_bwd.argtypes = [P, P, I64, P, P, P, P, I64, I64, P, P, I64, P, P]
+        lib.oracle_gating_bwd.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -157,4 +161,30 @@ def gdn_bwd(q, k, v, g, beta, h0, cu, scale, do, dht, use_l2norm=True, nthreads=
                        Hk, Hv, dk, dv, float(scale), int(bool(use_l2norm)), _ptr(do), _ptr(dht),
                        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                        _ptr(out["dbeta"]), _ptr(out["dh0"]), nt)
+    return out
+
+
+def gating_fwd(a, b, A_log, dt_bias):
+    """a, b [T, Hv]; A_log, dt_bias [Hv].  Returns g, beta [T, Hv]:
+    beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias)."""
+    lib = _load()
+    a, b, A_log, dt_bias = map(_f64, (a, b, A_log, dt_bias))
+    T, Hv = a.shape
+    g, beta = np.zeros((T, Hv)), np.zeros((T, Hv))
+    lib.oracle_gating_fwd(_ptr(a), _ptr(b), Hv, _ptr(A_log), _ptr(dt_bias), T, Hv, _ptr(g),
+                          _ptr(beta))
+    return g, beta
+
+
+def gating_bwd(a, b, A_log, dt_bias, dg, dbeta):
+    """Reverse mode of gating_fwd: returns dict da, db [T, Hv], dA_log,
+    ddt_bias [Hv]."""
+    lib = _load()
+    a, b, A_log, dt_bias, dg, dbeta = map(_f64, (a, b, A_log, dt_bias, dg, dbeta))
+    T, Hv = a.shape
+    out = dict(da=np.zeros((T, Hv)), db=np.zeros((T, Hv)), dA_log=np.zeros(Hv),
+               ddt_bias=np.zeros(Hv))
+    lib.oracle_gating_bwd(_ptr(a), _ptr(b), Hv, _ptr(A_log), _ptr(dt_bias), _ptr(dg), _ptr(dbeta),
+                          T, Hv, _ptr(out["da"]), _ptr(out["db"]), Hv, _ptr(out["dA_log"]),
+                          _ptr(out["ddt_bias"]))
     return out

@@ -31,6 +31,12 @@
  *   oracle_conv1d_silu_bwd -- reverse mode of oracle_conv1d_silu, with the
  *                             halo gradient the differentiable halo
  *                             all-to-all returns to the previous shard.
+ *   oracle_gating_fwd      -- the gating lines of the same page's CP
+ *                             wrappers (LinearAttentionP2PCPWrapper.forward
+ *                             and its siblings): per token and value head
+ *                               beta = sigmoid(b)
+ *                               g    = -exp(A_log) * softplus(a + dt_bias)
+ *   oracle_gating_bwd      -- its reverse mode (da, db, dA_log, ddt_bias).
  *
  * Layouts (row-major): x,y [T,C]; w [C,K]; halo [K-1,C]; q,k [T,Hk,dk];
  * v,o [T,Hv,dv]; g,beta [T,Hv]; states [N,Hv,dk,dv].  Varlen batches are
@@ -456,6 +462,50 @@ void oracle_gdn_bwd(const double *q, const double *k, const double *v, const dou
     free(dkh);
     free(tmp);
   }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Gating (hyper-parallel page, the CP wrappers' forward):                 */
+/*   beta = sigmoid(b),  g = -exp(A_log) * softplus(a + dt_bias)           */
+/* a, b [T, Hv] with token stride ld; A_log, dt_bias [Hv]; g, beta [T, Hv]. */
+/* ---------------------------------------------------------------------- */
+
+/* log(1 + e^x) without overflow: for x > 0 it is x + log(1 + e^-x). */
+static double softplus(double x) { return x > 0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+void oracle_gating_fwd(const double *a, const double *b, int64_t ld, const double *A_log,
+                       const double *dt_bias, int64_t T, int64_t Hv, double *g, double *beta) {
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t h = 0; h < Hv; h++) {
+      beta[t * Hv + h] = sigmoid(b[t * ld + h]);
+      g[t * Hv + h] = -exp(A_log[h]) * softplus(a[t * ld + h] + dt_bias[h]);
+    }
+}
+
+/* d softplus(x) / dx = sigmoid(x); d g / d A_log = g.  da, db [T, Hv] (token
+ * stride ld_d) and dA_log, ddt_bias [Hv] are overwritten; the per-head sums
+ * run over the tokens in order. */
+void oracle_gating_bwd(const double *a, const double *b, int64_t ld, const double *A_log,
+                       const double *dt_bias, const double *dg, const double *dbeta, int64_t T,
+                       int64_t Hv, double *da, double *db, int64_t ld_d, double *dA_log,
+                       double *ddt_bias) {
+  for (int64_t h = 0; h < Hv; h++) {
+    dA_log[h] = 0.0;
+    ddt_bias[h] = 0.0;
+  }
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t h = 0; h < Hv; h++) {
+      double sb = sigmoid(b[t * ld + h]);
+      double x = a[t * ld + h] + dt_bias[h];
+      double e = exp(A_log[h]);
+      double gv = -e * softplus(x);
+      double dgv = dg[t * Hv + h];
+      db[t * ld_d + h] = dbeta[t * Hv + h] * sb * (1.0 - sb);
+      double dx = dgv * (-e) * sigmoid(x);
+      da[t * ld_d + h] = dx;
+      ddt_bias[h] += dx;
+      dA_log[h] += dgv * gv;
+    }
 }
 
 int oracle_max_threads(void) {
