@@ -10,6 +10,8 @@
  *             _prepare_gdn_chunks_for_summary, _run_prepared_gdn_chunks,
  *             _RecvInitialStateP2PFunction, _SendFinalStateP2PFunction,
  *             _compute_gdn_state_summary_from_prepared,
+ *             the gating lines (beta = sigmoid(b), g = -exp(A_log) softplus(a +
+ *             dt_bias)) of the wrappers' forward,
  *             _merge_gdn_prefix_state_summaries_torch, _apply_gdn_state_summary,
  *             LinearAttentionP2PCPWrapper.forward (the data flow conv ->
  *             split -> GQA expansion -> gated delta rule).
@@ -247,6 +249,67 @@ int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v, in
                   int use_qk_l2norm, const void* d_o, const float* dht, void* dq, void* dk_,
                   int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta, float* dh0,
                   void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/*
+ * Gating step.  [HP-CP] LinearAttentionP2PCPWrapper.forward (and the
+ * all-gather and Ulysses wrappers), the lines that form the decay and the
+ * write strength from the projections: per token t and value head h,
+ *     beta[t,h] = sigmoid(b[t,h])
+ *     g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ * in float32 (softplus as max(x,0) + log1p(exp(-|x|)), which overflows
+ * nowhere; the page's beta is rounded to the activation dtype, here it is
+ * kept in float32).
+ *
+ *   a, b       [T, Hv] activations (dt), token stride ld_ab >= Hv elements
+ *              (e.g. two column blocks of packed projection rows).
+ *   A_log, dt_bias  float32 [Hv].
+ *   g, beta    float32 [T, Hv], contiguous (the gdn_chunk_fwd inputs).
+ * Errors: GDN_EINVAL for T < 0, Hv < 1, ld_ab < Hv, an unknown dtype or null
+ * pointers when T > 0.
+ */
+int gdn_gating_fwd(const void* a, const void* b, int64_t ld_ab, const float* A_log,
+                   const float* dt_bias, int64_t T, int32_t Hv, float* g, float* beta,
+                   gdn_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace gdn_gating_bwd needs (per-block partial sums). */
+size_t gdn_gating_bwd_workspace_size(int64_t T, int32_t Hv);
+
+/*
+ * Reverse mode of gdn_gating_fwd.  Given dg, dbeta float32 [T, Hv]:
+ *   db[t,h] = dbeta * beta (1 - beta);
+ *   da[t,h] = dg * (-exp(A_log[h])) * sigmoid(a + dt_bias[h]);
+ *   ddt_bias[h] = sum_t da[t,h];  dA_log[h] = sum_t dg[t,h] * g[t,h]
+ * (sums in a fixed order: run-to-run deterministic).  da, db: activations,
+ * token stride ld_dab >= Hv; dA_log, ddt_bias float32 [Hv] or NULL.
+ * ws: gdn_gating_bwd_workspace_size(T, Hv) bytes, 256-byte aligned.
+ * Errors: as gdn_gating_fwd, plus GDN_EWORKSPACE.
+ */
+int gdn_gating_bwd(const void* a, const void* b, int64_t ld_ab, const float* A_log,
+                   const float* dt_bias, const float* dg, const float* dbeta, int64_t T,
+                   int32_t Hv, void* da, void* db, int64_t ld_dab, float* dA_log,
+                   float* ddt_bias, void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace gdn_chunk_fwd_gated needs for these sizes. */
+size_t gdn_chunk_fwd_gated_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                                          int32_t dv, gdn_dtype dt);
+
+/*
+ * gdn_chunk_fwd with the gating step fused in: instead of g and beta it
+ * takes the projections a, b (activations, [T, Hv] with token stride ld_ab)
+ * and A_log, dt_bias (float32 [Hv]), and forms the gates as gdn_gating_fwd
+ * does (bit-identical values) where the chunk kernels load them, so g and
+ * beta never make a round trip through memory.  g_out / beta_out (float32
+ * [T, Hv] or NULL) receive the gates, for a backward.  Other arguments and
+ * results as gdn_chunk_fwd; ws: gdn_chunk_fwd_gated_workspace_size(...).
+ * Errors: as gdn_chunk_fwd, plus GDN_EINVAL for ld_ab < Hv or null A_log,
+ * dt_bias when T > 0.
+ */
+int gdn_chunk_fwd_gated(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                        const void* a, const void* b, int64_t ld_ab, const float* A_log,
+                        const float* dt_bias, const float* h0, const int32_t* cu_seqlens, int32_t N,
+                        int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                        int use_qk_l2norm, void* o, float* ht, float* g_out, float* beta_out,
+                        void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
 
 /* Bytes of workspace gdn_chunk_summary needs for these sizes. */
 size_t gdn_chunk_summary_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,

@@ -86,24 +86,36 @@ size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t
   if (T < 0 || N < 0 || Hv < 1) return 0;
   return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt), chunk_first_out(dk, dv, dt)).end;
 }
+
+// gdn_gating_fwd's kernel on a stream (gating.hip)
+int launch_gating_fwd(const void* a, const void* b, int64_t ld, const float* A_log,
+                      const float* dt_bias, int64_t T, int32_t Hv, float* g, float* beta,
+                      gdn_dtype dt, hipStream_t stream);
 }  // namespace gdn
 
-extern "C" int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const void* v,
-                             int64_t ld_v, const float* g, const float* beta, const float* h0,
-                             const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
-                             int32_t Hv, int32_t dk, int32_t dv, float scale, int use_qk_l2norm,
-                             void* o, float* ht, void* ws, size_t ws_bytes, gdn_dtype dt,
-                             hipStream_t stream) {
-  int rc = gdn::validate_chunk("gdn_chunk_fwd", q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk,
-                               Hv, dk, dv, dt);
-  if (rc != GDN_OK) return rc;
-  if (T > 0 && !o) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: o is null");
-  if (T > 0 && !gdn::aligned16(o)) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: o must be 16-byte aligned");
-  if (N > 0 && ht && !cu_seqlens) return gdn::fail(GDN_EINVAL, "gdn_chunk_fwd: null cu_seqlens");
-  const Plan pl = make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), gdn::chunk_first_out(dk, dv, dt));
-  if (!ws || ws_bytes < pl.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
-    return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_fwd: workspace needs %zu bytes, 256-byte aligned",
-                     pl.end);
+namespace {
+
+// whether (dt, dk, dv) runs the prepared-chunk path (whose prep reads the gates)
+bool prep_path(gdn_dtype dt, int dk, int dv) {
+  if (dt != GDN_BF16) return false;
+#define GDN_PCASE(K_, V_) \
+  if (dk == K_ && dv == V_) return uses_prep<bf16, K_, V_, kOut>();
+  GDN_PCASE(128, 128)
+  GDN_PCASE(128, 64)
+  GDN_PCASE(64, 128)
+  GDN_PCASE(128, 32)
+  GDN_PCASE(32, 128)
+  GDN_PCASE(64, 64)
+  GDN_PCASE(32, 32)
+  GDN_PCASE(64, 32)
+  GDN_PCASE(32, 64)
+#undef GDN_PCASE
+  return false;
+}
+
+LoopArgs loop_args(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                   const float* g, const float* beta, const float* h0, int32_t Hk, int32_t Hv,
+                   float scale, int use_qk_l2norm, void* o, float* ht) {
   LoopArgs a{};
   a.q = q;
   a.k = k;
@@ -119,6 +131,98 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const 
   a.use_l2norm = use_qk_l2norm ? 1 : 0;
   a.o = o;
   a.ht = ht;
+  return a;
+}
+
+int check_out(const char* fn, void* o, float* ht, int32_t N, int64_t T, const int32_t* cu) {
+  if (T > 0 && !o) return gdn::fail(GDN_EINVAL, "%s: o is null", fn);
+  if (T > 0 && !gdn::aligned16(o)) return gdn::fail(GDN_EINVAL, "%s: o must be 16-byte aligned", fn);
+  if (N > 0 && ht && !cu) return gdn::fail(GDN_EINVAL, "%s: null cu_seqlens", fn);
+  return GDN_OK;
+}
+
+Plan fwd_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
+  return make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), gdn::chunk_first_out(dk, dv, dt));
+}
+
+// the gated forward's gate buffers (g, beta [T, Hv] float32) after the plan,
+// when its kernels read given gates
+size_t gated_extra(int64_t T, int32_t Hv, gdn_dtype dt, int32_t dk, int32_t dv) {
+  return prep_path(dt, dk, dv) ? 0 : 2 * gdn::round_up(sizeof(float) * (size_t)T * Hv, 256);
+}
+
+}  // namespace
+
+extern "C" int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const void* v,
+                             int64_t ld_v, const float* g, const float* beta, const float* h0,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
+                             int32_t Hv, int32_t dk, int32_t dv, float scale, int use_qk_l2norm,
+                             void* o, float* ht, void* ws, size_t ws_bytes, gdn_dtype dt,
+                             hipStream_t stream) {
+  int rc = gdn::validate_chunk("gdn_chunk_fwd", q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk,
+                               Hv, dk, dv, dt);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_out("gdn_chunk_fwd", o, ht, N, T, cu_seqlens)) != GDN_OK) return rc;
+  const Plan pl = fwd_plan(T, N, Hv, dk, dv, dt);
+  if (!ws || ws_bytes < pl.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_fwd: workspace needs %zu bytes, 256-byte aligned",
+                     pl.end);
+  const LoopArgs a = loop_args(q, k, ld_qk, v, ld_v, g, beta, h0, Hk, Hv, scale, use_qk_l2norm, o, ht);
+  return dt == GDN_BF16 ? dispatch<bf16>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream)
+                        : dispatch<float>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream);
+}
+
+extern "C" size_t gdn_chunk_fwd_gated_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv,
+                                                     int32_t dk, int32_t dv, gdn_dtype dt) {
+  (void)Hk;
+  if (T < 0 || N < 0 || Hv < 1 || dk < 1 || dv < 1) return 0;
+  return gdn::round_up(fwd_plan(T, N, Hv, dk, dv, dt).end, 256) + gated_extra(T, Hv, dt, dk, dv);
+}
+
+extern "C" int gdn_chunk_fwd_gated(const void* q, const void* k, int64_t ld_qk, const void* v,
+                                   int64_t ld_v, const void* a_proj, const void* b_proj,
+                                   int64_t ld_ab, const float* A_log, const float* dt_bias,
+                                   const float* h0, const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                   int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                   int use_qk_l2norm, void* o, float* ht, float* g_out,
+                                   float* beta_out, void* ws, size_t ws_bytes, gdn_dtype dt,
+                                   hipStream_t stream) {
+  const char* fn = "gdn_chunk_fwd_gated";
+  // the projections stand in for g and beta in the shared checks
+  int rc = gdn::validate_chunk(fn, q, k, ld_qk, v, ld_v, (const float*)a_proj, (const float*)b_proj,
+                               cu_seqlens, N, T, Hk, Hv, dk, dv, dt);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_out(fn, o, ht, N, T, cu_seqlens)) != GDN_OK) return rc;
+  if (ld_ab < Hv) return gdn::fail(GDN_EINVAL, "%s: ld_ab smaller than Hv", fn);
+  if (T > 0 && (!A_log || !dt_bias)) return gdn::fail(GDN_EINVAL, "%s: null A_log or dt_bias", fn);
+  const Plan pl = fwd_plan(T, N, Hv, dk, dv, dt);
+  const size_t need = gdn_chunk_fwd_gated_workspace_size(T, N, Hk, Hv, dk, dv, dt);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return gdn::fail(GDN_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, need);
+  LoopArgs a = loop_args(q, k, ld_qk, v, ld_v, nullptr, nullptr, h0, Hk, Hv, scale, use_qk_l2norm,
+                         o, ht);
+  if (prep_path(dt, dk, dv)) {
+    // the prep forms each token's gates as it loads them
+    a.ga = a_proj;
+    a.gb = b_proj;
+    a.ld_ab = ld_ab;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.g_out = g_out;
+    a.beta_out = beta_out;
+  } else {
+    // kernels that read given gates: form them first (into the caller's
+    // g_out / beta_out, else the workspace)
+    char* extra = (char*)ws + gdn::round_up(pl.end, 256);
+    const size_t half = gdn::round_up(sizeof(float) * (size_t)T * Hv, 256);
+    float* gb = g_out ? g_out : reinterpret_cast<float*>(extra);
+    float* bb = beta_out ? beta_out : reinterpret_cast<float*>(extra + half);
+    if ((rc = gdn::launch_gating_fwd(a_proj, b_proj, ld_ab, A_log, dt_bias, T, Hv, gb, bb, dt,
+                                     stream)) != GDN_OK)
+      return rc;
+    a.g = gb;
+    a.beta = bb;
+  }
   return dt == GDN_BF16 ? dispatch<bf16>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream)
                         : dispatch<float>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream);
 }

@@ -75,7 +75,21 @@ struct LoopArgs {
   int first_done;    // the output of every sequence's first segment is already written
   int seg_base, seg_span;  // the state-pass grid covers segments seg_base .. + seg_span - 1
   int summary_all;         // kSummary: summarise a sequence's last segment too
+  // gates formed from projections in the prep (ga non-null; bf16 prep
+  // path), else the prep reads g, beta
+  const void* ga;
+  const void* gb;
+  int64_t ld_ab;
+  const float* A_log;
+  const float* dt_bias;
+  float* g_out;
+  float* beta_out;
 };
+
+// The prep's view of a call's gates.
+inline gdn_gate::Gates prep_gates(const LoopArgs& a) {
+  return gdn_gate::Gates{a.g, a.beta, a.ga, a.gb, a.ld_ab, a.A_log, a.dt_bias, a.g_out, a.beta_out};
+}
 
 // LDS of the chunk loop (one chunk of one head at a time; rows padded by
 // 16 bytes).  q, k are the raw rows (l2norm enters as per-row factors), v the
@@ -1165,7 +1179,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   if constexpr (PREP) {
     char* rec = ws + pl.off_rec;
     a.rec = rec;
-    PrepArgs pa{a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab,
+    PrepArgs pa{a.k, a.ld_qk, prep_gates(a), a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab,
                 pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
   }
@@ -1323,7 +1337,7 @@ int run_summary(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl,
   if constexpr (PREP) {
     char* rec = ws + pl.off_rec;
     a.rec = rec;
-    PrepArgs pa{a.k, a.ld_qk, a.g, a.beta, a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab, pp.counts, rec};
+    PrepArgs pa{a.k, a.ld_qk, prep_gates(a), a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab, pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
   }
   a.first_done = 0;

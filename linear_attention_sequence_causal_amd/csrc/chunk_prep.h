@@ -29,6 +29,7 @@
 
 #include "chunk_common.h"
 #include "chunk_plan.h"
+#include "gating.h"
 #include "gdn_internal.h"
 
 namespace gdn_chunk {
@@ -80,8 +81,7 @@ struct PrepSmem {
 struct PrepArgs {
   const void* k;
   int64_t ld_qk;
-  const float* g;
-  const float* beta;
+  gdn_gate::Gates gates;  // given g, beta, or the projections they are formed from
   int Hk, Hv;
   int use_l2norm;
   const int4* chunk_tab;
@@ -191,10 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void c
   // head's are loaded one head ahead
   const int64_t tg = tc + lane;
   float gn = 0.f, bn = 0.f;
-  if (tg < te) {
-    gn = a.g[tg * a.Hv + qa * GR];
-    bn = a.beta[tg * a.Hv + qa * GR];
-  }
+  if (tg < te) gdn_gate::load_gates<bf16>(a.gates, tg, qa * GR, a.Hv, gn, bn);
 
   // raw k rows (zero past the sequence end) and their l2norm factors
   {
@@ -241,10 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void c
     const int h = qa * GR + r;
     char* rec = a.rec + ((int64_t)chunk * a.Hv + h) * kRecBytes;
     const float gv = gn, bv = bn;
-    if (r + 1 < GR && tg < te) {
-      gn = a.g[tg * a.Hv + h + 1];
-      bn = a.beta[tg * a.Hv + h + 1];
-    }
+    if (r + 1 < GR && tg < te) gdn_gate::load_gates<bf16>(a.gates, tg, h + 1, a.Hv, gn, bn);
     const float Gv = wave_incl_scan(gv);  // in-chunk cumsum of g
     const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gv), 63));
     const float egv = __expf(Gv);

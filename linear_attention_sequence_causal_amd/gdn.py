@@ -36,11 +36,14 @@ ENTRY_POINTS = (
     "gdn_localize_cu_seqlens", "gdn_conv1d_silu_halo", "gdn_conv_bwd_workspace_size",
     "gdn_conv1d_silu_halo_bwd", "gdn_chunk_workspace_size", "gdn_chunk_fwd", "gdn_chunk_bwd",
     "gdn_chunk_summary_workspace_size", "gdn_chunk_summary", "gdn_merge_summaries",
-    "gdn_conv1d_silu_halo_bwd_noalloc", "gdn_last_error",
+    "gdn_conv1d_silu_halo_bwd_noalloc", "gdn_gating_fwd", "gdn_gating_bwd_workspace_size",
+    "gdn_gating_bwd", "gdn_chunk_fwd_gated_workspace_size", "gdn_chunk_fwd_gated",
+    "gdn_last_error",
 )
 CONV_BWD_SCRATCH_BYTES = 16 << 20  # GDN_CONV_BWD_SCRATCH_BYTES
 _SIZE_QUERIES = ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size",
-                 "gdn_chunk_summary_workspace_size")
+                 "gdn_chunk_summary_workspace_size", "gdn_gating_bwd_workspace_size",
+                 "gdn_chunk_fwd_gated_workspace_size")
 
 
 class GdnError(RuntimeError):
@@ -82,6 +85,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_summary.argtypes = [P, I64, P, I64, P, P, P, I32, I64, I32, I32, I32, I32, INT,
                                       P, P, P, SZ, INT, P]
     lib.gdn_merge_summaries.argtypes = [P, P, I32, I32, I32, I32, P, P, P]
+    lib.gdn_gating_fwd.argtypes = [P, P, I64, P, P, I64, I32, P, P, INT, P]
+    lib.gdn_gating_bwd_workspace_size.argtypes = [I64, I32]
+    lib.gdn_gating_bwd_workspace_size.restype = SZ
+    lib.gdn_gating_bwd.argtypes = [P, P, I64, P, P, P, P, I64, I32, P, P, I64, P, P, P, SZ, INT, P]
+    lib.gdn_chunk_fwd_gated_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, INT]
+    lib.gdn_chunk_fwd_gated_workspace_size.restype = SZ
+    lib.gdn_chunk_fwd_gated.argtypes = [P, P, I64, P, I64, P, P, I64, P, P, P, P, I32, I64, I32,
+                                        I32, I32, I32, F, INT, P, P, P, P, P, SZ, INT, P]
     lib.gdn_last_error.restype = ctypes.c_char_p
     for name in ENTRY_POINTS:
         if name not in _SIZE_QUERIES + ("gdn_last_error",):
@@ -417,3 +428,96 @@ def gdn_merge_summaries(M, E, h_in=None, out=None):
     rc = _lib.gdn_merge_summaries(_ptr(M), _ptr(E), R, S, dk, dv, _ptr(h_in), _ptr(h), _stream())
     _check("gdn_merge_summaries", rc)
     return h
+
+
+# --------------------------------------------------------------------------
+# gating: beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias)
+# --------------------------------------------------------------------------
+def _ab_views(a, b, Hv):
+    """a, b [T, Hv] views that share one token stride (columns of packed
+    rows or contiguous tensors); returns (T, ld)."""
+    if a.dim() != 2 or b.shape != a.shape or a.shape[1] != Hv:
+        raise ValueError("a and b must be [T, Hv] views of one shape")
+    if a.stride(1) != 1 or b.stride(1) != 1 or a.stride(0) != b.stride(0):
+        raise ValueError("a and b need unit head stride and one common token stride")
+    if a.dtype != b.dtype or a.device != b.device or not a.is_cuda:
+        raise ValueError("a and b must be GPU tensors of one dtype")
+    return a.shape[0], a.stride(0)
+
+
+def gdn_gating_fwd(a, b, A_log, dt_bias, out=None):
+    """Returns (g, beta) float32 [T, Hv]."""
+    load_library()
+    Hv = A_log.numel()
+    T, ld = _ab_views(a, b, Hv)
+    _req(A_log, "A_log", torch.float32, (Hv,), device=a)
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,), device=a)
+    g, beta = out if out is not None else (
+        torch.empty((T, Hv), dtype=torch.float32, device=a.device),
+        torch.empty((T, Hv), dtype=torch.float32, device=a.device))
+    _req(g, "g", torch.float32, (T, Hv), device=a)
+    _req(beta, "beta", torch.float32, (T, Hv), device=a)
+    rc = _lib.gdn_gating_fwd(_ptr(a), _ptr(b), ld, _ptr(A_log), _ptr(dt_bias), T, Hv, _ptr(g),
+                             _ptr(beta), _dt(a), _stream())
+    _check("gdn_gating_fwd", rc)
+    return g, beta
+
+
+def gdn_gating_bwd(a, b, A_log, dt_bias, dg, dbeta, ws=None):
+    """Returns dict da, db [T, Hv] (activations), dA_log, ddt_bias [Hv]."""
+    load_library()
+    Hv = A_log.numel()
+    T, ld = _ab_views(a, b, Hv)
+    _req(A_log, "A_log", torch.float32, (Hv,), device=a)
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,), device=a)
+    _req(dg, "dg", torch.float32, (T, Hv), device=a)
+    _req(dbeta, "dbeta", torch.float32, (T, Hv), device=a)
+    da = torch.empty((T, Hv), dtype=a.dtype, device=a.device)
+    db = torch.empty((T, Hv), dtype=a.dtype, device=a.device)
+    dA = torch.empty(Hv, dtype=torch.float32, device=a.device)
+    ddt = torch.empty(Hv, dtype=torch.float32, device=a.device)
+    nbytes = int(_lib.gdn_gating_bwd_workspace_size(T, Hv))
+    ws = _workspace(ws, nbytes, a)
+    rc = _lib.gdn_gating_bwd(_ptr(a), _ptr(b), ld, _ptr(A_log), _ptr(dt_bias), _ptr(dg),
+                             _ptr(dbeta), T, Hv, _ptr(da), _ptr(db), Hv, _ptr(dA), _ptr(ddt),
+                             _ptr(ws), nbytes, _dt(a), _stream())
+    _check("gdn_gating_bwd", rc)
+    return dict(da=da, db=db, dA_log=dA, ddt_bias=ddt)
+
+
+def gdn_chunk_fwd_gated(y, a, b, A_log, dt_bias, cu_seqlens, Hk, Hv, dk, dv, h0=None,
+                        scale=None, use_qk_l2norm=True, want_ht=True, want_gates=False, out=None,
+                        ws=None):
+    """gdn_chunk_fwd on the q/k/v blocks of y with the gates formed from a,
+    b, A_log, dt_bias inside the chunk kernels.  Returns (o, ht, g, beta);
+    g, beta are None unless ``want_gates``."""
+    load_library()
+    _req(y, "y", shape=(None, None))
+    T, C = y.shape
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=y)
+    N = cu_seqlens.numel() - 1
+    Ta, ld = _ab_views(a, b, Hv)
+    if Ta != T or a.dtype != y.dtype or a.device != y.device:
+        raise ValueError("a, b must be [T, Hv] in the activation dtype, on y's device")
+    _req(A_log, "A_log", torch.float32, (Hv,), device=y)
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,), device=y)
+    _req(h0, "h0", torch.float32, (N, Hv, dk, dv), device=y)
+    q, k, v = _qkv_views(y, Hk, Hv, dk, dv)
+    o = out if out is not None else torch.empty((T, Hv, dv), dtype=y.dtype, device=y.device)
+    _req(o, "out", y.dtype, (T, Hv, dv), device=y)
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=y.device) if want_ht else None
+    g = beta = None
+    if want_gates:
+        g = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
+        beta = torch.empty((T, Hv), dtype=torch.float32, device=y.device)
+    dt = GDN_BF16 if y.dtype == torch.bfloat16 else GDN_F32
+    nbytes = int(_lib.gdn_chunk_fwd_gated_workspace_size(T, N, Hk, Hv, dk, dv, dt))
+    ws = _workspace(ws, nbytes, y)
+    scale = dk ** -0.5 if scale is None else scale
+    rc = _lib.gdn_chunk_fwd_gated(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(a), _ptr(b), ld,
+                                  _ptr(A_log), _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), N, T, Hk,
+                                  Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)), _ptr(o),
+                                  _ptr(ht), _ptr(g), _ptr(beta), _ptr(ws), nbytes, _dt(y),
+                                  _stream())
+    _check("gdn_chunk_fwd_gated", rc)
+    return o, ht, g, beta
