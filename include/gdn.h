@@ -12,6 +12,7 @@
  *             _compute_gdn_state_summary_from_prepared,
  *             the gating lines (beta = sigmoid(b), g = -exp(A_log) softplus(a +
  *             dt_bias)) of the wrappers' forward,
+ *             LinearAttentionUlyssesCPWrapper (_seq_to_head_qkvba, its forward),
  *             _merge_gdn_prefix_state_summaries_torch, _apply_gdn_state_summary,
  *             LinearAttentionP2PCPWrapper.forward (the data flow conv ->
  *             split -> GQA expansion -> gated delta rule).
@@ -310,6 +311,47 @@ int gdn_chunk_fwd_gated(const void* q, const void* k, int64_t ld_qk, const void*
                         int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
                         int use_qk_l2norm, void* o, float* ht, float* g_out, float* beta_out,
                         void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
+
+/* Bytes of workspace gdn_ulysses_fwd needs for these (rank-local) sizes. */
+size_t gdn_ulysses_fwd_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                                      int32_t dv, gdn_dtype dt);
+
+/*
+ * One rank's forward in the head-sharded (Ulysses) layout.  [HP-CP]
+ * LinearAttentionUlyssesCPWrapper: after _seq_to_head_qkvba's all-to-all a
+ * rank holds, for the whole (packed) sequence batch, rows
+ *     [ q (Hk*dk) | k (Hk*dk) | v (Hv*dv) | b (Hv) | a (Hv) ]
+ * of its local heads (Hk, Hv here are the rank's counts: the model's divided
+ * by the group size).  It runs the causal conv + SiLU over the local
+ * q|k|v channels with the local conv weight slice (the page's
+ * _local_conv_weight), forms beta, g from the b, a columns with the local
+ * slices of A_log and dt_bias, and the gated delta rule on its heads (GQA
+ * v-head h reads q/k head h / (Hv/Hk)).  The q|k|v columns are read in place
+ * by the conv and the b|a columns by the chunk kernels' prep; there is no
+ * halo (every rank has the whole sequence).
+ *
+ *   packed     [T, >= 2*Hk*dk + Hv*dv + 2*Hv] activations, token stride
+ *              ld_packed elements (16-byte multiples run the vector path).
+ *   conv_w     [C, K] activations, C = 2*Hk*dk + Hv*dv (the rank's slice);
+ *              conv_bias [C] or NULL.  K in [1, 8].
+ *   A_log, dt_bias  float32 [Hv] (the rank's slices).
+ *   h0, ht     float32 [N, Hv, dk, dv] or NULL (the page passes none).
+ *   y          out, [T, C] activations: the conv output (q, k, v of the
+ *              chunk; keep it for a backward).
+ *   o          out, [T, Hv, dv] activations.
+ *   g_out, beta_out  float32 [T, Hv] or NULL: the gates, for a backward.
+ *   ws         gdn_ulysses_fwd_workspace_size(...) bytes, 256-byte aligned.
+ * Errors: GDN_EINVAL for ld_packed < C + 2*Hv, null pointers and the checks
+ * of gdn_conv1d_silu_halo and gdn_chunk_fwd_gated; GDN_EUNSUPPORTED and
+ * GDN_EWORKSPACE as gdn_chunk_fwd_gated.  Nothing is launched when a check
+ * fails.
+ */
+int gdn_ulysses_fwd(const void* packed, int64_t ld_packed, const void* conv_w,
+                    const void* conv_bias, int32_t K, const float* A_log, const float* dt_bias,
+                    const float* h0, const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
+                    int32_t Hv, int32_t dk, int32_t dv, float scale, int use_qk_l2norm, void* y,
+                    void* o, float* ht, float* g_out, float* beta_out, void* ws, size_t ws_bytes,
+                    gdn_dtype dt, hipStream_t stream);
 
 /* Bytes of workspace gdn_chunk_summary needs for these sizes. */
 size_t gdn_chunk_summary_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,

@@ -103,7 +103,7 @@ template <typename E, int K, int V>
 __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
     const E* __restrict__ x, const E* __restrict__ w, const E* __restrict__ bias,
     const E* __restrict__ halo, const int32_t* __restrict__ cu, int N, int64_t T, int C,
-    int cgroups, const gdn_cp_meta* __restrict__ meta, E* __restrict__ y) {
+    int64_t ldx, int cgroups, const gdn_cp_meta* __restrict__ meta, E* __restrict__ y) {
   constexpr int R = kFwdRows;
   // channel groups vary fastest so that concurrent blocks cover whole rows
   const int64_t b = blockIdx.x;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 #pragma unroll
   for (int i = 0; i < R + K - 1; i++) {
     const int64_t tau = t0 - (K - 1) + i;
-    xr[i] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
+    xr[i] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * ldx + c0) : zero_row<E, V>();
   }
   int n = find_seq(cu, N, t0);
   int64_t s = cu[n], e = cu[n + 1];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
       for (int j = 0; j < K; j++) {
         const int64_t tau = t - (K - 1) + j;
         if (tau >= s) {
-          const Row<E, V> xv = load_row<E, V>(x + tau * C + c0);
+          const Row<E, V> xv = load_row<E, V>(x + tau * ldx + c0);
 #pragma unroll
           for (int i = 0; i < V; i++) z[i] += wv[j][i] * xv.at(i);
         } else if (n == 0 && s - tau <= n_halo) {
@@ -441,13 +441,14 @@ struct ConvArgs {
   int64_t T;
   int C, K;
   const gdn_cp_meta* meta;
+  int64_t ldx;  // token stride of x in elements (forward; C for a contiguous x)
 };
 
 template <typename E, int K>
 int launch_fwd_k(const ConvArgs& a, void* y, hipStream_t stream) {
   constexpr int VE = Vec16<E>::N;
-  const bool vec = (a.C % VE == 0) && gdn::aligned16(a.x) && gdn::aligned16(y) &&
-                   (a.halo == nullptr || gdn::aligned16(a.halo));
+  const bool vec = (a.C % VE == 0) && (a.ldx % VE == 0) && gdn::aligned16(a.x) &&
+                   gdn::aligned16(y) && (a.halo == nullptr || gdn::aligned16(a.halo));
   const int V = vec ? VE : 1;
   const int cvec = (a.C + V - 1) / V;
   dim3 block(kLanes, kRunsPerBlock);
@@ -459,11 +460,11 @@ int launch_fwd_k(const ConvArgs& a, void* y, hipStream_t stream) {
   if (vec)
     hipLaunchKernelGGL((conv_fwd_kernel<E, K, VE>), grid, block, 0, stream, (const E*)a.x,
                        (const E*)a.w, (const E*)a.bias, (const E*)a.halo, a.cu, a.N, a.T, a.C,
-                       cgroups, a.meta, (E*)y);
+                       a.ldx, cgroups, a.meta, (E*)y);
   else
     hipLaunchKernelGGL((conv_fwd_kernel<E, K, 1>), grid, block, 0, stream, (const E*)a.x,
                        (const E*)a.w, (const E*)a.bias, (const E*)a.halo, a.cu, a.N, a.T, a.C,
-                       cgroups, a.meta, (E*)y);
+                       a.ldx, cgroups, a.meta, (E*)y);
   return gdn::check_launch("gdn_conv1d_silu_halo");
 }
 
@@ -569,9 +570,24 @@ extern "C" int gdn_conv1d_silu_halo(const void* x, const void* w, const void* bi
                                     void* y, gdn_dtype dt, hipStream_t stream) {
   int rc = validate("gdn_conv1d_silu_halo", x, w, cu_seqlens, N, T, C, K, y, dt);
   if (rc != GDN_OK || T == 0) return rc;
-  ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta};
+  ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta, C};
   return dt == GDN_BF16 ? launch_fwd<bf16>(a, y, stream) : launch_fwd<float>(a, y, stream);
 }
+
+namespace gdn {
+// The forward conv reading x with token stride ldx (>= C) elements, e.g. the
+// leading C columns of packed projection rows.
+int conv_fwd_strided(const void* x, int64_t ldx, const void* w, const void* bias,
+                     const void* halo, const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t C,
+                     int32_t K, const gdn_cp_meta* meta, void* y, gdn_dtype dt,
+                     hipStream_t stream) {
+  int rc = validate("conv (strided)", x, w, cu_seqlens, N, T, C, K, y, dt);
+  if (rc != GDN_OK || T == 0) return rc;
+  if (ldx < C) return fail(GDN_EINVAL, "conv: row stride of x smaller than C");
+  ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta, ldx};
+  return dt == GDN_BF16 ? launch_fwd<bf16>(a, y, stream) : launch_fwd<float>(a, y, stream);
+}
+}  // namespace gdn
 
 extern "C" size_t gdn_conv_bwd_workspace_size(int64_t T, int32_t C, int32_t K) {
   if (T <= 0 || C <= 0 || K <= 0) return 0;
@@ -592,7 +608,7 @@ extern "C" int gdn_conv1d_silu_halo_bwd(const void* x, const void* w, const void
   if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
     return gdn::fail(GDN_EWORKSPACE,
                      "gdn_conv1d_silu_halo_bwd: workspace needs %zu bytes, 256-byte aligned", need);
-  ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta};
+  ConvArgs a{x, w, bias, halo, cu_seqlens, N, T, C, K, meta, C};
   return dt == GDN_BF16 ? launch_bwd<bf16>(a, dy, dx, dw, dbias, dhalo, ws, stream)
                         : launch_bwd<float>(a, dy, dx, dw, dbias, dhalo, ws, stream);
 }

@@ -42,4 +42,9 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
 size_t chunk_rec_bytes(gdn_dtype dt);
 
+// The forward conv with an x token stride (conv.hip).
+int conv_fwd_strided(const void* x, int64_t ldx, const void* w, const void* bias,
+                     const void* halo, const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t C,
+                     int32_t K, const gdn_cp_meta* meta, void* y, gdn_dtype dt, hipStream_t stream);
+
 }  // namespace gdn

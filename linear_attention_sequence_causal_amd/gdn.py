@@ -38,12 +38,12 @@ ENTRY_POINTS = (
     "gdn_chunk_summary_workspace_size", "gdn_chunk_summary", "gdn_merge_summaries",
     "gdn_conv1d_silu_halo_bwd_noalloc", "gdn_gating_fwd", "gdn_gating_bwd_workspace_size",
     "gdn_gating_bwd", "gdn_chunk_fwd_gated_workspace_size", "gdn_chunk_fwd_gated",
-    "gdn_last_error",
+    "gdn_ulysses_fwd_workspace_size", "gdn_ulysses_fwd", "gdn_last_error",
 )
 CONV_BWD_SCRATCH_BYTES = 16 << 20  # GDN_CONV_BWD_SCRATCH_BYTES
 _SIZE_QUERIES = ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size",
                  "gdn_chunk_summary_workspace_size", "gdn_gating_bwd_workspace_size",
-                 "gdn_chunk_fwd_gated_workspace_size")
+                 "gdn_chunk_fwd_gated_workspace_size", "gdn_ulysses_fwd_workspace_size")
 
 
 class GdnError(RuntimeError):
@@ -93,6 +93,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_gated_workspace_size.restype = SZ
     lib.gdn_chunk_fwd_gated.argtypes = [P, P, I64, P, I64, P, P, I64, P, P, P, P, I32, I64, I32,
                                         I32, I32, I32, F, INT, P, P, P, P, P, SZ, INT, P]
+    lib.gdn_ulysses_fwd_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, INT]
+    lib.gdn_ulysses_fwd_workspace_size.restype = SZ
+    lib.gdn_ulysses_fwd.argtypes = [P, I64, P, P, I32, P, P, P, P, I32, I64, I32, I32, I32, I32, F,
+                                    INT, P, P, P, P, P, P, SZ, INT, P]
     lib.gdn_last_error.restype = ctypes.c_char_p
     for name in ENTRY_POINTS:
         if name not in _SIZE_QUERIES + ("gdn_last_error",):
@@ -521,3 +525,46 @@ def gdn_chunk_fwd_gated(y, a, b, A_log, dt_bias, cu_seqlens, Hk, Hv, dk, dv, h0=
                                   _stream())
     _check("gdn_chunk_fwd_gated", rc)
     return o, ht, g, beta
+
+
+# --------------------------------------------------------------------------
+# head-sharded (Ulysses) layout: one rank's packed [q | k | v | b | a] rows
+# --------------------------------------------------------------------------
+def gdn_ulysses_fwd(packed, conv_w, A_log, dt_bias, cu_seqlens, Hk, Hv, dk, dv, conv_bias=None,
+                    h0=None, scale=None, use_qk_l2norm=True, want_ht=False, want_gates=False,
+                    ws=None):
+    """packed [T, >= C + 2 Hv] rows [q | k | v | b | a] of the rank's heads
+    (unit column stride, any token stride).  Returns (y [T, C], o
+    [T, Hv, dv], ht or None, g or None, beta or None)."""
+    load_library()
+    if packed.dim() != 2 or packed.stride(1) != 1 or not packed.is_cuda:
+        raise ValueError("packed must be a [T, W] GPU tensor with unit column stride")
+    T, W = packed.shape
+    C = 2 * Hk * dk + Hv * dv
+    if W < C + 2 * Hv:
+        raise ValueError("packed rows hold %d columns, [q|k|v|b|a] needs %d" % (W, C + 2 * Hv))
+    _req(conv_w, "conv_w", packed.dtype, (C, None), device=packed)
+    K = conv_w.shape[1]
+    _req(conv_bias, "conv_bias", packed.dtype, (C,), device=packed)
+    _req(A_log, "A_log", torch.float32, (Hv,), device=packed)
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,), device=packed)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, (None,), device=packed)
+    N = cu_seqlens.numel() - 1
+    _req(h0, "h0", torch.float32, (N, Hv, dk, dv), device=packed)
+    y = torch.empty((T, C), dtype=packed.dtype, device=packed.device)
+    o = torch.empty((T, Hv, dv), dtype=packed.dtype, device=packed.device)
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=packed.device) if want_ht else None
+    g = beta = None
+    if want_gates:
+        g = torch.empty((T, Hv), dtype=torch.float32, device=packed.device)
+        beta = torch.empty((T, Hv), dtype=torch.float32, device=packed.device)
+    dt = _dt(packed)
+    nbytes = int(_lib.gdn_ulysses_fwd_workspace_size(T, N, Hk, Hv, dk, dv, dt))
+    ws = _workspace(ws, nbytes, packed)
+    scale = dk ** -0.5 if scale is None else scale
+    rc = _lib.gdn_ulysses_fwd(_ptr(packed), packed.stride(0), _ptr(conv_w), _ptr(conv_bias), K,
+                              _ptr(A_log), _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), N, T, Hk, Hv,
+                              dk, dv, float(scale), int(bool(use_qk_l2norm)), _ptr(y), _ptr(o),
+                              _ptr(ht), _ptr(g), _ptr(beta), _ptr(ws), nbytes, dt, _stream())
+    _check("gdn_ulysses_fwd", rc)
+    return y, o, ht, g, beta
