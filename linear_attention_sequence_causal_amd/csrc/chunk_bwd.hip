@@ -65,8 +65,11 @@ struct BwdArgs {
   const int32_t* counts;
   const int4* chunk_tab;
   const int32_t* seq_chunk_off;
-  const float* states;  // [chunk_cap][Hv][DK][DV]
-  float* dstates;       // [chunk_cap][Hv][DK][DV]
+  // the state entering / the state gradient leaving every chunk,
+  // [chunk_cap][Hv][DK][DV] in the activation type (they feed MFMAs of that
+  // type only)
+  const void* states;
+  void* dstates;
   float* dqk;           // [T][Hv][2][DK]
   // segments of the sequences (the forward plan's), for the dS pass
   const int4* seg_table;
@@ -165,14 +168,15 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
     stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
     if (c > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, tc - BT, e0, tid);
     if (!SUM) {  // dS' of this chunk for the gradient kernel
-      float* dst = a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV;
+      E* dst = (E*)a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
         for (int nt = 0; nt < 2; nt++)
 #pragma unroll
           for (int j = 0; j < 4; j++)
-            dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
+            dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] =
+                from_f<E>(dS[mt][nt][j]);
     }
     __syncthreads();
     gram_kk<O, DK, NW>(sm, wave, lane);
@@ -346,8 +350,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   __syncthreads();
 
   const float GC = sm.G[BT - 1];
-  const float* Sg = a.states + ((int64_t)c * Hv + h) * DK * DV;
-  const float* dSg = a.dstates + ((int64_t)c * Hv + h) * DK * DV;
+  const E* Sg = (const E*)a.states + ((int64_t)c * Hv + h) * DK * DV;
+  const E* dSg = (const E*)a.dstates + ((int64_t)c * Hv + h) * DK * DV;
 
   // S and dS' as B fragments (K = dk, N = this wave's value columns) and <dS', S>
   typename M::frag sb[NSK][2], dsb[NSK][2];
@@ -363,8 +367,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const int idx = (16 * (TPS * s + q) + 4 * g4 + j) * DV + c0 + 16 * nt + ln;
-          st[q][j] = Sg[idx];
-          dt[q][j] = dSg[idx];
+          st[q][j] = to_f(Sg[idx]);
+          dt[q][j] = to_f(dSg[idx]);
           dot += st[q][j] * dt[q][j];
         }
       if constexpr (TPS == 2) {
@@ -599,8 +603,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     typename M::frag st[NSK], dst[NSK], kc[NSB], qc[NSB];
 #pragma unroll
     for (int s = 0; s < NSK; s++) {
-      st[s] = M::load_f32(Sg, DV, dc, s * KS, lane);    // B[k = value idx][n = key idx] = S[n][k]
-      dst[s] = M::load_f32(dSg, DV, dc, s * KS, lane);
+      st[s] = M::load(Sg, DV, dc, s * KS, lane);    // B[k = value idx][n = key idx] = S[n][k]
+      dst[s] = M::load(dSg, DV, dc, s * KS, lane);
     }
 #pragma unroll
     for (int s = 0; s < NSB; s++) {
@@ -763,7 +767,8 @@ BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, g
   BwdLayout L;
   L.plan = make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt));
   size_t o = L.plan.end;
-  const size_t st = sizeof(float) * (size_t)L.plan.chunk_cap * Hv * dk * dv;
+  const size_t es = dt == GDN_BF16 ? 2 : 4;  // states in the activation type
+  const size_t st = es * (size_t)L.plan.chunk_cap * Hv * dk * dv;
   L.off_states = o;
   o = gdn::round_up(o + st, 256);
   L.off_dstates = o;
@@ -782,11 +787,11 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
   b.counts = pp.counts;
   b.chunk_tab = pp.chunk_tab;
   b.seq_chunk_off = pp.seq_chunk_off;
-  b.states = reinterpret_cast<const float*>(ws + L.off_states);
-  b.dstates = reinterpret_cast<float*>(ws + L.off_dstates);
+  b.states = ws + L.off_states;
+  b.dstates = ws + L.off_dstates;
   b.dqk = reinterpret_cast<float*>(ws + L.off_dqk);
   LoopArgs la = la_in;
-  la.states = reinterpret_cast<float*>(ws + L.off_states);
+  la.states = ws + L.off_states;
   if (int rc = run_pipeline<E, DK, DV, kStates>(la, b.cu, N, T, L.plan, ws, true, stream)) return rc;
   // dS pass over the forward's segments (its summary and initial-state buffers
   // are free again): reverse summaries, reverse scan from dht, final pass

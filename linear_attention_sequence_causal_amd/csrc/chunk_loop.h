@@ -69,7 +69,8 @@ struct LoopArgs {
   const int32_t* seg_chunk0;
   float* seg_state;  // [seg_cap][Hv][DK][DK+DV] summaries
   float* seg_init;   // [seg_cap][Hv][DK][DV] initial states of non-first segments
-  float* states;     // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk
+  void* states;      // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk, in the
+                     // activation type (the backward uses it as MFMA operands of that type)
   const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
   int seg_cap;       // capacity of the segment table
   int first_done;    // the output of every sequence's first segment is already written
@@ -308,14 +309,14 @@ void chunk_loop_kernel(LoopArgs a) {
     stage_raw(sm, pf, a.scale, a.use_l2norm, tid_c);
     if constexpr (MODE == kStates) {
       // the state entering this chunk, for the backward
-      float* dst = a.states + ((int64_t)(a.seg_chunk0[seg] + c) * Hv + h) * DK * DV;
+      E* dst = (E*)a.states + ((int64_t)(a.seg_chunk0[seg] + c) * Hv + h) * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
         for (int nt = 0; nt < 2; nt++)
 #pragma unroll
           for (int j = 0; j < 4; j++)
-            dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
+            dst[(16 * mt + 4 * g4 + j) * DV + c0 + 16 * nt + ln] = from_f<E>(S[mt][nt][j]);
     }
     lds_barrier();
     // L (and P) tiles
@@ -826,14 +827,14 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
       const char* R = C.rec;
       if constexpr (MODE == kStates) {
         // the state entering this chunk, for the backward
-        float* dst = a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
+        E* dst = (E*)a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
 #pragma unroll
         for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
           for (int nt = 0; nt < NN; nt++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dst[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] = S[mt][nt][j];
+              dst[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] = from_f<E>(S[mt][nt][j]);
       }
       // k S (into x) and q S (into o), one contraction step of S at a time
 #pragma unroll

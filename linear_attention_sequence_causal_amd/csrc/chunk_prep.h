@@ -163,7 +163,10 @@ GDN_DEV void prep_column(SM& sm, const floatx4& Ai, float* Lt, char* rec, int la
 // blocks of row block w (L_ww, L_wm for m < w: the inversion and E_wm stay in
 // the wave) and column block w of T.
 template <int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void chunk_prep_kernel(PrepArgs a) {
+#ifndef GDN_PREP_WAVES
+#define GDN_PREP_WAVES 6
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GDN_PREP_WAVES))) void chunk_prep_kernel(PrepArgs a) {
   typedef Mfma<bf16> M;
   typedef M::frag Fr;
   typedef Tile16<float> F;
