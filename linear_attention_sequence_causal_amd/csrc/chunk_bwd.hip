@@ -76,7 +76,34 @@ struct BwdArgs {
   const int32_t* seg_chunk0;
   float* seg_sum;       // [seg_cap][Hv][DK][DK+DV] reverse summaries [M | E]
   float* seg_in;        // [seg_cap][Hv][DK][DV] dS leaving each non-last segment
+  // the forward prep's records [chunk_cap][Hv] (bfloat16 only, else null):
+  // T = (I + diag(beta) L)^-1 diag(beta) as MFMA A fragments
+  const char* rec;
 };
+
+// w = T diag(beta e^G) kh of one chunk from the prep's record: with the
+// record's T_r = (I + diag(beta) L)^-1 diag(beta) that is T_r diag(e^G) kh, a
+// product of the stored fragments (no gram, inversion or solve again).  Each
+// wave forms the tiles of one row block (mt = wave % 4), whose T fragments it
+// read from the record into tf.
+template <int DK, int NW, class SM>
+GDN_DEV void compute_w_rec(SM& sm, int wave, int lane, const bf16x8 (&tf)[2]) {
+  typedef Mfma<bf16> M;
+  static_assert(NW % 4 == 0, "one row block a wave");
+  constexpr int NTILE = 4 * (DK / 16);
+  const int mt = wave % 4;
+  for (int tt = wave; tt < NTILE; tt += NW) {
+    const int nt = tt / 4;
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+      if (2 * s <= mt)  // the fragments right of the diagonal are zero
+        M::mma(acc, tf[s], M::load_col_scaled(sm.k, SM::LDK, 16 * nt, s * M::KSTEP, sm.eg, lane));
+    const int rb = 16 * mt + 4 * (lane >> 4), c = 16 * nt + (lane & 15);
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) sm.w[(rb + jj) * SM::LDK + c] = from_f<bf16>(acc[jj]);
+  }
+}
 
 template <typename E, int DK, int DV>
 struct BwdCfg {
@@ -179,10 +206,29 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
                 from_f<E>(dS[mt][nt][j]);
     }
     __syncthreads();
-    gram_kk<O, DK, NW>(sm, wave, lane);
-    __syncthreads();
-    solve<O, DK, NW, true>(sm, wave, lane);
-    compute_w<O, DK, NW>(sm, wave, lane);
+    if constexpr (std::is_same<E, bf16>::value && NW % 4 == 0) {
+      // T from the forward prep's record (this wave's row block), P tiles on
+      // every wave
+      bf16x8 tf[2];
+      {
+        const int mt = wave % 4;
+        const char* R = a.rec + ((int64_t)(chunk0 + c) * Hv + h) * kRecBytes + kRecT + lane * 16;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
+          tf[s2] = 2 * s2 <= mt ? *reinterpret_cast<const bf16x8*>(R + p_frag(mt, s2) * 1024) : bf16x8{};
+      }
+      for (int t = wave; t < 10; t += NW) {
+        int ti, tj;
+        lower_tile_ij(t, ti, tj);
+        gram_tile<O, DK>(sm, true, ti, tj, lane);
+      }
+      compute_w_rec<DK, NW>(sm, wave, lane, tf);
+    } else {
+      gram_kk<O, DK, NW>(sm, wave, lane);
+      __syncthreads();
+      solve<O, DK, NW, true>(sm, wave, lane);
+      compute_w<O, DK, NW>(sm, wave, lane);
+    }
     __syncthreads();
 
     const float GC = sm.G[BT - 1];
@@ -797,6 +843,7 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
   // are free again): reverse summaries, reverse scan from dht, final pass
   b.seg_table = pp.table;
   b.seg_chunk0 = pp.seg_chunk0;
+  b.rec = uses_prep<E, DK, DV, kStates>() ? ws + L.plan.off_rec : nullptr;
   b.seg_sum = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_state) : nullptr;
   b.seg_in = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_init) : nullptr;
   const dim3 sgrid((unsigned)L.plan.seg_cap, b.Hv);
