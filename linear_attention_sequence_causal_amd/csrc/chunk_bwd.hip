@@ -117,10 +117,21 @@ struct BwdCfg {
 // dS pass: 32 state columns a wave; the summary mode carries the extended
 // state [M | E] (DK + DV columns) in one workgroup, so the chunk's shared
 // work (gram, T, w) is formed once for both.
+#ifndef GDN_DS_CW_SUM
+#define GDN_DS_CW_SUM 32
+#endif
+#ifndef GDN_DS_CW_FIN
+#define GDN_DS_CW_FIN 16
+#endif
 template <typename E, int DK, int DV, bool SUM>
 struct DsCfg {
   typedef E O;
-  static constexpr int NW = (SUM ? DK + DV : DV) / 32;
+  // state columns a wave: the final pass's waves hold 16 (eight waves, two a
+  // SIMD, at dv = 128), the summary's 32 (its 256 columns in eight waves)
+  static constexpr int COLS = SUM ? DK + DV : DV;
+  static constexpr int CW_REQ = SUM ? GDN_DS_CW_SUM : GDN_DS_CW_FIN;
+  static constexpr int CW = COLS / CW_REQ >= 4 ? CW_REQ : 32;  // at least four waves, else 32
+  static constexpr int NW = COLS / CW;
   static constexpr int NT = NW * 64;
   typedef Smem<O, DK, DV, true> SM;
   typedef Prefetch<E, DK, DV, NT, true> PF;
@@ -142,7 +153,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   typedef typename CF::O O;
   typedef Mfma<O> M;
   typedef typename CF::SM SM;
-  constexpr int NW = CF::NW, NT = CF::NT, KS = M::KSTEP;
+  constexpr int NW = CF::NW, NT = CF::NT, KS = M::KSTEP, CW = CF::CW, NN = CW / 16;
   constexpr int NSK = DK / KS, NSB = BT / KS, DKT = DK / 16;
   __shared__ SM sm;  // sm.v holds the chunk of dO
 
@@ -153,7 +164,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   const int n = ent.x;
   const int Hv = a.Hv, qa = h / (Hv / a.Hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c0 = wave * 32;                 // first (extended) state column
+  const int c0 = wave * CW;                 // first (extended) state column
   const bool mcol = SUM && c0 < DK;         // columns of M: no dO
   const int vc0 = SUM ? c0 - DK : c0;       // value column of the first column
   const int64_t s0 = ent.y, e0 = ent.z;
@@ -161,7 +172,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   const int chunk0 = a.seg_chunk0[seg];
 
   zero_upper<O, true, NT>(sm, tid);
-  floatx4 dS[DKT][2];
+  floatx4 dS[DKT][NN];
   {
     const float* src = nullptr;
     if (!SUM) {
@@ -171,7 +182,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++)
+      for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const int row = 16 * mt + 4 * (lane >> 4) + j, col = c0 + 16 * nt + (lane & 15);
@@ -199,7 +210,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
+        for (int nt = 0; nt < NN; nt++)
 #pragma unroll
           for (int j = 0; j < 4; j++)
             dst[(16 * mt + 4 * (lane >> 4) + j) * DV + c0 + 16 * nt + (lane & 15)] =
@@ -233,54 +244,56 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 
     const float GC = sm.G[BT - 1];
     // dVn = P^T dO + D o (K dS')
-    typename M::frag sb[NSK][2];
+    typename M::frag sb[NSK][NN];
 #pragma unroll
     for (int s = 0; s < NSK; s++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++) sb[s][nt] = acc_as_b<O>(dS, s, nt);
-    floatx4 dvn[4][2];
+      for (int nt = 0; nt < NN; nt++) sb[s][nt] = acc_as_b<O>(dS, s, nt);
+    floatx4 dvn[4][NN];
     // this wave's dO columns (the identity columns see no dO: their operand
     // is zero -- a select, not a branch, keeps both modes' registers alike)
-    typename M::frag dof[NSB][2];
+    typename M::frag dof[NSB][NN];
 #pragma unroll
-    for (int s = 0; s < NSB; s++) {
-      const typename M::frag v0 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 0 : vc0, s * KS, lane);
-      const typename M::frag v1 = M::load_col(sm.v, SM::LDV, vc0 < 0 ? 16 : vc0 + 16, s * KS, lane);
-      dof[s][0] = mcol ? typename M::frag{} : v0;
-      dof[s][1] = mcol ? typename M::frag{} : v1;
-    }
+    for (int s = 0; s < NSB; s++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) {
+        const typename M::frag vv = M::load_col(sm.v, SM::LDV, (vc0 < 0 ? 0 : vc0) + 16 * nt, s * KS, lane);
+        dof[s][nt] = mcol ? typename M::frag{} : vv;
+      }
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
-      floatx4 k0 = zero4(), k1 = zero4(), p0 = zero4(), p1 = zero4();
+      floatx4 kk[NN], pp[NN];
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) kk[nt] = pp[nt] = zero4();
 #pragma unroll
       for (int s = 0; s < NSK; s++) {
         const typename M::frag kf = M::load(sm.k, SM::LDK, 16 * mt, s * KS, lane);
-        M::mma(k0, kf, sb[s][0]);
-        M::mma(k1, kf, sb[s][1]);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(kk[nt], kf, sb[s][nt]);
       }
 #pragma unroll
       for (int s = 0; s < NSB; s++) {
         const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
-        M::mma(p0, pt, dof[s][0]);
-        M::mma(p1, pt, dof[s][1]);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(pp[nt], pt, dof[s][nt]);
       }
       const int rb = 16 * mt + 4 * (lane >> 4);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const float d = __expf(GC - sm.G[rb + j]);
-        p0[j] += d * k0[j];
-        p1[j] += d * k1[j];
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) pp[nt][j] += d * kk[nt][j];
       }
-      dvn[mt][0] = -p0;  // stored negated: the W^T term enters with a minus
-      dvn[mt][1] = -p1;
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) dvn[mt][nt] = -pp[nt];  // negated: the W^T term enters with a minus
     }
     // dS <- gamma_C dS' + Q^T (gamma o dO) - W^T dVn
     const float eC = __expf(GC);
-    typename M::frag db[NSB][2], gb[NSB][2];
+    typename M::frag db[NSB][NN], gb[NSB][NN];
 #pragma unroll
     for (int s = 0; s < NSB; s++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++) {
+      for (int nt = 0; nt < NN; nt++) {
         db[s][nt] = acc_as_b<O>(dvn, s, nt);
         const typename M::frag gv =
             M::load_col_scaled(sm.v, SM::LDV, (vc0 < 0 ? 0 : vc0) + 16 * nt, s * KS, sm.eg, lane);
@@ -288,18 +301,20 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
       }
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++) {
-      floatx4 acc0 = dS[mt][0] * eC, acc1 = dS[mt][1] * eC;
+      floatx4 acc[NN];
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) acc[nt] = dS[mt][nt] * eC;
 #pragma unroll
       for (int s = 0; s < NSB; s++) {
         const typename M::frag qt = M::load_col(sm.q, SM::LDK, 16 * mt, s * KS, lane);
-        M::mma(acc0, qt, gb[s][0]);
-        M::mma(acc1, qt, gb[s][1]);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], qt, gb[s][nt]);
         const typename M::frag wt = M::load_col(sm.w, SM::LDK, 16 * mt, s * KS, lane);
-        M::mma(acc0, wt, db[s][0]);
-        M::mma(acc1, wt, db[s][1]);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], wt, db[s][nt]);
       }
-      dS[mt][0] = acc0;
-      dS[mt][1] = acc1;
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) dS[mt][nt] = acc[nt];
     }
   }
   // the summary [M | E] of the segment, or dh0 from a sequence's first segment
@@ -315,7 +330,7 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++)
+      for (int nt = 0; nt < NN; nt++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
           dst[(16 * mt + 4 * (lane >> 4) + j) * ld + c0 + 16 * nt + (lane & 15)] = dS[mt][nt][j];
