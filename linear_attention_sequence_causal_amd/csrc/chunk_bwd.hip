@@ -105,10 +105,16 @@ GDN_DEV void compute_w_rec(SM& sm, int wave, int lane, const bf16x8 (&tf)[2]) {
   }
 }
 
+#ifndef GDN_GRAD_CW
+#define GDN_GRAD_CW 16
+#endif
 template <typename E, int DK, int DV>
 struct BwdCfg {
   typedef E O;
-  static constexpr int NW = DV / 32;
+  // value columns a wave: 16 (eight waves, two a SIMD, at dv = 128) while
+  // that leaves at least four waves, else 32
+  static constexpr int CW = DV / GDN_GRAD_CW >= 4 ? GDN_GRAD_CW : 32;
+  static constexpr int NW = DV / CW;
   static constexpr int NT = NW * 64;
   typedef Smem<O, DK, DV, true> SM;
   typedef Prefetch<E, DK, DV, NT, true> PF;
@@ -344,7 +350,7 @@ template <typename E, int DK, int DV>
 struct GradSmem {
   typedef Smem<E, DK, DV, true> SM;
   static constexpr int LDA = BT + 4;  // dA, dA^T, M1 + M1^T: [64][68] operand type
-  static constexpr int NW = DV / 32;
+  static constexpr int NW = BwdCfg<E, DK, DV>::NW;
   static constexpr bool MS_IN_V = sizeof(E) * BT * SM::LDV >= sizeof(E) * BT * LDA;
   SM b;
   alignas(16) E dO[BT * SM::LDV];
@@ -383,7 +389,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   const int Hv = a.Hv, qa = h / (Hv / a.Hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, ln = lane & 15;
-  const int c0 = wave * 32;
+  constexpr int CW = CF::CW, NN = CW / 16;
+  const int c0 = wave * CW;
 
   zero_upper<O, true, NT>(sm, tid);
   {
@@ -405,8 +412,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   gram_kk<O, DK, NW>(sm, wave, lane);
   __syncthreads();
   solve<O, DK, NW, true>(sm, wave, lane);
-  floatx4 vn[4][2];
-  compute_u<O>(sm, c0, lane, vn);  // u, turned into Vn below
+  floatx4 vn[4][NN];
+  compute_u<O, NN>(sm, c0, lane, vn);  // u, turned into Vn below
   compute_w<O, DK, NW>(sm, wave, lane);
   __syncthreads();
 
@@ -415,12 +422,12 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   const E* dSg = (const E*)a.dstates + ((int64_t)c * Hv + h) * DK * DV;
 
   // S and dS' as B fragments (K = dk, N = this wave's value columns) and <dS', S>
-  typename M::frag sb[NSK][2], dsb[NSK][2];
+  typename M::frag sb[NSK][NN], dsb[NSK][NN];
   float dot = 0.f;
 #pragma unroll
   for (int s = 0; s < NSK; s++)
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
+    for (int nt = 0; nt < NN; nt++) {
       constexpr int TPS = KS / 16;  // C-tiles per contraction step
       floatx4 st[TPS], dt[TPS];
 #pragma unroll
@@ -442,90 +449,99 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     }
 
   // Vn = u - W S; QS; KS; K dS'
-  floatx4 ks[4][2], kds[4][2];
+  floatx4 ks[4][NN], kds[4][NN];
   float r_doqs[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
-    floatx4 w0 = zero4(), w1 = zero4(), q0 = zero4(), q1 = zero4(), k0 = zero4(), k1 = zero4(),
-            d0 = zero4(), d1 = zero4();
+    floatx4 wq[NN], qq[NN], kq[NN], dq[NN];
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) wq[nt] = qq[nt] = kq[nt] = dq[nt] = zero4();
 #pragma unroll
     for (int s = 0; s < NSK; s++) {
       const typename M::frag wf = M::load(sm.w, SM::LDK, 16 * mt, s * KS, lane);
       const typename M::frag qf = M::load(sm.q, SM::LDK, 16 * mt, s * KS, lane);
       const typename M::frag kf = M::load(sm.k, SM::LDK, 16 * mt, s * KS, lane);
-      M::mma(w0, wf, sb[s][0]);
-      M::mma(w1, wf, sb[s][1]);
-      M::mma(q0, qf, sb[s][0]);
-      M::mma(q1, qf, sb[s][1]);
-      M::mma(k0, kf, sb[s][0]);
-      M::mma(k1, kf, sb[s][1]);
-      M::mma(d0, kf, dsb[s][0]);
-      M::mma(d1, kf, dsb[s][1]);
-    }
-    vn[mt][0] -= w0;
-    vn[mt][1] -= w1;
-    ks[mt][0] = k0;
-    ks[mt][1] = k1;
-    kds[mt][0] = d0;
-    kds[mt][1] = d1;
-    {
-      // dO tiles (mt, this wave's columns) in C layout
-      const floatx4 o0 = lds_tile_c(gs.dO, LDV, 16 * mt, c0, lane);
-      const floatx4 o1 = lds_tile_c(gs.dO, LDV, 16 * mt, c0 + 16, lane);
 #pragma unroll
-      for (int j = 0; j < 4; j++) r_doqs[mt][j] = o0[j] * q0[j] + o1[j] * q1[j];
+      for (int nt = 0; nt < NN; nt++) {
+        M::mma(wq[nt], wf, sb[s][nt]);
+        M::mma(qq[nt], qf, sb[s][nt]);
+        M::mma(kq[nt], kf, sb[s][nt]);
+        M::mma(dq[nt], kf, dsb[s][nt]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) {
+      vn[mt][nt] -= wq[nt];
+      ks[mt][nt] = kq[nt];
+      kds[mt][nt] = dq[nt];
+    }
+    // dO tiles (mt, this wave's columns) in C layout
+#pragma unroll
+    for (int j = 0; j < 4; j++) r_doqs[mt][j] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) {
+      const floatx4 o = lds_tile_c(gs.dO, LDV, 16 * mt, c0 + 16 * nt, lane);
+#pragma unroll
+      for (int j = 0; j < 4; j++) r_doqs[mt][j] += o[j] * qq[nt][j];
     }
   }
   // dVn = P^T dO + D o K dS'
-  floatx4 dvn[4][2];
+  floatx4 dvn[4][NN];
   float r_kdsvn[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
-    floatx4 p0 = zero4(), p1 = zero4();
+    floatx4 pp[NN];
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) pp[nt] = zero4();
 #pragma unroll
     for (int s = 0; s < NSB; s++) {
       const typename M::frag pt = M::load_col(sm.p, SM::LDT, 16 * mt, s * KS, lane);
-      M::mma(p0, pt, M::load_col(gs.dO, LDV, c0, s * KS, lane));
-      M::mma(p1, pt, M::load_col(gs.dO, LDV, c0 + 16, s * KS, lane));
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++)
+        M::mma(pp[nt], pt, M::load_col(gs.dO, LDV, c0 + 16 * nt, s * KS, lane));
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int row = 16 * mt + 4 * g4 + j;
       const float d = __expf(GC - sm.G[row]);
-      r_kdsvn[mt][j] = kds[mt][0][j] * vn[mt][0][j] + kds[mt][1][j] * vn[mt][1][j];
-      p0[j] += d * kds[mt][0][j];
-      p1[j] += d * kds[mt][1][j];
+      r_kdsvn[mt][j] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) {
+        r_kdsvn[mt][j] += kds[mt][nt][j] * vn[mt][nt][j];
+        pp[nt][j] += d * kds[mt][nt][j];
+      }
     }
-    dvn[mt][0] = p0;
-    dvn[mt][1] = p1;
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) dvn[mt][nt] = pp[nt];
   }
   // Y = T^T dVn; dv = beta o Y
-  floatx4 y[4][2];
+  floatx4 y[4][NN];
   float r_b[4][4], r_yks[4][4];
   E* dvp = (E*)a.dv + (int64_t)h * DV + c0 + ln;
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
-    floatx4 y0 = zero4(), y1 = zero4();
+    floatx4 yy[NN];
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) yy[nt] = zero4();
 #pragma unroll
     for (int s = 0; s < NSB; s++) {
       const typename M::frag tt = M::load_col_f32(sm.Tm, SM::LDF, 16 * mt, s * KS, nullptr, lane);
-      M::mma(y0, tt, acc_as_b<O>(dvn, s, 0));
-      M::mma(y1, tt, acc_as_b<O>(dvn, s, 1));
-    }
-    y[mt][0] = y0;
-    y[mt][1] = y1;
-    const floatx4 v0 = lds_tile_c(sm.v, LDV, 16 * mt, c0, lane);
-    const floatx4 v1 = lds_tile_c(sm.v, LDV, 16 * mt, c0 + 16, lane);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int row = 16 * mt + 4 * g4 + j;
-      const float bt = sm.beta[row];
-      r_b[mt][j] = y0[j] * v0[j] + y1[j] * v1[j];
-      r_yks[mt][j] = y0[j] * ks[mt][0][j] + y1[j] * ks[mt][1][j];
-      const int64_t t = tc + row;
-      if (t < te) {
-        dvp[t * a.ld_dv] = from_f<E>(bt * y0[j]);
-        dvp[t * a.ld_dv + 16] = from_f<E>(bt * y1[j]);
+      for (int nt = 0; nt < NN; nt++) M::mma(yy[nt], tt, acc_as_b<O>(dvn, s, nt));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) r_b[mt][j] = r_yks[mt][j] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) {
+      y[mt][nt] = yy[nt];
+      const floatx4 vv = lds_tile_c(sm.v, LDV, 16 * mt, c0 + 16 * nt, lane);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * mt + 4 * g4 + j;
+        r_b[mt][j] += yy[nt][j] * vv[j];
+        r_yks[mt][j] += yy[nt][j] * ks[mt][nt][j];
+        const int64_t t = tc + row;
+        if (t < te) dvp[t * a.ld_dv + 16 * nt] = from_f<E>(sm.beta[row] * yy[nt][j]);
       }
     }
   }
@@ -555,10 +571,11 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int row = 16 * mt + 4 * g4 + j;
-      sVn[row * LDV + c0 + ln] = from_f<O>(vn[mt][0][j]);
-      sVn[row * LDV + c0 + 16 + ln] = from_f<O>(vn[mt][1][j]);
-      sY[row * LDV + c0 + ln] = from_f<O>(y[mt][0][j]);
-      sY[row * LDV + c0 + 16 + ln] = from_f<O>(y[mt][1][j]);
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) {
+        sVn[row * LDV + c0 + 16 * nt + ln] = from_f<O>(vn[mt][nt][j]);
+        sY[row * LDV + c0 + 16 * nt + ln] = from_f<O>(y[mt][nt][j]);
+      }
     }
   __syncthreads();
 
@@ -656,10 +673,10 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   }
   __syncthreads();
 
-  // dk-side: this wave's key columns [c0, c0+32)
+  // dk-side: this wave's key columns [c0, c0 + CW)
   float* dqk = a.dqk + (int64_t)h * 2 * DK;
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++) {
+  for (int nt = 0; nt < NN; nt++) {
     const int dc = c0 + 16 * nt;
     typename M::frag st[NSK], dst[NSK], kc[NSB], qc[NSB];
 #pragma unroll

@@ -276,28 +276,30 @@ GDN_DEV void solve(SM& sm, int wave, int lane) {
   }
 }
 
-// u tiles for 32 value columns [vc0, vc0+32) into registers (C layout,
-// u[mt][nt]: token rows 16mt.., value cols vc0+16nt..).
-template <typename O, class SM>
-GDN_DEV void compute_u(const SM& sm, int vc0, int lane, floatx4 (&u)[4][2]) {
+// u tiles for 16 NN value columns [vc0, vc0 + 16 NN) into registers (C
+// layout, u[mt][nt]: token rows 16mt.., value cols vc0+16nt..).
+template <typename O, int NN, class SM>
+GDN_DEV void compute_u(const SM& sm, int vc0, int lane, floatx4 (&u)[4][NN]) {
   typedef Mfma<O> M;
   constexpr int NS = BT / M::KSTEP;
-  typename M::frag b[2][NS];
+  typename M::frag b[NN][NS];
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++)
+  for (int nt = 0; nt < NN; nt++)
 #pragma unroll
     for (int s = 0; s < NS; s++) b[nt][s] = M::load_col(sm.v, SM::LDV, vc0 + 16 * nt, s * M::KSTEP, lane);
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
-    floatx4 acc0 = zero4(), acc1 = zero4();
+    floatx4 acc[NN];
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) acc[nt] = zero4();
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const typename M::frag a = M::load_scaled(sm.Tm, SM::LDF, 16 * mt, s * M::KSTEP, sm.beta, lane);
-      M::mma(acc0, a, b[0][s]);
-      M::mma(acc1, a, b[1][s]);
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) M::mma(acc[nt], a, b[nt][s]);
     }
-    u[mt][0] = acc0;
-    u[mt][1] = acc1;
+#pragma unroll
+    for (int nt = 0; nt < NN; nt++) u[mt][nt] = acc[nt];
   }
 }
 
