@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle sample (0: chosen for ~10-30 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", default="",
+                    help="profiling only: comma-separated calls (localize, conv_fwd, chunk_fwd, "
+                         "chunk_bwd, conv_bwd) run in the loop, the others once before it; the "
+                         "line then reports those calls' times, not the workload's throughput")
     return ap.parse_args()
 
 
@@ -125,28 +129,40 @@ def main():
         ws_cb = torch.empty(max(gdn.conv_bwd_workspace_size(T, C, K), 1), dtype=torch.uint8,
                             device=dev)
 
-    def step(ev=None):
+    def step(ev=None, only=None):
+        # only: the calls run (profiling); the others keep their last outputs
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
+
+        def run(name):
+            return only is None or name in only
         mark(0)
-        local, meta = gdn.gdn_localize_cu_seqlens(cu_glob, total, spec.world_size, spec.rank, K,
-                                                  out=(local_buf, meta_buf))
-        m = meta if spec.world_size > 1 else meta_fixed
+        if run("localize"):
+            gdn.gdn_localize_cu_seqlens(cu_glob, total, spec.world_size, spec.rank, K,
+                                        out=(local_buf, meta_buf))
+        local = local_buf
+        m = meta_buf if spec.world_size > 1 else meta_fixed
         mark(1)
-        gdn.gdn_conv1d_silu_halo(x, w, local, halo=halo, meta=m, out=y)
+        if run("conv_fwd"):
+            gdn.gdn_conv1d_silu_halo(x, w, local, halo=halo, meta=m, out=y)
         mark(2)
-        gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht, ws=ws_f)
+        if run("chunk_fwd"):
+            gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht, ws=ws_f)
         mark(3)
         if spec.backward:
-            gr = gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht, ws=ws_b,
-                                   out=bwd_out)
+            if run("chunk_bwd"):
+                gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht, ws=ws_b,
+                                  out=bwd_out)
             mark(4)
-            gdn.gdn_conv1d_silu_halo_bwd(x, w, local, gr["dy"], halo=halo, meta=m, out=conv_out,
-                                         ws=ws_cb)
+            if run("conv_bwd"):
+                gdn.gdn_conv1d_silu_halo_bwd(x, w, local, bwd_out[0], halo=halo, meta=m,
+                                             out=conv_out, ws=ws_cb)
             mark(5)
 
     names = ["localize", "conv_fwd", "chunk_fwd"] + (["chunk_bwd", "conv_bwd"] if spec.backward else [])
+    if args.calls:
+        return profile_calls(args, names, step, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -215,6 +231,36 @@ def main():
         "rooflines_other": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def profile_calls(args, names, step, stream):
+    """Runs the calls that make the named calls' inputs once, then only the
+    named calls, so that a profiler sees those calls' kernels alone (the
+    chunk forward's outputs feed no later call, so it is not run as set-up)."""
+    import torch
+    keep = [c.strip() for c in args.calls.split(",") if c.strip()]
+    bad = [c for c in keep if c not in names]
+    if bad:
+        sys.exit("--calls: %s not among %s" % (bad, names))
+    first = min(names.index(c) for c in keep)
+    setup = {c for c in names[:first] if c != "chunk_fwd"}
+    if "conv_bwd" in keep and "chunk_bwd" not in keep:
+        setup.add("chunk_bwd")  # dy of the conv backward
+    step(only=setup)
+    torch.cuda.synchronize()
+    times = {c: [] for c in keep}
+    for i in range(args.warmup + args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        step(ev, only=set(keep))
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            for j, n in enumerate(names):
+                if n in keep:
+                    times[n].append(ev[j].elapsed_time(ev[j + 1]))
+    print(json.dumps({"profile_only": True, "calls": keep, "steps": args.steps,
+                      "warmup": args.warmup,
+                      "per_call_ms": {n: float(np.median(t)) for n, t in times.items()}}),
+          flush=True)
 
 
 def measured_traffic(call, workload):
