@@ -59,6 +59,14 @@ def chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s):
     return T * per_tok + 2 * N * Hv * dk * dv * 4
 
 
+def chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s):
+    """Algorithmic HBM bytes of one chunk backward: read q, k, v, g, beta and
+    dO, write dq, dk, dv, dg and dbeta; read h0 and dht and write dh0 once
+    per sequence."""
+    per_tok = 4 * Hk * dk * s + 3 * Hv * dv * s + 16 * Hv
+    return T * per_tok + 3 * N * Hv * dk * dv * 4
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,7 +86,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -208,6 +216,9 @@ def main():
                     "unit": "TFLOP/s", "frac": bwd_flops / t_bwd / peak,
                     "traffic": measured_traffic("chunk_bwd", spec.name),
                     "kernel": "gdn_chunk_bwd call: per-chunk states, dS passes, gradients, finalize"}
+        bwd_hbm = chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
+        extra["chunk_bwd_hbm"] = {"achieved": bwd_hbm / t_bwd / 1e9, "peak": HBM_PEAK / 1e9,
+                                  "unit": "GB/s", "frac": bwd_hbm / t_bwd / HBM_PEAK}
         t_cbwd = per_call["conv_bwd"] * 1e-3
         cbwd_b = conv_bwd_bytes_per_token(C, s_bytes) * T + C * K * (s_bytes + 4)
         extra["conv_bwd"] = {"bound": "hbm", "achieved": cbwd_b / t_cbwd / 1e9, "peak": HBM_PEAK / 1e9,
