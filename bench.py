@@ -297,15 +297,20 @@ def cpu_baseline(spec, inp, sample_tokens):
     from oracle import capi
     T = inp["T"]
     thr = capi.max_threads()
-    rec_threads = min(thr, spec.Hv)  # the recurrence runs its (sequence, head) chains in parallel
     if sample_tokens <= 0:
         # ~7*dk*dv fp64 FLOP per token and head; aim for ~15 s at ~2.5 GFLOP/s/thread
         per_tok = 7.0 * spec.dk * spec.dv * spec.Hv
-        sample_tokens = int(min(T, max(256, 15 * 2.5e9 * rec_threads / per_tok)))
+        sample_tokens = int(min(T, max(256, 15 * 2.5e9 * min(thr, spec.Hv) / per_tok)))
     n = min(sample_tokens, T)
     x = inp["x"][:n].double().numpy()
     w = inp["w"].double().numpy()
-    cu = [0, n]
+    # the workload's own sequence boundaries within the sample (a shard's
+    # tokens start at rank * T of the global batch)
+    start = spec.rank * T if spec.world_size > 1 else 0
+    cuts = np.clip(np.asarray(inp["cu_global"]) - start, 0, n)
+    cu = [0] + sorted({int(c) for c in cuts if 0 < c < n}) + [n]
+    # the recurrence runs its (sequence, head) chains in parallel
+    rec_threads = min(thr, (len(cu) - 1) * spec.Hv)
     Hk, Hv, dk, dv = spec.Hk, spec.Hv, spec.dk, spec.dv
     t0 = time.perf_counter()
     yv = capi.conv1d_silu(x, w, None, None, 0, cu)
