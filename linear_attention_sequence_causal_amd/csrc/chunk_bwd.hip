@@ -358,6 +358,11 @@ struct GradSmem {
   alignas(16) float part[4][NW][BT];  // row sums over each wave's columns
   alignas(16) float tp[5][4][BT];     // row/column sums of the 64x64 tiles
   alignas(16) float dot[NW];
+  // one value head a q/k head: per-wave row sums of u_q . dq-hat and
+  // u_k . dk-hat over each wave's key columns, and their totals (the l2norm
+  // backward in place)
+  alignas(16) float epi[2][NW][BT];
+  alignas(16) float etot[2][BT];
 };
 
 // row-partials kinds
@@ -673,8 +678,13 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   }
   __syncthreads();
 
-  // dk-side: this wave's key columns [c0, c0 + CW)
+  // dk-side: this wave's key columns [c0, c0 + CW).  With one value head a
+  // q/k head there is nothing to sum over heads, so the l2norm backward runs
+  // here (fused) and dq, dk are written directly; otherwise dq-hat, dk-hat go
+  // to the fp32 partials for finalize_qk_kernel.
+  const bool fused = a.Hv == a.Hk;
   float* dqk = a.dqk + (int64_t)h * 2 * DK;
+  float fq[NN][4][4], fk[NN][4][4];
 #pragma unroll
   for (int nt = 0; nt < NN; nt++) {
     const int dc = c0 + 16 * nt;
@@ -712,12 +722,71 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
         const float d = __expf(GC - sm.G[row]);
         const float dqv = gm * a1[j] + a2[j];
         const float dkv = b3[j] + d * b4[j] - sm.beta[row] * gm * b5[j] + b6[j];
-        if (t < te) {
+        fq[nt][mt][j] = dqv;
+        fk[nt][mt][j] = dkv;
+        if (!fused && t < te) {
           dqk[t * Hv * 2 * DK + dc + ln] = dqv;
           dqk[t * Hv * 2 * DK + DK + dc + ln] = dkv;
         }
       }
     }
+  }
+  if (fused) {
+    // the unit rows u = q-hat / scale and k-hat of this wave's columns (staged
+    // in LDS) give dq = scale r_q (dq-hat - u (u . dq-hat)) and dk = r_k
+    // (dk-hat - u_k (u_k . dk-hat)); the row dots are summed over the waves
+    const float inv_scale = 1.f / a.scale;
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * mt + 4 * g4 + j;
+        float sqd = 0.f, skd = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          const int col = c0 + 16 * nt + ln;
+          sqd += to_f(sm.q[row * SM::LDK + col]) * inv_scale * fq[nt][mt][j];
+          skd += to_f(sm.k[row * SM::LDK + col]) * fk[nt][mt][j];
+        }
+        sqd = row16_sum(sqd);
+        skd = row16_sum(skd);
+        if (ln == 0) {
+          gs.epi[0][wave][row] = sqd;
+          gs.epi[1][wave][row] = skd;
+        }
+      }
+    __syncthreads();
+    for (int i = tid; i < 2 * BT; i += NT) {
+      const int kind = i / BT, row = i % BT;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; w++) acc += gs.epi[kind][w][row];
+      gs.etot[kind][row] = acc;
+    }
+    __syncthreads();
+    E* dqo = (E*)a.dq + (int64_t)qa * DK + c0 + ln;
+    E* dko = (E*)a.dk + (int64_t)qa * DK + c0 + ln;
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * mt + 4 * g4 + j;
+        const int64_t t = tc + row;
+        if (t >= te) continue;
+        const float nq = sm.rnq[row], nk = sm.rnk[row];
+        const float qd = gs.etot[0][row], kd = gs.etot[1][row];
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          const int col = c0 + 16 * nt + ln;
+          float gq = a.scale * fq[nt][mt][j], gk = fk[nt][mt][j];
+          if (a.use_l2norm) {
+            gq = a.scale * nq * (fq[nt][mt][j] - to_f(sm.q[row * SM::LDK + col]) * inv_scale * qd);
+            gk = nk * (fk[nt][mt][j] - to_f(sm.k[row * SM::LDK + col]) * kd);
+          }
+          dqo[t * a.ld_dqk + 16 * nt] = from_f<E>(gq);
+          dko[t * a.ld_dqk + 16 * nt] = from_f<E>(gk);
+        }
+      }
   }
 
   // dbeta, dG -> dg (wave 0, lane = row)
@@ -898,6 +967,7 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
   hipLaunchKernelGGL((grad_kernel<E, DK, DV>), dim3((unsigned)L.plan.chunk_cap, b.Hv), dim3(CF::NT),
                      0, stream, b);
   if (int rc = gdn::check_launch("gdn_chunk_bwd(grad)")) return rc;
+  if (b.Hv == b.Hk) return GDN_OK;  // the gradient kernel wrote dq and dk itself
   const int64_t units = T * b.Hk;
   constexpr int64_t kUnitsPerBlock = 4 * (64 / (DK / 4));  // four waves
   hipLaunchKernelGGL((finalize_qk_kernel<E, DK>),

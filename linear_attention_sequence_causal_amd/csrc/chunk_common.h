@@ -51,6 +51,8 @@ struct Smem {
   alignas(16) float beta[BT];
   alignas(16) float bg[BT];  // beta * exp(G)
   alignas(16) float eg[BT];  // exp(G)
+  alignas(16) float rnq[BT];  // l2norm factors of the raw q, k rows (1 without)
+  alignas(16) float rnk[BT];
 };
 
 // Global -> register prefetch of one chunk (q, k rows of q/k head `qa`, v
@@ -131,6 +133,10 @@ GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale
     if constexpr (HAS_Q) {
       qss = group_sum<PF::QPR>(qss);
       if (use_l2norm) qr = scale / sqrtf(qss + 1e-6f);
+    }
+    if (i < PF::QV && vi == 0) {
+      sm.rnk[row] = kr;
+      if constexpr (HAS_Q) sm.rnq[row] = use_l2norm ? 1.f / sqrtf(qss + 1e-6f) : 1.f;
     }
     if (i < PF::QV) {
       OV kv, qv;
