@@ -539,12 +539,6 @@ struct WsSmem {
   alignas(16) O v[BT * LDV];
 };
 
-#ifdef GDN_WS_EXACT
-#define GDN_WS_OCC(NT_) __attribute__((amdgpu_waves_per_eu((NT_) / 256, (NT_) / 256)))
-#else
-#define GDN_WS_OCC(NT_)
-#endif
-
 template <typename E, int DK, int DV, int MODE>
 struct WsCfg {
   static constexpr bool OUT = MODE == kOut;
@@ -1020,8 +1014,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
 }
 
 template <typename E, int DK, int DV, int MODE>
-__global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) GDN_WS_OCC((WsCfg<E, DK, DV, MODE>::NT))
-void chunk_ws_kernel(LoopArgs a) {
+__global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(LoopArgs a) {
   typedef typename WsCfg<E, DK, DV, MODE>::SM SM;
   __shared__ SM buf[2];
   __shared__ unsigned p_count;  // loader waves' stored chunks, a running count (P hand-off)
@@ -1048,8 +1041,7 @@ void chunk_ws_kernel(LoopArgs a) {
 // there (from h0) instead of a summary: one launch, the mode chosen per
 // workgroup (both modes have the same waves).
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) GDN_WS_OCC((WsCfg<E, DK, DV, kOut>::NT))
-void chunk_ws_first_kernel(LoopArgs a) {
+__global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) void chunk_ws_first_kernel(LoopArgs a) {
   typedef typename WsCfg<E, DK, DV, kOut>::SM SMO;
   typedef typename WsCfg<E, DK, DV, kSummary>::SM SMS;
   static_assert(WsCfg<E, DK, DV, kOut>::NT == WsCfg<E, DK, DV, kSummary>::NT, "one block shape");
