@@ -125,7 +125,7 @@ def main():
 
     local_buf = torch.empty(N + 1, dtype=torch.int32, device=dev)
     meta_buf = torch.empty(gdn.META_BYTES, dtype=torch.uint8, device=dev)
-    bwd_out = conv_out = ws_b = ws_cb = None
+    bwd_out = conv_out = ws_b = ws_cb = saved = None
     if spec.backward:
         bwd_out = (torch.empty_like(x), torch.empty((T, Hv), dtype=torch.float32, device=dev),
                    torch.empty((T, Hv), dtype=torch.float32, device=dev),
@@ -136,6 +136,10 @@ def main():
                            dtype=torch.uint8, device=dev)
         ws_cb = torch.empty(max(gdn.conv_bwd_workspace_size(T, C, K), 1), dtype=torch.uint8,
                             device=dev)
+        # the training pair: the forward keeps the per-chunk states and records
+        # for the backward
+        saved = torch.empty(max(gdn.chunk_saved_size(T, N, Hk, Hv, dk, dv, dtype), 1),
+                            dtype=torch.uint8, device=dev)
 
     def step(ev=None, only=None):
         # only: the calls run (profiling); the others keep their last outputs
@@ -156,12 +160,17 @@ def main():
             gdn.gdn_conv1d_silu_halo(x, w, local, halo=halo, meta=m, out=y)
         mark(2)
         if run("chunk_fwd"):
-            gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht, ws=ws_f)
+            if spec.backward:
+                gdn.gdn_chunk_fwd_save(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht,
+                                       ws=ws_f, saved=saved)
+            else:
+                gdn.gdn_chunk_fwd(y, g, beta, local, Hk, Hv, dk, dv, h0=h0, out=o, ht_out=ht,
+                                  ws=ws_f)
         mark(3)
         if spec.backward:
             if run("chunk_bwd"):
-                gdn.gdn_chunk_bwd(y, g, beta, local, Hk, Hv, dk, dv, do, h0=h0, dht=dht, ws=ws_b,
-                                  out=bwd_out)
+                gdn.gdn_chunk_bwd_saved(y, g, beta, local, Hk, Hv, dk, dv, do, saved, h0=h0,
+                                        dht=dht, ws=ws_b, out=bwd_out)
             mark(4)
             if run("conv_bwd"):
                 gdn.gdn_conv1d_silu_halo_bwd(x, w, local, bwd_out[0], halo=halo, meta=m,
@@ -170,7 +179,7 @@ def main():
 
     names = ["localize", "conv_fwd", "chunk_fwd"] + (["chunk_bwd", "conv_bwd"] if spec.backward else [])
     if args.calls:
-        return profile_calls(args, names, step, stream)
+        return profile_calls(args, names, step, stream, spec.backward)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -211,11 +220,13 @@ def main():
         # the forward's moves to the other entries
         t_bwd = per_call["chunk_bwd"] * 1e-3
         bwd_flops = 2 * flops  # reverse mode of the chunk algorithm: twice the forward's products
-        extra["chunk_fwd"] = dict(roofline, kernel="gdn_chunk_fwd call")
+        extra["chunk_fwd"] = dict(roofline, kernel="gdn_chunk_fwd_save call (keeps the "
+                                  "per-chunk states for the backward)")
         roofline = {"bound": "mfma", "achieved": bwd_flops / t_bwd / 1e12, "peak": peak / 1e12,
                     "unit": "TFLOP/s", "frac": bwd_flops / t_bwd / peak,
                     "traffic": measured_traffic("chunk_bwd", spec.name),
-                    "kernel": "gdn_chunk_bwd call: per-chunk states, dS passes, gradients, finalize"}
+                    "kernel": "gdn_chunk_bwd_saved call: plan, dS summaries, scan, dS "
+                              "final pass, gradients (per-chunk states saved by the forward)"}
         bwd_hbm = chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
         extra["chunk_bwd_hbm"] = {"achieved": bwd_hbm / t_bwd / 1e9, "peak": HBM_PEAK / 1e9,
                                   "unit": "GB/s", "frac": bwd_hbm / t_bwd / HBM_PEAK}
@@ -244,17 +255,17 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def profile_calls(args, names, step, stream):
+def profile_calls(args, names, step, stream, fwd_feeds_bwd):
     """Runs the calls that make the named calls' inputs once, then only the
     named calls, so that a profiler sees those calls' kernels alone (the
-    chunk forward's outputs feed no later call, so it is not run as set-up)."""
+    chunk forward is set-up only where its saved states feed the backward)."""
     import torch
     keep = [c.strip() for c in args.calls.split(",") if c.strip()]
     bad = [c for c in keep if c not in names]
     if bad:
         sys.exit("--calls: %s not among %s" % (bad, names))
     first = min(names.index(c) for c in keep)
-    setup = {c for c in names[:first] if c != "chunk_fwd"}
+    setup = {c for c in names[:first] if c != "chunk_fwd" or fwd_feeds_bwd}
     if "conv_bwd" in keep and "chunk_bwd" not in keep:
         setup.add("chunk_bwd")  # dy of the conv backward
     step(only=setup)

@@ -251,6 +251,52 @@ int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v, in
                   int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta, float* dh0,
                   void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream);
 
+/* Bytes of the buffer gdn_chunk_fwd_save fills for gdn_chunk_bwd_saved. */
+size_t gdn_chunk_saved_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                            gdn_dtype dt);
+
+/*
+ * gdn_chunk_fwd that also keeps what gdn_chunk_bwd would otherwise compute
+ * again: the state entering every chunk (activations, [chunks][Hv][dk][dv])
+ * and, for bfloat16, the prepared per-(chunk, value head) records (T =
+ * (I + diag(beta) L)^-1 diag(beta) and the decay factors of the chunk
+ * algorithm of [HP-CP] _prepare_gdn_chunks_for_summary).  The training
+ * pattern of the page's autograd functions: the forward saves, the backward
+ * reads.  o and ht are bit-identical to gdn_chunk_fwd's.
+ *
+ *   saved   device buffer of gdn_chunk_saved_size(...) bytes, 256-byte
+ *           aligned, owned by the caller; its contents are only meaningful
+ *           to gdn_chunk_bwd_saved on the same inputs.
+ *   other arguments as gdn_chunk_fwd (ws: gdn_chunk_workspace_size(..., 0)).
+ * Errors: as gdn_chunk_fwd; GDN_EWORKSPACE also for a null, short or
+ * misaligned saved buffer.
+ */
+int gdn_chunk_fwd_save(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                       const float* g, const float* beta, const float* h0,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk, int32_t Hv,
+                       int32_t dk, int32_t dv, float scale, int use_qk_l2norm, void* o, float* ht,
+                       void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, gdn_dtype dt,
+                       hipStream_t stream);
+
+/*
+ * gdn_chunk_bwd reading the buffer of a gdn_chunk_fwd_save call made with the
+ * same q, k, v, g, beta, h0, cu_seqlens, sizes, scale and l2norm flag: the
+ * forward pipeline (prep, summaries, per-chunk states) is not run again.
+ * Results agree with gdn_chunk_bwd up to rounding (the saved states come
+ * from the forward's own segment plan).  Arguments and results as
+ * gdn_chunk_bwd (ws: gdn_chunk_workspace_size(..., 1)); saved as above.
+ * Errors: as gdn_chunk_bwd; GDN_EINVAL also for a null, short or misaligned
+ * saved buffer.  Nothing checks that the buffer belongs to these inputs.
+ */
+int gdn_chunk_bwd_saved(const void* q, const void* k, int64_t ld_qk, const void* v, int64_t ld_v,
+                        const float* g, const float* beta, const float* h0,
+                        const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk, int32_t Hv,
+                        int32_t dk, int32_t dv, float scale, int use_qk_l2norm, const void* d_o,
+                        const float* dht, void* dq, void* dk_, int64_t ld_dqk, void* dv_,
+                        int64_t ld_dv, float* dg, float* dbeta, float* dh0, const void* saved,
+                        size_t saved_bytes, void* ws, size_t ws_bytes, gdn_dtype dt,
+                        hipStream_t stream);
+
 /*
  * Gating step.  [HP-CP] LinearAttentionP2PCPWrapper.forward (and the
  * all-gather and Ulysses wrappers), the lines that form the decay and the

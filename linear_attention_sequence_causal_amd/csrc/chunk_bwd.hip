@@ -926,25 +926,41 @@ BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, g
   return L;
 }
 
+// saved: the buffer of a saving forward (gdn_chunk_fwd_save) on the same
+// inputs, holding the records and the state entering every chunk; then the
+// forward pipeline is not run again, only its plan.
 template <typename E, int DK, int DV>
 int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayout& L, char* ws,
-               hipStream_t stream) {
+               const char* saved, hipStream_t stream) {
   typedef BwdCfg<E, DK, DV> CF;
+  // a saving forward writes records exactly when this backward reads them
+  static_assert(!std::is_same<E, bf16>::value ||
+                    uses_prep<E, DK, DV, kStates>() == uses_prep<E, DK, DV, kOut>(),
+                "records of the forward and the backward");
   PlanPtrs pp = L.plan.ptrs(ws, true);
   b.counts = pp.counts;
   b.chunk_tab = pp.chunk_tab;
   b.seq_chunk_off = pp.seq_chunk_off;
-  b.states = ws + L.off_states;
   b.dstates = ws + L.off_dstates;
   b.dqk = reinterpret_cast<float*>(ws + L.off_dqk);
-  LoopArgs la = la_in;
-  la.states = ws + L.off_states;
-  if (int rc = run_pipeline<E, DK, DV, kStates>(la, b.cu, N, T, L.plan, ws, true, stream)) return rc;
+  if (saved) {
+    const gdn::SavedLayout SL = gdn::chunk_saved_layout(T, N, b.Hv, DK, DV, std::is_same<E, bf16>::value ? GDN_BF16 : GDN_F32);
+    b.states = saved + SL.off_states;
+    b.rec = uses_prep<E, DK, DV, kStates>() ? saved + SL.off_rec : nullptr;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, b.cu, N, T, (int)L.plan.seg_first,
+                       (int)L.plan.seg_len, (int)L.plan.seg_cap, (int)L.plan.chunk_cap, pp);
+    if (int rc = gdn::check_launch("gdn_chunk_bwd(plan)")) return rc;
+  } else {
+    b.states = ws + L.off_states;
+    LoopArgs la = la_in;
+    la.states = ws + L.off_states;
+    if (int rc = run_pipeline<E, DK, DV, kStates>(la, b.cu, N, T, L.plan, ws, true, stream)) return rc;
+    b.rec = uses_prep<E, DK, DV, kStates>() ? ws + L.plan.off_rec : nullptr;
+  }
   // dS pass over the forward's segments (its summary and initial-state buffers
   // are free again): reverse summaries, reverse scan from dht, final pass
   b.seg_table = pp.table;
   b.seg_chunk0 = pp.seg_chunk0;
-  b.rec = uses_prep<E, DK, DV, kStates>() ? ws + L.plan.off_rec : nullptr;
   b.seg_sum = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_state) : nullptr;
   b.seg_in = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_init) : nullptr;
   const dim3 sgrid((unsigned)L.plan.seg_cap, b.Hv);
@@ -993,30 +1009,36 @@ extern "C" size_t gdn_chunk_workspace_size(int64_t T, int32_t N, int32_t Hk, int
   return bwd_layout(T, N, Hv, dk, dv, dt).end;
 }
 
-extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v,
-                             int64_t ld_v, const float* g, const float* beta, const float* h0,
-                             const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
-                             int32_t Hv, int32_t dk, int32_t dv, float scale, int use_qk_l2norm,
-                             const void* d_o, const float* dht, void* dq, void* dk_,
-                             int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta,
-                             float* dh0, void* ws, size_t ws_bytes, gdn_dtype dt,
-                             hipStream_t stream) {
-  int rc = gdn::validate_chunk("gdn_chunk_bwd", q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk,
-                               Hv, dk, dv, dt);
+namespace {
+
+int chunk_bwd(const char* fn, const void* q, const void* k, int64_t ld_qk, const void* v,
+              int64_t ld_v, const float* g, const float* beta, const float* h0,
+              const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk, int32_t Hv, int32_t dk,
+              int32_t dv, float scale, int use_qk_l2norm, const void* d_o, const float* dht,
+              void* dq, void* dk_, int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg,
+              float* dbeta, float* dh0, const void* saved, size_t saved_bytes, bool use_saved,
+              void* ws, size_t ws_bytes, gdn_dtype dt, hipStream_t stream) {
+  int rc = gdn::validate_chunk(fn, q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk, Hv, dk, dv,
+                               dt);
   if (rc != GDN_OK) return rc;
   const bool have = (dt == GDN_BF16 && dk == dv && (dk == 128 || dk == 64)) ||
                     (dt == GDN_F32 && dk == dv && (dk == 32 || dk == 64));
   if (!have)
     return gdn::fail(GDN_EUNSUPPORTED,
-                     "gdn_chunk_bwd: needs dk == dv (128 or 64 for bfloat16, 32 or 64 for float32)");
+                     "%s: needs dk == dv (128 or 64 for bfloat16, 32 or 64 for float32)", fn);
   if (T > 0 && (!d_o || !dq || !dk_ || !dv_ || !dg || !dbeta))
-    return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: null gradient pointer");
+    return gdn::fail(GDN_EINVAL, "%s: null gradient pointer", fn);
   if (ld_dqk < (int64_t)Hk * dk || ld_dv < (int64_t)Hv * dv)
-    return gdn::fail(GDN_EINVAL, "gdn_chunk_bwd: gradient row strides smaller than the head blocks");
+    return gdn::fail(GDN_EINVAL, "%s: gradient row strides smaller than the head blocks", fn);
   const BwdLayout L = bwd_layout(T, N, Hv, dk, dv, dt);
   if (!ws || ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
-    return gdn::fail(GDN_EWORKSPACE, "gdn_chunk_bwd: workspace needs %zu bytes, 256-byte aligned",
-                     L.end);
+    return gdn::fail(GDN_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, L.end);
+  if (use_saved) {
+    const size_t need = gdn::chunk_saved_layout(T, N, Hv, dk, dv, dt).end;
+    if (!saved || saved_bytes < need || (reinterpret_cast<uintptr_t>(saved) & 255u))
+      return gdn::fail(GDN_EINVAL, "%s: saved buffer needs %zu bytes, 256-byte aligned", fn, need);
+  }
+  const char* sv = use_saved ? static_cast<const char*>(saved) : nullptr;
   if (T == 0 || N == 0) {
     if (dh0 && N > 0) {
       const int64_t n = (int64_t)N * Hv * dk * dv;
@@ -1064,9 +1086,38 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const 
   la.scale = scale;
   la.use_l2norm = b.use_l2norm;
   if (dt == GDN_BF16) {
-    if (dk == 128) return launch_bwd<bf16, 128, 128>(b, la, N, T, L, (char*)ws, stream);
-    return launch_bwd<bf16, 64, 64>(b, la, N, T, L, (char*)ws, stream);
+    if (dk == 128) return launch_bwd<bf16, 128, 128>(b, la, N, T, L, (char*)ws, sv, stream);
+    return launch_bwd<bf16, 64, 64>(b, la, N, T, L, (char*)ws, sv, stream);
   }
-  if (dk == 32) return launch_bwd<float, 32, 32>(b, la, N, T, L, (char*)ws, stream);
-  return launch_bwd<float, 64, 64>(b, la, N, T, L, (char*)ws, stream);
+  if (dk == 32) return launch_bwd<float, 32, 32>(b, la, N, T, L, (char*)ws, sv, stream);
+  return launch_bwd<float, 64, 64>(b, la, N, T, L, (char*)ws, sv, stream);
+}
+
+}  // namespace
+
+extern "C" int gdn_chunk_bwd(const void* q, const void* k, int64_t ld_qk, const void* v,
+                             int64_t ld_v, const float* g, const float* beta, const float* h0,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
+                             int32_t Hv, int32_t dk, int32_t dv, float scale, int use_qk_l2norm,
+                             const void* d_o, const float* dht, void* dq, void* dk_,
+                             int64_t ld_dqk, void* dv_, int64_t ld_dv, float* dg, float* dbeta,
+                             float* dh0, void* ws, size_t ws_bytes, gdn_dtype dt,
+                             hipStream_t stream) {
+  return chunk_bwd("gdn_chunk_bwd", q, k, ld_qk, v, ld_v, g, beta, h0, cu_seqlens, N, T, Hk, Hv, dk,
+                   dv, scale, use_qk_l2norm, d_o, dht, dq, dk_, ld_dqk, dv_, ld_dv, dg, dbeta, dh0,
+                   nullptr, 0, false, ws, ws_bytes, dt, stream);
+}
+
+extern "C" int gdn_chunk_bwd_saved(const void* q, const void* k, int64_t ld_qk, const void* v,
+                                   int64_t ld_v, const float* g, const float* beta,
+                                   const float* h0, const int32_t* cu_seqlens, int32_t N,
+                                   int64_t T, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                                   float scale, int use_qk_l2norm, const void* d_o,
+                                   const float* dht, void* dq, void* dk_, int64_t ld_dqk,
+                                   void* dv_, int64_t ld_dv, float* dg, float* dbeta, float* dh0,
+                                   const void* saved, size_t saved_bytes, void* ws,
+                                   size_t ws_bytes, gdn_dtype dt, hipStream_t stream) {
+  return chunk_bwd("gdn_chunk_bwd_saved", q, k, ld_qk, v, ld_v, g, beta, h0, cu_seqlens, N, T, Hk,
+                   Hv, dk, dv, scale, use_qk_l2norm, d_o, dht, dq, dk_, ld_dqk, dv_, ld_dv, dg,
+                   dbeta, dh0, saved, saved_bytes, true, ws, ws_bytes, dt, stream);
 }

@@ -13,21 +13,23 @@ namespace {
 
 template <typename E, int DK, int DV>
 int launch_fwd(const LoopArgs& a, const int32_t* cu, int N, int64_t T, const Plan& pl, char* ws,
-               hipStream_t stream) {
+               hipStream_t stream, char* rec_buf) {
+  // a saving forward (states set) stores the state entering every chunk
   if (N > 0 && a.ht) {
     hipLaunchKernelGGL(empty_seq_state_kernel, dim3(N, a.Hv), dim3(256), 0, stream, cu, a.h0, a.ht,
                        a.Hv, DK * DV);
     if (int rc = gdn::check_launch("gdn_chunk_fwd(empty)")) return rc;
   }
   if (T == 0 || N == 0) return GDN_OK;
-  return run_pipeline<E, DK, DV, kOut>(a, cu, N, T, pl, ws, false, stream);
+  if (a.states) return run_pipeline<E, DK, DV, kOutSave>(a, cu, N, T, pl, ws, false, stream, rec_buf);
+  return run_pipeline<E, DK, DV, kOut>(a, cu, N, T, pl, ws, false, stream, rec_buf);
 }
 
 template <typename E>
 int dispatch(int dk, int dv, const LoopArgs& a, const int32_t* cu, int N, int64_t T, const Plan& pl,
-             char* ws, hipStream_t stream) {
+             char* ws, hipStream_t stream, char* rec_buf = nullptr) {
 #define GDN_CASE(K_, V_) \
-  if (dk == K_ && dv == V_) return launch_fwd<E, K_, V_>(a, cu, N, T, pl, ws, stream);
+  if (dk == K_ && dv == V_) return launch_fwd<E, K_, V_>(a, cu, N, T, pl, ws, stream, rec_buf);
   if constexpr (sizeof(E) == 2) {
     GDN_CASE(128, 128)
     GDN_CASE(128, 64)
@@ -85,6 +87,18 @@ bool chunk_first_out(int32_t dk, int32_t dv, gdn_dtype dt) { return dt == GDN_BF
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
   if (T < 0 || N < 0 || Hv < 1) return 0;
   return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt), chunk_first_out(dk, dv, dt)).end;
+}
+
+SavedLayout chunk_saved_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv,
+                               gdn_dtype dt) {
+  // every plan of these sizes has the same chunk capacity and chunk order
+  const size_t cap = (size_t)make_plan(T, N, Hv, dk, dv, 0).chunk_cap;
+  const size_t es = dt == GDN_BF16 ? 2 : 4;
+  SavedLayout L;
+  L.off_rec = 0;
+  L.off_states = round_up(chunk_rec_bytes(dt) * cap * Hv, 256);
+  L.end = round_up(L.off_states + es * cap * Hv * dk * dv, 256);
+  return L;
 }
 
 // gdn_gating_fwd's kernel on a stream (gating.hip)
@@ -170,6 +184,40 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const 
   const LoopArgs a = loop_args(q, k, ld_qk, v, ld_v, g, beta, h0, Hk, Hv, scale, use_qk_l2norm, o, ht);
   return dt == GDN_BF16 ? dispatch<bf16>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream)
                         : dispatch<float>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream);
+}
+
+extern "C" size_t gdn_chunk_saved_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                                       int32_t dv, gdn_dtype dt) {
+  (void)Hk;
+  if (T < 0 || N < 0 || Hv < 1 || dk < 1 || dv < 1) return 0;
+  return gdn::chunk_saved_layout(T, N, Hv, dk, dv, dt).end;
+}
+
+extern "C" int gdn_chunk_fwd_save(const void* q, const void* k, int64_t ld_qk, const void* v,
+                                  int64_t ld_v, const float* g, const float* beta, const float* h0,
+                                  const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t Hk,
+                                  int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                  int use_qk_l2norm, void* o, float* ht, void* saved,
+                                  size_t saved_bytes, void* ws, size_t ws_bytes, gdn_dtype dt,
+                                  hipStream_t stream) {
+  const char* fn = "gdn_chunk_fwd_save";
+  int rc = gdn::validate_chunk(fn, q, k, ld_qk, v, ld_v, g, beta, cu_seqlens, N, T, Hk, Hv, dk, dv,
+                               dt);
+  if (rc != GDN_OK) return rc;
+  if ((rc = check_out(fn, o, ht, N, T, cu_seqlens)) != GDN_OK) return rc;
+  const Plan pl = fwd_plan(T, N, Hv, dk, dv, dt);
+  if (!ws || ws_bytes < pl.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return gdn::fail(GDN_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, pl.end);
+  const gdn::SavedLayout SL = gdn::chunk_saved_layout(T, N, Hv, dk, dv, dt);
+  if (!saved || saved_bytes < SL.end || (reinterpret_cast<uintptr_t>(saved) & 255u))
+    return gdn::fail(GDN_EWORKSPACE, "%s: saved buffer needs %zu bytes, 256-byte aligned", fn,
+                     SL.end);
+  LoopArgs a = loop_args(q, k, ld_qk, v, ld_v, g, beta, h0, Hk, Hv, scale, use_qk_l2norm, o, ht);
+  char* sv = static_cast<char*>(saved);
+  a.states = sv + SL.off_states;
+  char* rec = gdn::chunk_rec_bytes(dt) ? sv + SL.off_rec : nullptr;
+  return dt == GDN_BF16 ? dispatch<bf16>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream, rec)
+                        : dispatch<float>(dk, dv, a, cu_seqlens, N, T, pl, (char*)ws, stream, rec);
 }
 
 extern "C" size_t gdn_chunk_fwd_gated_workspace_size(int64_t T, int32_t N, int32_t Hk, int32_t Hv,

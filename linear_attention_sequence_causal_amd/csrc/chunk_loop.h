@@ -48,7 +48,11 @@
 namespace gdn_chunk {
 namespace {
 
-enum Mode { kOut = 0, kSummary = 1, kStates = 2 };
+// kOutSave: the output mode that also stores the state entering every chunk
+// (for a later backward), as kStates does.
+enum Mode { kOut = 0, kSummary = 1, kStates = 2, kOutSave = 3 };
+__host__ __device__ constexpr bool is_out(int mode) { return mode == kOut || mode == kOutSave; }
+__host__ __device__ constexpr bool stores_states(int mode) { return mode == kStates || mode == kOutSave; }
 
 struct LoopArgs {
   const void* q;
@@ -69,8 +73,9 @@ struct LoopArgs {
   const int32_t* seg_chunk0;
   float* seg_state;  // [seg_cap][Hv][DK][DK+DV] summaries
   float* seg_init;   // [seg_cap][Hv][DK][DV] initial states of non-first segments
-  void* states;      // kStates: [chunk_cap][Hv][DK][DV] state entering each chunk, in the
-                     // activation type (the backward uses it as MFMA operands of that type)
+  void* states;      // kStates, kOutSave: [chunk_cap][Hv][DK][DV] state entering each
+                     // chunk, in the activation type (the backward uses it as MFMA
+                     // operands of that type)
   const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
   int seg_cap;       // capacity of the segment table
   int first_done;    // the output of every sequence's first segment is already written
@@ -121,7 +126,7 @@ struct LoopSmem {
 template <typename E, int DK, int DV, int MODE>
 struct LoopCfg {
   typedef E O;  // operand type equals the activation type (bf16 or fp32)
-  static constexpr bool HAS_Q = MODE == kOut;
+  static constexpr bool HAS_Q = is_out(MODE);
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
   static constexpr int NW = NSC / 32;
   static constexpr int NT = NW * 64;
@@ -241,7 +246,7 @@ void chunk_loop_kernel(LoopArgs a) {
   constexpr int NSK = DK / KS;  // contraction steps over dk
   constexpr int NSB = BT / KS;  // contraction steps over the chunk
   constexpr int DKT = DK / 16;  // state row tiles
-  constexpr bool OUT = MODE == kOut;
+  constexpr bool OUT = is_out(MODE);
   typedef typename CF::SM SM;
   __shared__ SM sm;
 
@@ -307,7 +312,7 @@ void chunk_loop_kernel(LoopArgs a) {
     const int lane = tid_c & 63, g4 = lane >> 4, ln = lane & 15;
     lds_barrier();  // the previous chunk's LDS readers are done
     stage_raw(sm, pf, a.scale, a.use_l2norm, tid_c);
-    if constexpr (MODE == kStates) {
+    if constexpr (stores_states(MODE)) {
       // the state entering this chunk, for the backward
       E* dst = (E*)a.states + ((int64_t)(a.seg_chunk0[seg] + c) * Hv + h) * DK * DV;
 #pragma unroll
@@ -541,7 +546,7 @@ struct WsSmem {
 
 template <typename E, int DK, int DV, int MODE>
 struct WsCfg {
-  static constexpr bool OUT = MODE == kOut;
+  static constexpr bool OUT = is_out(MODE);
   static constexpr int NSC = MODE == kSummary ? DK + DV : DV;  // state columns
   // columns per consumer wave: 16 in the output pass (eight consumer waves, two
   // a SIMD, like the summary's), 32 otherwise
@@ -825,7 +830,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     if (it >= 0) {
       SM& C = buf[it & 1];
       const char* R = C.rec;
-      if constexpr (MODE == kStates) {
+      if constexpr (stores_states(MODE)) {
         // the state entering this chunk, for the backward
         E* dst = (E*)a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
 #pragma unroll
@@ -1018,7 +1023,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   typedef typename WsCfg<E, DK, DV, MODE>::SM SM;
   __shared__ SM buf[2];
   __shared__ unsigned p_count;  // loader waves' stored chunks, a running count (P hand-off)
-  if (MODE == kOut) {
+  if (is_out(MODE)) {
     if (threadIdx.x == 0) p_count = 0u;
     __syncthreads();
   }
@@ -1033,18 +1038,18 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
-  if (MODE == kOut && a.first_done && (ent.w & kFirst)) return;
+  if (is_out(MODE) && a.first_done && (ent.w & kFirst)) return;
   ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent, false);
 }
 
 // The summary pass when every sequence's first segment runs the output mode
 // there (from h0) instead of a summary: one launch, the mode chosen per
 // workgroup (both modes have the same waves).
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) void chunk_ws_first_kernel(LoopArgs a) {
-  typedef typename WsCfg<E, DK, DV, kOut>::SM SMO;
+template <typename E, int DK, int DV, int OMODE>
+__global__ __launch_bounds__((WsCfg<E, DK, DV, OMODE>::NT)) void chunk_ws_first_kernel(LoopArgs a) {
+  typedef typename WsCfg<E, DK, DV, OMODE>::SM SMO;
   typedef typename WsCfg<E, DK, DV, kSummary>::SM SMS;
-  static_assert(WsCfg<E, DK, DV, kOut>::NT == WsCfg<E, DK, DV, kSummary>::NT, "one block shape");
+  static_assert(WsCfg<E, DK, DV, OMODE>::NT == WsCfg<E, DK, DV, kSummary>::NT, "one block shape");
   constexpr size_t BYTES = 2 * (sizeof(SMO) > sizeof(SMS) ? sizeof(SMO) : sizeof(SMS));
   __shared__ __attribute__((aligned(16))) char raw[BYTES];
   __shared__ unsigned p_count;
@@ -1057,7 +1062,7 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, kOut>::NT)) void chunk_ws_first_k
   if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (ent.w & kFirst)
-    ws_body<E, DK, DV, kOut>(a, reinterpret_cast<SMO*>(raw), &p_count, seg, h, ent, !(ent.w & kLast));
+    ws_body<E, DK, DV, OMODE>(a, reinterpret_cast<SMO*>(raw), &p_count, seg, h, ent, !(ent.w & kLast));
   else if (!(ent.w & kLast))
     ws_body<E, DK, DV, kSummary>(a, reinterpret_cast<SMS*>(raw), &p_count, seg, h, ent, false);
 }
@@ -1162,10 +1167,11 @@ void launch_loop(const LoopArgs& a, const Plan& pl, hipStream_t stream) {
 }
 
 // Plan, summaries + scan when segments split a sequence, then the final pass
-// in `FINAL` mode (kOut or kStates).  `a` carries the caller's tensors.
+// in `FINAL` mode (kOut, kOutSave or kStates).  `a` carries the caller's tensors;
+// rec_buf, if not null, takes the prepared records instead of the workspace.
 template <typename E, int DK, int DV, int FINAL>
 int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl, char* ws,
-                 bool with_chunks, hipStream_t stream) {
+                 bool with_chunks, hipStream_t stream, char* rec_buf = nullptr) {
   constexpr bool PREP = uses_prep<E, DK, DV, FINAL>();
   PlanPtrs pp = pl.ptrs(ws, with_chunks || PREP);
   a.seg_cap = (int)pl.seg_cap;
@@ -1178,7 +1184,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
                      (int)pl.seg_cap, (int)pl.chunk_cap, pp);
   if (int rc = gdn::check_launch("chunk plan")) return rc;
   if constexpr (PREP) {
-    char* rec = ws + pl.off_rec;
+    char* rec = rec_buf ? rec_buf : ws + pl.off_rec;
     a.rec = rec;
     PrepArgs pa{a.k, a.ld_qk, prep_gates(a), a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab,
                 pp.counts, rec};
@@ -1189,14 +1195,14 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
   a.seg_span = (int)pl.seg_span;
   bool first_out = false;
   if (pl.split) {
-    if constexpr (PREP && FINAL == kOut &&
-                  WsCfg<E, DK, DV, kOut>::NT == WsCfg<E, DK, DV, kSummary>::NT) {
+    if constexpr (PREP && is_out(FINAL) &&
+                  WsCfg<E, DK, DV, FINAL>::NT == WsCfg<E, DK, DV, kSummary>::NT) {
       if (pl.first_out) {
         // first segments run the output mode here, from h0
         const int64_t unit = 8 * (int64_t)(a.Hv / a.Hk);
         const int64_t n = ((int64_t)a.seg_span * a.Hv + unit - 1) / unit * unit;
-        hipLaunchKernelGGL((chunk_ws_first_kernel<E, DK, DV>), dim3((unsigned)n),
-                           dim3(WsCfg<E, DK, DV, kOut>::NT), 0, stream, a);
+        hipLaunchKernelGGL((chunk_ws_first_kernel<E, DK, DV, FINAL>), dim3((unsigned)n),
+                           dim3(WsCfg<E, DK, DV, FINAL>::NT), 0, stream, a);
         first_out = true;
       }
     }

@@ -42,6 +42,16 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt);
 size_t chunk_rec_bytes(gdn_dtype dt);
 
+// The buffer a saving forward (gdn_chunk_fwd_save) fills for the backward
+// (gdn_chunk_bwd_saved): the prepared records ([chunk_cap][Hv] x
+// chunk_rec_bytes, bfloat16 only) and the state entering every chunk
+// ([chunk_cap][Hv][dk][dv] activations), each 256-byte aligned.
+struct SavedLayout {
+  size_t off_rec, off_states, end;
+};
+SavedLayout chunk_saved_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv,
+                               gdn_dtype dt);
+
 // The forward conv with an x token stride (conv.hip).
 int conv_fwd_strided(const void* x, int64_t ldx, const void* w, const void* bias,
                      const void* halo, const int32_t* cu_seqlens, int32_t N, int64_t T, int32_t C,

@@ -38,12 +38,14 @@ ENTRY_POINTS = (
     "gdn_chunk_summary_workspace_size", "gdn_chunk_summary", "gdn_merge_summaries",
     "gdn_conv1d_silu_halo_bwd_noalloc", "gdn_gating_fwd", "gdn_gating_bwd_workspace_size",
     "gdn_gating_bwd", "gdn_chunk_fwd_gated_workspace_size", "gdn_chunk_fwd_gated",
-    "gdn_ulysses_fwd_workspace_size", "gdn_ulysses_fwd", "gdn_last_error",
+    "gdn_ulysses_fwd_workspace_size", "gdn_ulysses_fwd", "gdn_chunk_saved_size",
+    "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_last_error",
 )
 CONV_BWD_SCRATCH_BYTES = 16 << 20  # GDN_CONV_BWD_SCRATCH_BYTES
 _SIZE_QUERIES = ("gdn_conv_bwd_workspace_size", "gdn_chunk_workspace_size",
                  "gdn_chunk_summary_workspace_size", "gdn_gating_bwd_workspace_size",
-                 "gdn_chunk_fwd_gated_workspace_size", "gdn_ulysses_fwd_workspace_size")
+                 "gdn_chunk_fwd_gated_workspace_size", "gdn_ulysses_fwd_workspace_size",
+                 "gdn_chunk_saved_size")
 
 
 class GdnError(RuntimeError):
@@ -80,6 +82,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   INT, P, P, P, SZ, INT, P]
     lib.gdn_chunk_bwd.argtypes = [P, P, I64, P, I64, P, P, P, P, I32, I64, I32, I32, I32, I32, F,
                                   INT, P, P, P, P, I64, P, I64, P, P, P, P, SZ, INT, P]
+    lib.gdn_chunk_saved_size.argtypes = [I64, I32, I32, I32, I32, I32, INT]
+    lib.gdn_chunk_saved_size.restype = SZ
+    lib.gdn_chunk_fwd_save.argtypes = [P, P, I64, P, I64, P, P, P, P, I32, I64, I32, I32, I32, I32,
+                                       F, INT, P, P, P, SZ, P, SZ, INT, P]
+    lib.gdn_chunk_bwd_saved.argtypes = [P, P, I64, P, I64, P, P, P, P, I32, I64, I32, I32, I32, I32,
+                                        F, INT, P, P, P, P, I64, P, I64, P, P, P, P, SZ, P, SZ,
+                                        INT, P]
     lib.gdn_chunk_summary_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, INT]
     lib.gdn_chunk_summary_workspace_size.restype = SZ
     lib.gdn_chunk_summary.argtypes = [P, I64, P, I64, P, P, P, I32, I64, I32, I32, I32, I32, INT,
@@ -323,11 +332,34 @@ def _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv):
     return T, N
 
 
+def chunk_saved_size(T, N, Hk, Hv, dk, dv, dtype) -> int:
+    load_library()
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(_lib.gdn_chunk_saved_size(T, N, Hk, Hv, dk, dv, dt))
+
+
 def gdn_chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0=None, scale=None,
                   use_qk_l2norm=True, want_ht=True, out=None, ht_out=None, ws=None):
     """Chunked gated delta rule on the q/k/v channel blocks of y [T, C].
 
     Returns (o [T, Hv, dv] act, ht [N, Hv, dk, dv] fp32 or None)."""
+    o, ht, _ = _chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0, scale, use_qk_l2norm,
+                          want_ht, out, ht_out, ws, None, False)
+    return o, ht
+
+
+def gdn_chunk_fwd_save(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0=None, scale=None,
+                       use_qk_l2norm=True, want_ht=True, out=None, ht_out=None, ws=None,
+                       saved=None):
+    """gdn_chunk_fwd that also fills ``saved`` (uint8, chunk_saved_size
+    bytes; allocated when None) for gdn_chunk_bwd_saved.  Returns (o, ht,
+    saved)."""
+    return _chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0, scale, use_qk_l2norm, want_ht,
+                      out, ht_out, ws, saved, True)
+
+
+def _chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0, scale, use_qk_l2norm, want_ht, out,
+               ht_out, ws, saved, save):
     load_library()
     T, N = _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv)
     C = y.shape[1]
@@ -342,12 +374,32 @@ def gdn_chunk_fwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, h0=None, scale=None,
     nbytes = chunk_workspace_size(T, N, Hk, Hv, dk, dv, y.dtype)
     ws = _workspace(ws, nbytes, y)
     scale = dk ** -0.5 if scale is None else scale
-    rc = _lib.gdn_chunk_fwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
-                            _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
-                            int(bool(use_qk_l2norm)), _ptr(o), _ptr(ht), _ptr(ws), nbytes,
-                            _dt(y), _stream())
-    _check("gdn_chunk_fwd", rc)
-    return o, ht
+    if not save:
+        rc = _lib.gdn_chunk_fwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
+                                _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
+                                int(bool(use_qk_l2norm)), _ptr(o), _ptr(ht), _ptr(ws), nbytes,
+                                _dt(y), _stream())
+        _check("gdn_chunk_fwd", rc)
+        return o, ht, None
+    sbytes = chunk_saved_size(T, N, Hk, Hv, dk, dv, y.dtype)
+    saved = _saved_buffer(saved, sbytes, y)
+    rc = _lib.gdn_chunk_fwd_save(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
+                                 _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
+                                 int(bool(use_qk_l2norm)), _ptr(o), _ptr(ht), _ptr(saved),
+                                 saved.numel(), _ptr(ws), nbytes, _dt(y), _stream())
+    _check("gdn_chunk_fwd_save", rc)
+    return o, ht, saved
+
+
+def _saved_buffer(saved, nbytes, like):
+    """The saved-state buffer: the caller's (uint8, on like's device, at
+    least nbytes) or a new one."""
+    if saved is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    _req(saved, "saved", torch.uint8, (None,), device=like)
+    if saved.numel() < nbytes:
+        raise ValueError("saved buffer holds %d bytes, needs %d" % (saved.numel(), nbytes))
+    return saved
 
 
 def gdn_chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0=None, dht=None, scale=None,
@@ -356,6 +408,21 @@ def gdn_chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0=None, dht=None
     gradients w.r.t. the q, k, v channel blocks of y), dg, dbeta [T, Hv] fp32
     and dh0 [N, Hv, dk, dv] fp32.  ``out`` may supply (dy, dg, dbeta, dh0)
     and ``ws`` the workspace, so that the call allocates nothing."""
+    return _chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0, dht, scale, use_qk_l2norm,
+                      ws, out, None)
+
+
+def gdn_chunk_bwd_saved(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, saved, h0=None, dht=None,
+                        scale=None, use_qk_l2norm=True, ws=None, out=None):
+    """gdn_chunk_bwd from the buffer of gdn_chunk_fwd_save on the same inputs."""
+    if saved is None:
+        raise ValueError("gdn_chunk_bwd_saved needs the saved buffer")
+    return _chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0, dht, scale, use_qk_l2norm,
+                      ws, out, saved)
+
+
+def _chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0, dht, scale, use_qk_l2norm, ws,
+               out, saved):
     load_library()
     T, N = _chunk_common(y, g, beta, cu_seqlens, h0, Hk, Hv, dk, dv)
     C = y.shape[1]
@@ -377,12 +444,23 @@ def gdn_chunk_bwd(y, g, beta, cu_seqlens, Hk, Hv, dk, dv, d_o, h0=None, dht=None
     nbytes = chunk_workspace_size(T, N, Hk, Hv, dk, dv, y.dtype, bwd=True)
     ws = _workspace(ws, nbytes, y)
     scale = dk ** -0.5 if scale is None else scale
-    rc = _lib.gdn_chunk_bwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
-                            _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
-                            int(bool(use_qk_l2norm)), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk_), C,
-                            _ptr(dv_), C, _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), nbytes,
-                            _dt(y), _stream())
-    _check("gdn_chunk_bwd", rc)
+    if saved is None:
+        rc = _lib.gdn_chunk_bwd(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta), _ptr(h0),
+                                _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv, float(scale),
+                                int(bool(use_qk_l2norm)), _ptr(d_o), _ptr(dht), _ptr(dq),
+                                _ptr(dk_), C, _ptr(dv_), C, _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                _ptr(ws), nbytes, _dt(y), _stream())
+        _check("gdn_chunk_bwd", rc)
+    else:
+        sbytes = chunk_saved_size(T, N, Hk, Hv, dk, dv, y.dtype)
+        saved = _saved_buffer(saved, sbytes, y)
+        rc = _lib.gdn_chunk_bwd_saved(_ptr(q), _ptr(k), C, _ptr(v), C, _ptr(g), _ptr(beta),
+                                      _ptr(h0), _ptr(cu_seqlens), N, T, Hk, Hv, dk, dv,
+                                      float(scale), int(bool(use_qk_l2norm)), _ptr(d_o),
+                                      _ptr(dht), _ptr(dq), _ptr(dk_), C, _ptr(dv_), C, _ptr(dg),
+                                      _ptr(dbeta), _ptr(dh0), _ptr(saved), saved.numel(),
+                                      _ptr(ws), nbytes, _dt(y), _stream())
+        _check("gdn_chunk_bwd_saved", rc)
     return dict(dy=dy, dg=dg, dbeta=dbeta, dh0=dh0)
 
 

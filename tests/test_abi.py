@@ -115,6 +115,34 @@ def test_chunk_rejects_bad_arguments(lib):
     assert b"workspace" in lib.gdn_last_error()
 
 
+def test_saved_pair_rejects_bad_buffers(lib):
+    """gdn_chunk_fwd_save / gdn_chunk_bwd_saved: the saved buffer is checked
+    (null, short, misaligned) before anything is launched."""
+    f = ctypes.c_void_p(0x1000)
+    need = lib.gdn_chunk_saved_size(64, 1, 16, 16, 128, 128, 1)
+    # records (7424 B per chunk and head) and bf16 states, 3 chunk slots
+    assert need >= 3 * 16 * (7424 + 2 * 128 * 128)
+    assert lib.gdn_chunk_saved_size(64, 1, 16, 16, 64, 64, 0) >= 3 * 16 * 4 * 64 * 64
+    assert lib.gdn_chunk_saved_size(-1, 1, 16, 16, 128, 128, 1) == 0
+
+    def fwd(saved, nbytes):
+        return lib.gdn_chunk_fwd_save(f, f, 6144, f, 6144, f, f, None, f, 1, 64, 16, 16, 128, 128,
+                                      0.1, 1, f, None, saved, nbytes, f, 1 << 40, 1, None)
+
+    def bwd(saved, nbytes):
+        return lib.gdn_chunk_bwd_saved(f, f, 6144, f, 6144, f, f, None, f, 1, 64, 16, 16, 128, 128,
+                                       0.1, 1, f, None, f, f, 6144, f, 2048, f, f, None, saved,
+                                       nbytes, f, 1 << 40, 1, None)
+    assert fwd(None, 0) == gdn.GDN_EWORKSPACE
+    assert fwd(f, need - 1) == gdn.GDN_EWORKSPACE
+    assert fwd(ctypes.c_void_p(0x1010), need) == gdn.GDN_EWORKSPACE
+    assert b"saved" in lib.gdn_last_error()
+    assert bwd(None, 0) == gdn.GDN_EINVAL
+    assert bwd(f, need - 1) == gdn.GDN_EINVAL
+    assert bwd(ctypes.c_void_p(0x1010), need) == gdn.GDN_EINVAL
+    assert b"saved" in lib.gdn_last_error()
+
+
 def test_workspace_sizes_are_host_only(lib):
     # sizes are pure host arithmetic; segment summaries appear for long sequences
     small = lib.gdn_chunk_workspace_size(256, 1, 2, 2, 32, 32, 0, 0)

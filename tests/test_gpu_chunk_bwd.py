@@ -3,9 +3,12 @@ oracle's hand-written reverse mode.
 
 Small cases: ragged tails, empty sequences, GQA head sharing (dq, dk summed
 over the value heads of a q/k head), random initial state and final-state
-gradient, l2norm on/off, the segmented state pass.  Workloads: the float32
+gradient, l2norm on/off, the segmented state pass, and the training pair
+gdn_chunk_fwd_save / gdn_chunk_bwd_saved (the forward keeps the per-chunk
+states and records, the backward reads them).  Workloads: the float32
 single sequence and the 4 x 4096 bfloat16 batch end to end (conv forward,
-chunk forward, chunk backward, conv backward) at full size."""
+chunk forward, chunk backward, conv backward) at full size, the latter also
+through the saved pair."""
 
 import numpy as np
 import pytest
@@ -151,3 +154,75 @@ def test_workload_forward_backward(name):
     assert_close("dg(e2e)", f64(r["dg"]), e["dg"], dtype)
     assert_close("dbeta(e2e)", f64(r["dbeta"]), e["dbeta"], dtype)
     assert_close("dh0(e2e)", f64(r["dh0"]), e["dh0"], dtype)
+
+
+SAVED = [
+    # lengths, Hk, Hv, d, dtype, forced segment chunks (0: the plan's own)
+    ([256], 2, 2, 32, torch.float32, 0),
+    ([1, 63, 64, 65, 0, 130], 1, 2, 64, torch.float32, 0),
+    ([300, 0, 77], 2, 4, 128, torch.bfloat16, 0),
+    ([1, 63, 64, 65, 0, 129, 250], 2, 2, 128, torch.bfloat16, 2),
+    ([190, 70], 1, 2, 64, torch.bfloat16, 0),
+    ([3000], 1, 1, 128, torch.bfloat16, 0),  # one sequence: the forward's first-segment plan
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SAVED)))
+def test_saved_pair(ci):
+    """gdn_chunk_fwd_save returns gdn_chunk_fwd's o and ht bit for bit;
+    gdn_chunk_bwd_saved from its buffer matches the oracle and agrees with
+    gdn_chunk_bwd (which recomputes the forward) to the dtype's bar."""
+    lengths, Hk, Hv, d, dtype, seg = SAVED[ci]
+    print("case", SAVED[ci], flush=True)
+    y, g, beta, h0, do, dht, cu = _inputs(200 + ci, lengths, Hk, Hv, d, dtype)
+    yc, gc, bc, h0c = y.cuda(), g.cuda(), beta.cuda(), h0.cuda()
+    cut = cu_tensor(cu)
+    with forced_segments(seg):
+        o1, ht1 = gdn.gdn_chunk_fwd(yc, gc, bc, cut, Hk, Hv, d, d, h0=h0c)
+        o2, ht2, saved = gdn.gdn_chunk_fwd_save(yc, gc, bc, cut, Hk, Hv, d, d, h0=h0c)
+        r1 = gdn.gdn_chunk_bwd(yc, gc, bc, cut, Hk, Hv, d, d, do.cuda(), h0=h0c, dht=dht.cuda())
+        r2 = gdn.gdn_chunk_bwd_saved(yc, gc, bc, cut, Hk, Hv, d, d, do.cuda(), saved, h0=h0c,
+                                     dht=dht.cuda())
+        torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    q, k, v = split_qkv(f64(y), Hk, Hv, d, d)
+    ref = capi.gdn_bwd(q, k, v, f64(g), f64(beta), f64(h0), cu, d ** -0.5, f64(do), f64(dht), True)
+    dq, dk, dv = split_qkv(f64(r2["dy"]), Hk, Hv, d, d)
+    assert_close("dq", dq, ref["dq"], dtype)
+    assert_close("dk", dk, ref["dk"], dtype)
+    assert_close("dv", dv, ref["dv"], dtype)
+    assert_close("dbeta", f64(r2["dbeta"]), ref["dbeta"], dtype)
+    assert_close("dg", f64(r2["dg"]), ref["dg"], dtype)
+    assert_close("dh0", f64(r2["dh0"]), ref["dh0"], dtype)
+    for key in r1:
+        assert_close(key + "(vs recomputed)", f64(r2[key]), f64(r1[key]), dtype)
+
+
+def test_saved_pair_workload():
+    """The 4 x 4096 bfloat16 batch through the saved pair: the backward from
+    the forward's buffer against the oracle and the recomputing backward."""
+    spec = workloads.config("fwdbwd_4x4096_h16_d128_bf16")
+    inp = workloads.make(spec)
+    Hk, Hv, d = spec.Hk, spec.Hv, spec.dk
+    cu = cu_tensor(inp["cu_global"])
+    meta = gdn.make_meta("cuda", n_halo=spec.n_halo)
+    y = gdn.gdn_conv1d_silu_halo(inp["x"].cuda(), inp["w"].cuda(), cu, halo=inp["halo"].cuda(),
+                                 meta=meta)
+    g, beta, h0 = inp["g"].cuda(), inp["beta"].cuda(), inp["h0"].cuda()
+    do, dht = inp["do"].cuda(), inp["dht"].cuda()
+    _, _, saved = gdn.gdn_chunk_fwd_save(y, g, beta, cu, Hk, Hv, d, d, h0=h0)
+    r2 = gdn.gdn_chunk_bwd_saved(y, g, beta, cu, Hk, Hv, d, d, do, saved, h0=h0, dht=dht)
+    r1 = gdn.gdn_chunk_bwd(y, g, beta, cu, Hk, Hv, d, d, do, h0=h0, dht=dht)
+    torch.cuda.synchronize()
+    q, k, v = split_qkv(f64(y), Hk, Hv, d, d)
+    ref = capi.gdn_bwd(q, k, v, f64(inp["g"]), f64(inp["beta"]), f64(inp["h0"]),
+                       inp["cu_global"], d ** -0.5, f64(inp["do"]), f64(inp["dht"]))
+    dq, dk, dv = split_qkv(f64(r2["dy"]), Hk, Hv, d, d)
+    assert_close("dq", dq, ref["dq"], torch.bfloat16)
+    assert_close("dk", dk, ref["dk"], torch.bfloat16)
+    assert_close("dv", dv, ref["dv"], torch.bfloat16)
+    assert_close("dbeta", f64(r2["dbeta"]), ref["dbeta"], torch.bfloat16)
+    assert_close("dg", f64(r2["dg"]), ref["dg"], torch.bfloat16)
+    assert_close("dh0", f64(r2["dh0"]), ref["dh0"], torch.bfloat16)
+    for key in r1:
+        assert_close(key + "(vs recomputed)", f64(r2[key]), f64(r1[key]), torch.bfloat16)
