@@ -721,6 +721,10 @@ struct PHalf {
   }
 };
 
+// log of a transition norm below which a summary's M columns are zero
+// (e^-200 is about 1e-87)
+constexpr float kNegligibleLog = -200.f;
+
 // One (segment, value head) of the state pass in mode MODE, from LDS buffers
 // `buf` and the P hand-off counter (zeroed).  first_summary: the segment is a
 // sequence's first, run in the output mode from h0, and its end state goes to
@@ -826,8 +830,14 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
   }
   const int64_t o_ld = (int64_t)Hv * DV;
   floatx4 x[4][NN], o[OUT ? 4 : 1][NN];
+  // M columns of a summary: once the bound on the log of the transition's
+  // norm accumulated over the segment (the records' lb) is below
+  // kNegligibleLog, |M| < e^kNegligibleLog, far below the smallest bf16 or
+  // fp32 magnitude: M is zero from there on and its waves skip their products
+  float log_norm = 0.f;
+  bool m_zero = false;
   for (int it = -1; it < nchunks; it++) {
-    if (it >= 0) {
+    if (it >= 0 && !(mcol && m_zero)) {
       SM& C = buf[it & 1];
       const char* R = C.rec;
       if constexpr (stores_states(MODE)) {
@@ -871,6 +881,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
       const float* Fd = reinterpret_cast<const float*>(R + kRecF);
       const float* Fk = Fd + 64;
       const float eC = Fd[128];
+      if (mcol) log_norm += Fd[129];
       // x = T (v - fk o (k S)): the right side in accumulator layout (token
       // rows), then one lower-triangular product with T's fragments
 #pragma unroll
@@ -960,6 +971,13 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
         }
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) S[mt][nt] = acc[nt];
+      }
+      if (mcol && log_norm < kNegligibleLog) {
+        m_zero = true;
+#pragma unroll
+        for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) S[mt][nt] = zero4();
       }
       if constexpr (OUT) {
         // o, after the state update's products (which hide the latency of

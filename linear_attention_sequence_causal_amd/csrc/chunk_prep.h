@@ -37,7 +37,11 @@ namespace gdn_chunk {
 // Record of one (chunk, value head), bytes:
 //   [kRecT, +6 KiB)  T as six 16x16x32 A fragments (16 B a lane): row block
 //                    mt, contraction half s, for (mt, s) in p_frag order
-//   [kRecF, kRecG)   fd[64], fk[64], eC (fp32)
+//   [kRecF, kRecG)   fd[64], fk[64], eC, lb (fp32): lb bounds the log of the
+//                    norm of the chunk's state transition (G_C when every
+//                    write strength is in [0, 1] and k is l2-normalised, each
+//                    token's map then being e^g times a contraction; else
+//                    +inf: no bound)
 //   [kRecG, kRecEnd) G[64], rk[64] (fp32; read by the output pass only)
 constexpr int kRecT = 0;
 constexpr int kRecF = 6 * 1024;
@@ -253,6 +257,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GDN_PREP_WA
       F32[lane] = sm.rk[lane] * __expf(GC - Gv);  // fd
       F32[64 + lane] = fkv;                       // fk
       if (lane == 0) F32[128] = __expf(GC);       // eC
+      // every valid token's beta in [0, 1] (past the end beta = 0)
+      const bool contract = a.use_l2norm && __all(bv >= 0.f && bv <= 1.f);
+      if (lane == 0) F32[129] = contract ? GC : __builtin_inff();  // lb
       float* G32 = reinterpret_cast<float*>(rec + kRecG);
       G32[lane] = Gv;
       G32[64 + lane] = sm.rk[lane];
