@@ -81,8 +81,16 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
 // bytes of the prepared record per (chunk, value head): bfloat16 only
 size_t chunk_rec_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? (size_t)kRecBytes : 0; }
 
-// the summary pass can run first segments in the output mode (same block shape)
-bool chunk_first_out(int32_t dk, int32_t dv, gdn_dtype dt) { return dt == GDN_BF16 && dk == 128 && dv == 128; }
+// the summary pass can run first segments in the output mode (same block
+// shape).  Not used: with equal segments, sequences whose heads replay (no
+// summaries) finish in one output pass, which the first-segment plan's
+// shorter first segment would lengthen.
+bool chunk_first_out(int32_t dk, int32_t dv, gdn_dtype dt) {
+  (void)dk;
+  (void)dv;
+  (void)dt;
+  return false;
+}
 
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
   if (T < 0 || N < 0 || Hv < 1) return 0;

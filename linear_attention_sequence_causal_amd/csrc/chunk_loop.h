@@ -81,6 +81,13 @@ struct LoopArgs {
   int first_done;    // the output of every sequence's first segment is already written
   int seg_base, seg_span;  // the state-pass grid covers segments seg_base .. + seg_span - 1
   int summary_all;         // kSummary: summarise a sequence's last segment too
+  // replay (warm_kernel): per (segment, head) the chunks before the segment
+  // that its final pass replays from a zero state (| kWarmFromStart: from
+  // the sequence start, with h0); per (sequence, head) 1 when every segment
+  // but the first replays, and then no summary or scan is needed.  Null:
+  // summaries and scan as usual.
+  const int32_t* warm;
+  const int32_t* seq_warm;
   // gates formed from projections in the prep (ga non-null; bf16 prep
   // path), else the prep reads g, beta
   const void* ga;
@@ -254,6 +261,8 @@ void chunk_loop_kernel(LoopArgs a) {
   if (seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
+  // a replaying sequence needs no summaries
+  if (MODE == kSummary && a.seq_warm && a.seq_warm[(int64_t)ent.x * a.Hv + h]) return;
   const int n = ent.x;
   const int64_t tb = ent.y, te = ent.z;
   const int Hv = a.Hv;
@@ -725,6 +734,58 @@ struct PHalf {
 // (e^-200 is about 1e-87)
 constexpr float kNegligibleLog = -200.f;
 
+// Replay instead of summaries.  The state entering a segment is S = M_W S' +
+// E_W over the W chunks before it, S' the state W chunks earlier.  When the
+// records' bound on log |M_W| (the sum of their lb) is below kNegligibleLog,
+// M_W S' is below 1e-87 |S'|: the state is E_W, the recurrence over those W
+// chunks from zero, to far below the resolution of fp32.  A segment's final
+// pass then replays those chunks itself (or, reaching the sequence start,
+// runs from h0 exactly), and the sequence needs no summaries or scan.
+constexpr int kWarmMax = 16;                 // longest replay tried, chunks
+constexpr int32_t kWarmFromStart = 1 << 30;  // replay from the sequence start
+
+// Per (sequence, head): the replay length of every segment but the first,
+// -1 when the bound is not reached within kWarmMax chunks; seq_warm = 1 when
+// none is -1.
+__global__ __launch_bounds__(256) void warm_kernel(const char* __restrict__ rec, int Hv,
+                                                   const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ seg_chunk0,
+                                                   const int32_t* __restrict__ seq_off,
+                                                   const int32_t* __restrict__ seq_nseg,
+                                                   const int32_t* __restrict__ seq_chunk_off,
+                                                   int seg_cap, int32_t* __restrict__ warm,
+                                                   int32_t* __restrict__ seq_warm) {
+  const int n = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int off = seq_off[n], nseg = seq_nseg[n], c0 = seq_chunk_off[n];
+  const int nchunks = counts[1];
+  int cold = 0;
+  for (int p = 1 + t; p < nseg; p += 256) {
+    const int s = off + p;
+    if (s >= seg_cap) break;
+    const int cb = seg_chunk0[s];
+    int val = -1;
+    float sum = 0.f;
+    for (int w = 0; w < kWarmMax; w++) {
+      const int c = cb - 1 - w;
+      if (c < c0) {  // the sequence start: replay all of it, from h0
+        val = w | kWarmFromStart;
+        break;
+      }
+      if (c >= nchunks) break;
+      sum += *reinterpret_cast<const float*>(rec + ((int64_t)c * Hv + h) * kRecBytes + kRecF +
+                                             129 * sizeof(float));
+      if (sum < kNegligibleLog) {
+        val = w + 1;
+        break;
+      }
+    }
+    warm[(int64_t)s * Hv + h] = val;
+    cold |= val < 0;
+  }
+  cold = __syncthreads_or(cold);
+  if (t == 0) seq_warm[(int64_t)n * Hv + h] = cold ? 0 : 1;
+}
+
 // One (segment, value head) of the state pass in mode MODE, from LDS buffers
 // `buf` and the P hand-off counter (zeroed).  first_summary: the segment is a
 // sequence's first, run in the output mode from h0, and its end state goes to
@@ -757,6 +818,15 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
   const int nchunks = (int)((te - tb + BT - 1) / BT);
   const int chunk0 = a.seg_chunk0[seg];
   const char* recs = a.rec + (int64_t)h * kRecBytes;  // + chunk * Hv * kRecBytes
+  // final passes of a replaying sequence: the chunks before the segment run
+  // first (no outputs), from zero or, reaching the sequence start, from h0
+  int nwarm = 0;
+  bool warm_h0 = false;
+  if (MODE != kSummary && a.seq_warm && !(ent.w & kFirst) && a.seq_warm[(int64_t)n * Hv + h]) {
+    const int v = a.warm[(int64_t)seg * Hv + h];
+    nwarm = v & ~kWarmFromStart;
+    warm_h0 = (v & kWarmFromStart) != 0;
+  }
 
   if (wave >= NC) {
     // ======================= loaders =======================
@@ -769,14 +839,17 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     const int64_t rstride = (int64_t)Hv * kRecBytes;
     const typename LD::Off off = LD::offsets(a.ld_qk, a.ld_v, ltid);
     LD ld;
-    if (nchunks > 0) ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + chunk0 * rstride, tb, te, off, ltid);
-    for (int it = -1; it < nchunks; it++) {
+    // segment chunk pc (from -nwarm: the replayed ones) goes to buffer pc & 1
+    if (nchunks > 0)
+      ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (int64_t)(chunk0 - nwarm) * rstride,
+              tb - (int64_t)nwarm * BT, te, off, ltid);
+    for (int it = -1 - nwarm; it < nchunks; it++) {
       const int pc = it + 1;
       if (pc < nchunks) {
         SM& B = buf[pc & 1];
         ld.store(B, ltid, a.scale, a.use_l2norm);
         if (pc + 1 < nchunks)
-          ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (chunk0 + pc + 1) * rstride,
+          ld.load(qp, kp, a.ld_qk, vp, a.ld_v, recs + (int64_t)(chunk0 + pc + 1) * rstride,
                   tb + (int64_t)(pc + 1) * BT, te, off, ltid);
         if constexpr (OUT) {
           // P and fo of the chunk just stored, made here while the consumers
@@ -785,7 +858,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
           // three halves of P (all products issued before any is finished)
           const int lw = wave - NC;
           count_arrive(&p_count, lane);
-          count_wait(&p_count, (unsigned)NL * (unsigned)(pc + 1));
+          count_wait(&p_count, (unsigned)NL * (unsigned)(pc + nwarm + 1));
           constexpr int NR = kPHalves / NL;
           PHalf<DK> ph[NR];
 #pragma unroll
@@ -812,8 +885,10 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
   {
     const float* src = nullptr;
     if (MODE != kSummary) {
-      if (!(ent.w & kFirst)) src = a.seg_init + ((int64_t)seg * Hv + h) * DK * DV;
-      else if (a.h0) src = a.h0 + ((int64_t)n * Hv + h) * DK * DV;
+      const float* h0n = a.h0 ? a.h0 + ((int64_t)n * Hv + h) * DK * DV : nullptr;
+      if (nwarm > 0) src = warm_h0 ? h0n : nullptr;
+      else if (!(ent.w & kFirst)) src = a.seg_init + ((int64_t)seg * Hv + h) * DK * DV;
+      else src = h0n;
     }
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
@@ -836,11 +911,12 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
   // fp32 magnitude: M is zero from there on and its waves skip their products
   float log_norm = 0.f;
   bool m_zero = false;
-  for (int it = -1; it < nchunks; it++) {
-    if (it >= 0 && !(mcol && m_zero)) {
-      SM& C = buf[it & 1];
+  // one chunk (buffer C, chunk it of the segment); EMIT false: a replayed
+  // chunk, the state update only
+  auto step = [&](auto emit, SM& C, const int it) {
+    constexpr bool EMIT = decltype(emit)::value;
       const char* R = C.rec;
-      if constexpr (stores_states(MODE)) {
+      if constexpr (stores_states(MODE) && EMIT) {
         // the state entering this chunk, for the backward
         E* dst = (E*)a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
 #pragma unroll
@@ -857,7 +933,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
 #pragma unroll
         for (int nt = 0; nt < NN; nt++) {
           x[mt][nt] = zero4();
-          if constexpr (OUT) o[mt][nt] = zero4();
+          if constexpr (OUT && EMIT) o[mt][nt] = zero4();
         }
 #pragma unroll
       for (int s = 0; s < NSK; s++) {
@@ -869,7 +945,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
           const Fr kf = M::load_k8(C.k, SM::LDK, 16 * mt, s * KS, lane);
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
-          if constexpr (OUT) {
+          if constexpr (OUT && EMIT) {
             // o^T = S^T q^T: the state fragment is the A operand (its column
             // index is the row of the product), q rows the B operand
             const Fr qf = M::load_k8(C.q, SM::LDK, 16 * mt, s * KS, lane);
@@ -917,7 +993,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
             for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], tf, ys[s][nt]);
           }
       }
-      if constexpr (OUT) {
+      if constexpr (OUT && EMIT) {
         // o^T = fo o (S^T q^T) + x^T P^T.  Tile o[mt][nt] holds value columns
         // c0 + 16 nt + 4(lane/16) + j of token 16 mt + lane%16, so fo is one
         // factor per lane, x fragments are the A operands and the P fragments
@@ -979,7 +1055,7 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
 #pragma unroll
           for (int nt = 0; nt < NN; nt++) S[mt][nt] = zero4();
       }
-      if constexpr (OUT) {
+      if constexpr (OUT && EMIT) {
         // o, after the state update's products (which hide the latency of
         // the last o products): four consecutive value columns of one token
         // per lane, one 8-byte (bf16) store per tile, straight to HBM
@@ -1005,7 +1081,14 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
           }
         }
       }
-    }
+  };
+  lds_barrier();  // the first chunk is published
+  for (int it = -nwarm; it < 0; it++) {
+    step(std::false_type{}, buf[it & 1], it);
+    lds_barrier();
+  }
+  for (int it = 0; it < nchunks; it++) {
+    if (!(mcol && m_zero)) step(std::true_type{}, buf[it & 1], it);
     lds_barrier();
   }
 
@@ -1056,6 +1139,8 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
+  // a replaying sequence needs no summaries
+  if (MODE == kSummary && a.seq_warm && a.seq_warm[(int64_t)ent.x * a.Hv + h]) return;
   if (is_out(MODE) && a.first_done && (ent.w & kFirst)) return;
   ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent, false);
 }
@@ -1097,7 +1182,8 @@ __global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restric
                                                           float* __restrict__ seg_init,
                                                           const float* __restrict__ h0,
                                                           const int32_t* __restrict__ seq_off,
-                                                          const int32_t* __restrict__ seq_nseg, int Hv) {
+                                                          const int32_t* __restrict__ seq_nseg, int Hv,
+                                                          const int32_t* __restrict__ seq_warm = nullptr) {
   typedef Mfma<float> M;
   constexpr int LDX = DK + DV;
   constexpr int NKT = DK / 16;
@@ -1105,6 +1191,7 @@ __global__ __launch_bounds__(DK * 2) void seg_scan_kernel(const float* __restric
   const int n = blockIdx.x, h = blockIdx.y, cb = blockIdx.z * 16;
   const int nseg = seq_nseg[n];
   if (nseg <= 1) return;
+  if (seq_warm && seq_warm[(int64_t)n * Hv + h]) return;  // replayed, no summaries
   const int off = seq_off[n];
   __shared__ float hs[DK][16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -1207,6 +1294,18 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
     PrepArgs pa{a.k, a.ld_qk, prep_gates(a), a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab,
                 pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
+    if (pl.split) {
+      // per (sequence, head): replay instead of summaries where the records'
+      // bounds allow it
+      int32_t* warm = reinterpret_cast<int32_t*>(ws + pl.off_warm);
+      int32_t* seq_warm = reinterpret_cast<int32_t*>(ws + pl.off_seq_warm);
+      hipLaunchKernelGGL(warm_kernel, dim3(N, a.Hv), dim3(256), 0, stream, rec, a.Hv, pp.counts,
+                         pp.seg_chunk0, pp.seq_off, pp.seq_nseg, pp.seq_chunk_off, (int)pl.seg_cap,
+                         warm, seq_warm);
+      if (int rc = gdn::check_launch("chunk replay table")) return rc;
+      a.warm = warm;
+      a.seq_warm = seq_warm;
+    }
   }
   a.first_done = 0;
   a.seg_base = 0;
@@ -1227,7 +1326,7 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
     if (!first_out) launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;
     hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(DK * 2), 0, stream,
-                       a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv);
+                       a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv, a.seq_warm);
     if (int rc = gdn::check_launch("chunk scan")) return rc;
     a.first_done = first_out ? 1 : 0;
   }

@@ -132,7 +132,7 @@ struct Plan {
   int64_t seg_cap, chunk_cap;
   bool split;  // some sequence may have more than one segment
   size_t off_counts, off_table, off_seg_chunk0, off_seq_off, off_seq_nseg, off_seq_chunk_off,
-      off_chunk_tab, off_state, off_init, off_rec, end;
+      off_chunk_tab, off_state, off_init, off_rec, off_warm, off_seq_warm, end;
 
   PlanPtrs ptrs(char* ws, bool with_chunks) const {
     PlanPtrs p;
@@ -228,6 +228,11 @@ inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, 
   p.off_state = take(p.split || summaries ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * (dk + dv) : 0);
   p.off_init = take(p.split ? sizeof(float) * (size_t)p.seg_cap * Hv * dk * dv : 0);
   p.off_rec = take(rec_bytes * (size_t)p.chunk_cap * Hv);
+  // replay lengths per (segment, head) and the per-(sequence, head) choice
+  // of the replay over the summaries (prepared path, split sequences)
+  const bool warm = rec_bytes > 0 && p.split;
+  p.off_warm = take(warm ? 4 * (size_t)p.seg_cap * Hv : 0);
+  p.off_seq_warm = take(warm ? 4 * (size_t)N * Hv : 0);
   p.end = o;
   return p;
 }
