@@ -81,20 +81,9 @@ int validate_chunk(const char* fn, const void* q, const void* k, int64_t ld_qk, 
 // bytes of the prepared record per (chunk, value head): bfloat16 only
 size_t chunk_rec_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? (size_t)kRecBytes : 0; }
 
-// the summary pass can run first segments in the output mode (same block
-// shape).  Not used: with equal segments, sequences whose heads replay (no
-// summaries) finish in one output pass, which the first-segment plan's
-// shorter first segment would lengthen.
-bool chunk_first_out(int32_t dk, int32_t dv, gdn_dtype dt) {
-  (void)dk;
-  (void)dv;
-  (void)dt;
-  return false;
-}
-
 size_t chunk_fwd_workspace(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
   if (T < 0 || N < 0 || Hv < 1) return 0;
-  return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt), chunk_first_out(dk, dv, dt)).end;
+  return make_plan(T, N, Hv, dk, dv, chunk_rec_bytes(dt)).end;
 }
 
 SavedLayout chunk_saved_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv,
@@ -164,7 +153,7 @@ int check_out(const char* fn, void* o, float* ht, int32_t N, int64_t T, const in
 }
 
 Plan fwd_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
-  return make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), gdn::chunk_first_out(dk, dv, dt));
+  return make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt));
 }
 
 // the gated forward's gate buffers (g, beta [T, Hv] float32) after the plan,

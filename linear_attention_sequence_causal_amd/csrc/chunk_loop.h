@@ -78,8 +78,7 @@ struct LoopArgs {
                      // operands of that type)
   const char* rec;   // prepared chunk records [chunk_cap][Hv] (bf16 state pass)
   int seg_cap;       // capacity of the segment table
-  int first_done;    // the output of every sequence's first segment is already written
-  int seg_base, seg_span;  // the state-pass grid covers segments seg_base .. + seg_span - 1
+  int seg_span;      // the state-pass grid covers segments 0 .. seg_span - 1
   int summary_all;         // kSummary: summarise a sequence's last segment too
   // replay (warm_kernel): per (segment, head) the chunks before the segment
   // that its final pass replays from a zero state (| kWarmFromStart: from
@@ -787,12 +786,10 @@ __global__ __launch_bounds__(256) void warm_kernel(const char* __restrict__ rec,
 }
 
 // One (segment, value head) of the state pass in mode MODE, from LDS buffers
-// `buf` and the P hand-off counter (zeroed).  first_summary: the segment is a
-// sequence's first, run in the output mode from h0, and its end state goes to
-// the segment summaries as [0 | S] (for the scan).
+// `buf` and the P hand-off counter (zeroed).
 template <typename E, int DK, int DV, int MODE>
 GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf, unsigned* p_count_ptr,
-                     int seg, int h, int4 ent, bool first_summary) {
+                     int seg, int h, int4 ent) {
   typedef WsCfg<E, DK, DV, MODE> CF;
   typedef E O;
   typedef Mfma<O> M;
@@ -1092,17 +1089,12 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     lds_barrier();
   }
 
-  // final state: ht (output), the summary X = [M | E], or for a first segment
-  // run from h0 the summary [0 | S]
+  // final state: ht (output) or the summary X = [M | E]
   float* dst = nullptr;
   int ld = DV;
-  if (MODE == kSummary || first_summary) {
+  if (MODE == kSummary) {
     dst = a.seg_state + ((int64_t)seg * Hv + h) * DK * (DK + DV);
     ld = DK + DV;
-    if (first_summary) {
-      for (int i = tid; i < DK * DK; i += NC * 64) dst[(i / DK) * (DK + DV) + i % DK] = 0.f;
-      dst += DK;
-    }
   } else if ((ent.w & kLast) && a.ht) {
     dst = a.ht + ((int64_t)n * Hv + h) * DK * DV;
   }
@@ -1131,43 +1123,17 @@ __global__ __launch_bounds__((WsCfg<E, DK, DV, MODE>::NT)) void chunk_ws_kernel(
   // Workgroup order: the value heads of one q/k head and segment take ids 8
   // apart, so they run together on one XCD (ids go round-robin over the 8
   // XCDs) and share q and k through its L2; with a span of 8 segments, XCD x
-  // runs segment seg_base + x of every head.
+  // runs segment x of every head.
   const int GR = a.Hv / a.Hk;
   const int id = blockIdx.x;
   const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
-  const int seg = a.seg_base + grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
+  const int seg = grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
   if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
   const int4 ent = a.seg_table[seg];
   if (MODE == kSummary && (ent.w & kLast) && !a.summary_all) return;
   // a replaying sequence needs no summaries
   if (MODE == kSummary && a.seq_warm && a.seq_warm[(int64_t)ent.x * a.Hv + h]) return;
-  if (is_out(MODE) && a.first_done && (ent.w & kFirst)) return;
-  ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent, false);
-}
-
-// The summary pass when every sequence's first segment runs the output mode
-// there (from h0) instead of a summary: one launch, the mode chosen per
-// workgroup (both modes have the same waves).
-template <typename E, int DK, int DV, int OMODE>
-__global__ __launch_bounds__((WsCfg<E, DK, DV, OMODE>::NT)) void chunk_ws_first_kernel(LoopArgs a) {
-  typedef typename WsCfg<E, DK, DV, OMODE>::SM SMO;
-  typedef typename WsCfg<E, DK, DV, kSummary>::SM SMS;
-  static_assert(WsCfg<E, DK, DV, OMODE>::NT == WsCfg<E, DK, DV, kSummary>::NT, "one block shape");
-  constexpr size_t BYTES = 2 * (sizeof(SMO) > sizeof(SMS) ? sizeof(SMO) : sizeof(SMS));
-  __shared__ __attribute__((aligned(16))) char raw[BYTES];
-  __shared__ unsigned p_count;
-  if (threadIdx.x == 0) p_count = 0u;
-  __syncthreads();
-  const int GR = a.Hv / a.Hk;
-  const int id = blockIdx.x;
-  const int grp = (id / (8 * GR)) * 8 + (id & 7), member = (id >> 3) % GR;
-  const int seg = a.seg_base + grp % a.seg_span, h = (grp / a.seg_span) * GR + member;
-  if (grp >= a.seg_span * a.Hk || seg >= a.counts[0]) return;
-  const int4 ent = a.seg_table[seg];
-  if (ent.w & kFirst)
-    ws_body<E, DK, DV, OMODE>(a, reinterpret_cast<SMO*>(raw), &p_count, seg, h, ent, !(ent.w & kLast));
-  else if (!(ent.w & kLast))
-    ws_body<E, DK, DV, kSummary>(a, reinterpret_cast<SMS*>(raw), &p_count, seg, h, ent, false);
+  ws_body<E, DK, DV, MODE>(a, buf, &p_count, seg, h, ent);
 }
 
 // Scan over segment summaries (fp32): per (sequence, head, 16 columns),
@@ -1307,33 +1273,14 @@ int run_pipeline(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl
       a.seq_warm = seq_warm;
     }
   }
-  a.first_done = 0;
-  a.seg_base = 0;
   a.seg_span = (int)pl.seg_span;
-  bool first_out = false;
   if (pl.split) {
-    if constexpr (PREP && is_out(FINAL) &&
-                  WsCfg<E, DK, DV, FINAL>::NT == WsCfg<E, DK, DV, kSummary>::NT) {
-      if (pl.first_out) {
-        // first segments run the output mode here, from h0
-        const int64_t unit = 8 * (int64_t)(a.Hv / a.Hk);
-        const int64_t n = ((int64_t)a.seg_span * a.Hv + unit - 1) / unit * unit;
-        hipLaunchKernelGGL((chunk_ws_first_kernel<E, DK, DV, FINAL>), dim3((unsigned)n),
-                           dim3(WsCfg<E, DK, DV, FINAL>::NT), 0, stream, a);
-        first_out = true;
-      }
-    }
-    if (!first_out) launch_loop<E, DK, DV, kSummary>(a, pl, stream);
+    launch_loop<E, DK, DV, kSummary>(a, pl, stream);
     if (int rc = gdn::check_launch("chunk summary")) return rc;
     hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3(N, a.Hv, DV / 16), dim3(DK * 2), 0, stream,
                        a.seg_state, a.seg_init, a.h0, pp.seq_off, pp.seq_nseg, a.Hv, a.seq_warm);
     if (int rc = gdn::check_launch("chunk scan")) return rc;
-    a.first_done = first_out ? 1 : 0;
   }
-  // the output pass: segments out_base .. when the first segments are done,
-  // else every segment
-  a.seg_base = first_out ? (int)pl.out_base : 0;
-  a.seg_span = first_out ? (int)pl.seg_span : (int)pl.seg_cap;
   launch_loop<E, DK, DV, FINAL>(a, pl, stream);
   return gdn::check_launch("chunk loop");
 }
@@ -1464,8 +1411,6 @@ int run_summary(LoopArgs a, const int32_t* cu, int N, int64_t T, const Plan& pl,
     PrepArgs pa{a.k, a.ld_qk, prep_gates(a), a.Hk, a.Hv, a.use_l2norm, pp.chunk_tab, pp.counts, rec};
     if (int rc = launch_prep<DK>(pa, pl.chunk_cap, stream)) return rc;
   }
-  a.first_done = 0;
-  a.seg_base = 0;
   a.seg_span = (int)pl.seg_span;
   a.summary_all = 1;
   launch_loop<E, DK, DV, kSummary>(a, pl, stream);

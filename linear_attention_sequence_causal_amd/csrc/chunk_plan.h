@@ -125,10 +125,8 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 // Host-side layout of the plan inside a workspace.
 struct Plan {
   int64_t seg_first, seg_len;
-  bool first_out;  // a sequence's first segment runs the output mode in the summary pass
-  // segment indices a state-pass launch covers (its grid): seg_span of them
-  // from 0 (summary pass) or from out_base (output pass)
-  int64_t seg_span, out_base;
+  // segment indices a state-pass launch covers (its grid)
+  int64_t seg_span;
   int64_t seg_cap, chunk_cap;
   bool split;  // some sequence may have more than one segment
   size_t off_counts, off_table, off_seg_chunk0, off_seq_off, off_seq_nseg, off_seq_chunk_off,
@@ -150,66 +148,44 @@ struct Plan {
 // Segment lengths from the device size and the number of (sequence, head)
 // chains (a test hook on the calling thread can force them).  rec_bytes: bytes of the
 // prepared record per (chunk, value head), 0 when the state pass takes none.
-// first_out: the caller can run a sequence's first segment in the output mode
-// during the summary pass (from h0).  summaries: the plan of a shard summary,
-// which keeps every segment's [M | E].
+// summaries: the plan of a shard summary, which keeps every segment's [M | E].
 //
 // A state-pass workgroup takes most of a CU's LDS, so one runs per CU.  Each
 // XCD hands its share of a grid (ids x mod 8 go to XCD x) to its CUs in a
 // fixed rotation, also the workgroups that exit at once: more than one
 // workgroup per CU in a grid can put two long-running ones on one CU.  For a
 // single sequence the grids therefore hold exactly CUs / Hv segment indices a
-// head.  With first_out the first segment is shorter (kFirstRatio of the
-// others, the measured cost of a summary chunk against an output chunk): the
-// summary pass covers segments 0 .. B-1 (the first in the output mode), the
-// output pass segments 1 .. B, B = CUs / Hv.
-constexpr int kFirstRatioNum = 77, kFirstRatioDen = 100;
+// head, equal segments.
 inline Plan make_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, size_t rec_bytes,
-                      bool first_out = false, bool summaries = false) {
+                      bool summaries = false) {
   Plan p{};
   const int64_t chunks = (T + 63) / 64 + N;  // bound on chunk count over all sequences
-  int64_t per = 1, first = 1, span = 0;
+  int64_t per = 1, span = 0;
   const int forced = gdn::segment_chunks_override();
-  p.first_out = false;
   const int64_t C = (T + 63) / 64 + N - 1;
   const int64_t cus = gdn::device_cu_count();
   if (forced > 0) {
-    per = first = forced;
+    per = forced;
   } else if (N == 1) {
     const int64_t B = cus / Hv > 1 ? cus / Hv : 1;
-    if (first_out && B > 1) {
-      per = (C * kFirstRatioDen + B * kFirstRatioDen + kFirstRatioNum - 1) /
-            (B * kFirstRatioDen + kFirstRatioNum);
-      if (per < 1) per = 1;
-      first = per * kFirstRatioNum / kFirstRatioDen;
-      if (first < 1) first = 1;
-      while (first + B * per < C) per++;
-      p.first_out = true;
-      span = B;
-    } else {
-      per = first = C > B ? (C + B - 1) / B : 1;
-      span = C > 0 ? (C + per - 1) / per : 1;
-    }
+    per = C > B ? (C + B - 1) / B : 1;
+    span = C > 0 ? (C + per - 1) / per : 1;
   } else {
     // several sequences: segments per head at most ceil(C / per) + N - 1
     const int64_t slots = cus * 15 / 16;
     const int64_t budget = slots / Hv > 1 ? slots / Hv : 1;
     per = budget > N ? (C + (budget - N + 1) - 1) / (budget - N + 1) : C + 1;
     if (per < 1) per = 1;
-    first = per;
   }
-  p.seg_first = first * 64;
+  p.seg_first = per * 64;
   p.seg_len = per * 64;
   p.split = p.seg_first < T;
-  p.first_out = p.first_out && p.split;
   if (N == 1 && span > 0) {
-    p.seg_cap = p.first_out ? span + 1 : span;
-    p.seg_span = span;
+    p.seg_cap = span;
   } else {
     p.seg_cap = T / p.seg_len + N + 2;
-    p.seg_span = p.seg_cap;
   }
-  p.out_base = p.first_out ? 1 : 0;
+  p.seg_span = p.seg_cap;
   p.chunk_cap = chunks + 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {

@@ -13,7 +13,7 @@ using namespace gdn_chunk;
 namespace {
 
 Plan summary_plan(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
-  return make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), false, true);
+  return make_plan(T, N, Hv, dk, dv, gdn::chunk_rec_bytes(dt), true);
 }
 
 template <typename E>

@@ -3,7 +3,8 @@
 Small cases: several chunks and ragged tails (lengths 1, 63, 64, 65, ...),
 empty sequences, GQA head sharing, random initial states, l2norm on/off,
 float32 and bfloat16, and forced segmentation (the affine-summary path with
-1-3 chunks per segment); closed forms (beta = 0, total decay).  Workloads:
+1-3 chunks per segment, and the replay of the chunks before a segment where
+the decay bounds allow it); closed forms (beta = 0, total decay).  Workloads:
 each benchmark configuration at full size on every value head, per stage and
 end to end from x, and the long one also with weak or no decay."""
 
@@ -81,14 +82,39 @@ def test_segmented(seg, dtype):
 
 @pytest.mark.parametrize("length", [2000, 4097])
 def test_single_sequence_default_segments(length):
-    """One bfloat16 sequence at d = 128 under the default plan: its first
-    segment (shorter than the others) runs the output mode in the summary
-    pass from h0 and hands the scan [0 | S]; the rest must still equal the
-    oracle and the unsplit run."""
+    """One bfloat16 sequence at d = 128 under the default plan (equal
+    segments) with slow decay, so that every segment boundary goes through
+    summaries and the scan: equal to the oracle and the unsplit run."""
     y, g, beta, h0, cu = _inputs(50 + length, [length], 2, 4, 128, 128, torch.bfloat16)
     g = g * 0.05  # slow decay: the carried state matters across segments
     o1, h1 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128)
     o2, h2 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128, seg=100000)
+    assert rel_err(f64(o1), f64(o2)) <= TOL[torch.bfloat16]
+    assert rel_err(f64(h1), f64(h2)) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("variant", ["mixed_heads", "beta_above_one", "no_l2norm"])
+def test_replay_and_summaries(variant):
+    """The choice between replaying the chunks before a segment and summaries
+    + scan is made per (sequence, head) from the records' bounds.  Segments
+    of 3 chunks, so many boundaries lie within 16 chunks of their sequence's
+    start (replayed from h0) and others further in.  mixed_heads: value heads
+    0-1 decay fast (replay), 2-3 slowly (summaries) in one call;
+    beta_above_one: one head fast-decaying but with write strengths up to 1.5
+    on some tokens (no contraction bound there: summaries); no_l2norm: no
+    bound at all.  Every case equals the oracle and the unsplit run."""
+    lengths = [1, 700, 129, 0, 2600]
+    y, g, beta, h0, cu = _inputs(300 + len(variant), lengths, 2, 4, 128, 128, torch.bfloat16)
+    l2 = True
+    if variant == "mixed_heads":
+        g[:, 2:] *= 0.02
+    elif variant == "beta_above_one":
+        beta[1000:1100, 1] = 1.5
+    else:
+        l2 = False
+        y = (y.float() * 0.08).to(torch.bfloat16)  # |k| small: the recurrence stays contractive
+    o1, h1 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128, use_l2norm=l2, seg=3)
+    o2, h2 = _run_and_check(y, g, beta, h0, cu, 2, 4, 128, 128, use_l2norm=l2, seg=100000)
     assert rel_err(f64(o1), f64(o2)) <= TOL[torch.bfloat16]
     assert rel_err(f64(h1), f64(h2)) <= TOL[torch.bfloat16]
 
