@@ -79,7 +79,63 @@ struct BwdArgs {
   // the forward prep's records [chunk_cap][Hv] (bfloat16 only, else null):
   // T = (I + diag(beta) L)^-1 diag(beta) as MFMA A fragments
   const char* rec;
+  // replay of the dS recurrence (warm_rev_kernel): per (segment, head) the
+  // chunks after the segment its final pass runs first, from zero (|
+  // kWarmFromStart: from the sequence end, with dht); per (sequence, head) 1
+  // when every segment but the last replays (then no dS summaries or scan).
+  // Null: summaries and scan as usual.
+  const int32_t* rev_warm;
+  const int32_t* seq_rev_warm;
 };
+
+// The replay table of the dS recurrence: the mirror of warm_kernel.  The
+// chunk's adjoint map dS' -> dS is the transpose of its forward transition,
+// with the same norm, so the records' bounds lb serve here too, summed
+// forwards from the end of every segment but a sequence's last.
+__global__ __launch_bounds__(256) void warm_rev_kernel(const char* __restrict__ rec, int Hv,
+                                                       const int32_t* __restrict__ counts,
+                                                       const int4* __restrict__ seg_table,
+                                                       const int32_t* __restrict__ seg_chunk0,
+                                                       const int32_t* __restrict__ seq_off,
+                                                       const int32_t* __restrict__ seq_nseg,
+                                                       int seg_cap, int32_t* __restrict__ warm,
+                                                       int32_t* __restrict__ seq_warm) {
+  const int n = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int off = seq_off[n], nseg = seq_nseg[n];
+  const int nchunks = counts[1];
+  int cold = 0;
+  if (nseg > 1 && off + nseg - 1 < seg_cap) {
+    const int4 last = seg_table[off + nseg - 1];
+    const int clast = seg_chunk0[off + nseg - 1] + (last.z - last.y + BT - 1) / BT - 1;
+    for (int p = t; p + 1 < nseg; p += 256) {
+      const int s = off + p;
+      const int4 e = seg_table[s];
+      const int ce = seg_chunk0[s] + (e.z - e.y + BT - 1) / BT;  // first chunk after it
+      int val = -1;
+      float sum = 0.f;
+      for (int w = 0; w < kWarmMax; w++) {
+        const int c = ce + w;
+        if (c > clast) {  // the sequence end: replay all of it, from dht
+          val = w | kWarmFromStart;
+          break;
+        }
+        if (c >= nchunks) break;
+        sum += *reinterpret_cast<const float*>(rec + ((int64_t)c * Hv + h) * kRecBytes + kRecF +
+                                               129 * sizeof(float));
+        if (sum < kNegligibleLog) {
+          val = w + 1;
+          break;
+        }
+      }
+      warm[(int64_t)s * Hv + h] = val;
+      cold |= val < 0;
+    }
+  } else if (nseg > 1) {
+    cold = 1;
+  }
+  cold = __syncthreads_or(cold);
+  if (t == 0) seq_warm[(int64_t)n * Hv + h] = cold ? 0 : 1;
+}
 
 // w = T diag(beta e^G) kh of one chunk from the prep's record: with the
 // record's T_r = (I + diag(beta) L)^-1 diag(beta) that is T_r diag(e^G) kh, a
@@ -168,6 +224,8 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   const int4 ent = a.seg_table[seg];
   if (SUM && (ent.w & kFirst)) return;
   const int n = ent.x;
+  const bool replay = a.seq_rev_warm && a.seq_rev_warm[(int64_t)n * a.Hv + blockIdx.y];
+  if (SUM && replay) return;  // no summaries needed
   const int Hv = a.Hv, qa = h / (Hv / a.Hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = wave * CW;                 // first (extended) state column
@@ -176,14 +234,27 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   const int64_t s0 = ent.y, e0 = ent.z;
   const int nch = (int)((e0 - s0 + BT - 1) / BT);
   const int chunk0 = a.seg_chunk0[seg];
+  // final pass of a replaying sequence: the chunks after the segment run
+  // first (no dS' stores), from zero or, reaching the sequence end, from dht
+  int nwarm = 0;
+  bool warm_dht = false;
+  if (!SUM && replay && !(ent.w & kLast)) {
+    const int v = a.rev_warm[(int64_t)seg * Hv + h];
+    nwarm = v & ~kWarmFromStart;
+    warm_dht = (v & kWarmFromStart) != 0;
+  }
+  // rows past the sequence end are zero (replayed chunks lie beyond e0)
+  const int64_t te = nwarm > 0 ? (a.cu[n + 1] < a.T ? (int64_t)a.cu[n + 1] : a.T) : e0;
 
   zero_upper<O, true, NT>(sm, tid);
   floatx4 dS[DKT][NN];
   {
     const float* src = nullptr;
     if (!SUM) {
-      if (!(ent.w & kLast)) src = a.seg_in + ((int64_t)seg * Hv + h) * DK * DV;
-      else if (a.dht) src = a.dht + ((int64_t)n * Hv + h) * DK * DV;
+      const float* dhtn = a.dht ? a.dht + ((int64_t)n * Hv + h) * DK * DV : nullptr;
+      if (nwarm > 0) src = warm_dht ? dhtn : nullptr;
+      else if (!(ent.w & kLast)) src = a.seg_in + ((int64_t)seg * Hv + h) * DK * DV;
+      else src = dhtn;
     }
 #pragma unroll
     for (int mt = 0; mt < DKT; mt++)
@@ -204,14 +275,15 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
   const float* gp = a.g + h;
   const float* bp = a.beta + h;
   typename CF::PF pf;
-  if (nch > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, s0 + (int64_t)(nch - 1) * BT, e0, tid);
+  const int ctop = nch - 1 + nwarm;  // chunks ctop .. nch are replayed
+  if (nch > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, s0 + (int64_t)ctop * BT, te, tid);
 
-  for (int c = nch - 1; c >= 0; c--) {
+  for (int c = ctop; c >= 0; c--) {
     const int64_t tc = s0 + (int64_t)c * BT;
     __syncthreads();
     stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
-    if (c > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, tc - BT, e0, tid);
-    if (!SUM) {  // dS' of this chunk for the gradient kernel
+    if (c > 0) pf.load(qp, kp, a.ld_qk, dop, (int64_t)Hv * DV, gp, bp, Hv, tc - BT, te, tid);
+    if (!SUM && c < nch) {  // dS' of this chunk for the gradient kernel
       E* dst = (E*)a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV;
 #pragma unroll
       for (int mt = 0; mt < DKT; mt++)
@@ -907,7 +979,7 @@ __global__ __launch_bounds__(256) void finalize_qk_kernel(BwdArgs a, int64_t uni
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   Plan plan;
-  size_t off_states, off_dstates, off_dqk, end;
+  size_t off_states, off_dstates, off_dqk, off_rev_warm, off_seq_rev_warm, end;
 };
 
 BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, gdn_dtype dt) {
@@ -922,6 +994,10 @@ BwdLayout bwd_layout(int64_t T, int32_t N, int32_t Hv, int32_t dk, int32_t dv, g
   o = gdn::round_up(o + st, 256);
   L.off_dqk = o;
   o = gdn::round_up(o + sizeof(float) * (size_t)T * Hv * 2 * dk, 256);
+  L.off_rev_warm = o;
+  o = gdn::round_up(o + 4 * (size_t)L.plan.seg_cap * Hv, 256);
+  L.off_seq_rev_warm = o;
+  o = gdn::round_up(o + 4 * (size_t)N * Hv, 256);
   L.end = o;
   return L;
 }
@@ -961,6 +1037,17 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
   // are free again): reverse summaries, reverse scan from dht, final pass
   b.seg_table = pp.table;
   b.seg_chunk0 = pp.seg_chunk0;
+  if (L.plan.split && b.rec) {
+    // per (sequence, head): replay the dS recurrence instead of summaries
+    // where the records' bounds allow it
+    int32_t* rw = reinterpret_cast<int32_t*>(ws + L.off_rev_warm);
+    int32_t* srw = reinterpret_cast<int32_t*>(ws + L.off_seq_rev_warm);
+    hipLaunchKernelGGL(warm_rev_kernel, dim3(N, b.Hv), dim3(256), 0, stream, b.rec, b.Hv, pp.counts,
+                       pp.table, pp.seg_chunk0, pp.seq_off, pp.seq_nseg, (int)L.plan.seg_cap, rw, srw);
+    if (int rc = gdn::check_launch("gdn_chunk_bwd(replay table)")) return rc;
+    b.rev_warm = rw;
+    b.seq_rev_warm = srw;
+  }
   b.seg_sum = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_state) : nullptr;
   b.seg_in = L.plan.split ? reinterpret_cast<float*>(ws + L.plan.off_init) : nullptr;
   const dim3 sgrid((unsigned)L.plan.seg_cap, b.Hv);
@@ -969,7 +1056,8 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
                        stream, b);
     if (int rc = gdn::check_launch("gdn_chunk_bwd(dS summaries)")) return rc;
     hipLaunchKernelGGL((seg_scan_kernel<DK, DV, true>), dim3(N, b.Hv, DV / 16), dim3(DK * 2), 0,
-                       stream, b.seg_sum, b.seg_in, b.dht, pp.seq_off, pp.seq_nseg, b.Hv);
+                       stream, b.seg_sum, b.seg_in, b.dht, pp.seq_off, pp.seq_nseg, b.Hv,
+                       b.seq_rev_warm);
     if (int rc = gdn::check_launch("gdn_chunk_bwd(dS scan)")) return rc;
   }
   hipLaunchKernelGGL((dstate_kernel<E, DK, DV, false>), sgrid, dim3(DsCfg<E, DK, DV, false>::NT), 0,

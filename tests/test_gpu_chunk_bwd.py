@@ -81,6 +81,31 @@ def test_segmented_state_pass(seg):
     _check_bwd(y, g * 0.05, beta, h0, do, dht, cu, 2, 4, 128, seg=seg)
 
 
+@pytest.mark.parametrize("variant", ["mixed_heads", "beta_above_one"])
+def test_replay_and_summaries(variant):
+    """Both recurrences (the forward's states and the backward's dS) choose
+    per (sequence, head) between replaying the chunks next to a segment and
+    summaries + scan.  Segments of 3 chunks; mixed_heads: value heads 0-1
+    decay fast (replay), 2-3 slowly (summaries); beta_above_one: one head's
+    write strengths reach 1.5 on some tokens (no bound there).  Against the
+    oracle, saved pair included."""
+    y, g, beta, h0, do, dht, cu = _inputs(400 + len(variant), [1, 700, 129, 0, 1300], 2, 4, 128,
+                                          torch.bfloat16)
+    if variant == "mixed_heads":
+        g[:, 2:] *= 0.02
+    else:
+        beta[900:1000, 1] = 1.5
+    r = _check_bwd(y, g, beta, h0, do, dht, cu, 2, 4, 128, seg=3)
+    yc, gc, bc, h0c = y.cuda(), g.cuda(), beta.cuda(), h0.cuda()
+    with forced_segments(3):
+        _, _, saved = gdn.gdn_chunk_fwd_save(yc, gc, bc, cu_tensor(cu), 2, 4, 128, 128, h0=h0c)
+        r2 = gdn.gdn_chunk_bwd_saved(yc, gc, bc, cu_tensor(cu), 2, 4, 128, 128, do.cuda(), saved,
+                                     h0=h0c, dht=dht.cuda())
+        torch.cuda.synchronize()
+    for key in r:
+        assert_close(key + "(saved vs recomputed)", f64(r2[key]), f64(r[key]), torch.bfloat16)
+
+
 def test_no_l2norm_no_state():
     y, g, beta, _, do, _, cu = _inputs(9, [150, 40], 2, 2, 32, torch.float32, h0=False)
     _check_bwd(y * 0.1, g, beta, None, do, None, cu, 2, 2, 32, use_l2norm=False)
