@@ -207,7 +207,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic("chunk_fwd", spec.name),
-                "kernel": "gdn_chunk_fwd call: plan, prep, segment summaries, scan, output pass"}
+                "kernel": "gdn_chunk_fwd call: plan, prep, replay table, summaries + scan for "
+                          "the (sequence, head) pairs that cannot replay, output pass"}
     chunk_hbm = chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
     extra = {
         "chunk_fwd_hbm": {"achieved": chunk_hbm / t_chunk / 1e9, "peak": HBM_PEAK / 1e9,
@@ -225,8 +226,9 @@ def main():
         roofline = {"bound": "mfma", "achieved": bwd_flops / t_bwd / 1e12, "peak": peak / 1e12,
                     "unit": "TFLOP/s", "frac": bwd_flops / t_bwd / peak,
                     "traffic": measured_traffic("chunk_bwd", spec.name),
-                    "kernel": "gdn_chunk_bwd_saved call: plan, dS summaries, scan, dS "
-                              "final pass, gradients (per-chunk states saved by the forward)"}
+                    "kernel": "gdn_chunk_bwd_saved call: plan, replay table, dS summaries + "
+                              "scan where needed, dS final pass, gradients (per-chunk states "
+                              "saved by the forward)"}
         bwd_hbm = chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
         extra["chunk_bwd_hbm"] = {"achieved": bwd_hbm / t_bwd / 1e9, "peak": HBM_PEAK / 1e9,
                                   "unit": "GB/s", "frac": bwd_hbm / t_bwd / HBM_PEAK}
