@@ -67,6 +67,22 @@ def chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s):
     return T * per_tok + 3 * N * Hv * dk * dv * 4
 
 
+def roof(flops, nbytes, t, act):
+    """The call's position under both roofs, and the binding one: at the
+    call's algorithmic intensity (FLOP per algorithmic HBM byte) the bound
+    is HBM below the ridge (MFMA peak / HBM peak) and MFMA above it; frac is
+    the binding roof's time over the measured time."""
+    mfma = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": MFMA_PEAK[act] / 1e12,
+            "unit": "TFLOP/s", "frac": flops / t / MFMA_PEAK[act]}
+    hbm = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+           "frac": nbytes / t / HBM_PEAK}
+    ridge = MFMA_PEAK[act] / HBM_PEAK
+    intensity = flops / nbytes
+    binding = dict(hbm if intensity < ridge else mfma)
+    binding.update({"intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge})
+    return binding, mfma, hbm
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,19 +216,16 @@ def main():
     s_bytes = 2 if dtype == torch.bfloat16 else 4
     flops = chunk_fwd_flops_per_token_head(dk, dv) * T * Hv
     t_chunk = per_call["chunk_fwd"] * 1e-3
-    achieved = flops / t_chunk
-    peak = MFMA_PEAK[spec.act]
     conv_b = conv_bytes_per_token(C, s_bytes) * T + C * K * s_bytes
     t_conv = per_call["conv_fwd"] * 1e-3
-    roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": measured_traffic("chunk_fwd", spec.name),
-                "kernel": "gdn_chunk_fwd call: plan, prep, replay table, summaries + scan for "
-                          "the (sequence, head) pairs that cannot replay, output pass"}
     chunk_hbm = chunk_fwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
+    roofline, fwd_mfma, fwd_hbm = roof(flops, chunk_hbm, t_chunk, spec.act)
+    roofline.update({"traffic": measured_traffic("chunk_fwd", spec.name),
+                     "kernel": "gdn_chunk_fwd call: plan, prep, replay table, summaries + scan "
+                               "for the (sequence, head) pairs that cannot replay, output pass"})
     extra = {
-        "chunk_fwd_hbm": {"achieved": chunk_hbm / t_chunk / 1e9, "peak": HBM_PEAK / 1e9,
-                          "unit": "GB/s", "frac": chunk_hbm / t_chunk / HBM_PEAK},
+        "chunk_fwd_mfma": fwd_mfma,
+        "chunk_fwd_hbm": fwd_hbm,
         "conv_fwd": {"bound": "hbm", "achieved": conv_b / t_conv / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": conv_b / t_conv / HBM_PEAK},
     }
@@ -223,15 +236,14 @@ def main():
         bwd_flops = 2 * flops  # reverse mode of the chunk algorithm: twice the forward's products
         extra["chunk_fwd"] = dict(roofline, kernel="gdn_chunk_fwd_save call (keeps the "
                                   "per-chunk states for the backward)")
-        roofline = {"bound": "mfma", "achieved": bwd_flops / t_bwd / 1e12, "peak": peak / 1e12,
-                    "unit": "TFLOP/s", "frac": bwd_flops / t_bwd / peak,
-                    "traffic": measured_traffic("chunk_bwd", spec.name),
-                    "kernel": "gdn_chunk_bwd_saved call: plan, replay table, dS summaries + "
-                              "scan where needed, dS final pass, gradients (per-chunk states "
-                              "saved by the forward)"}
         bwd_hbm = chunk_bwd_bytes(T, N, Hk, Hv, dk, dv, s_bytes)
-        extra["chunk_bwd_hbm"] = {"achieved": bwd_hbm / t_bwd / 1e9, "peak": HBM_PEAK / 1e9,
-                                  "unit": "GB/s", "frac": bwd_hbm / t_bwd / HBM_PEAK}
+        roofline, bwd_mfma, bwd_hbm_roof = roof(bwd_flops, bwd_hbm, t_bwd, spec.act)
+        roofline.update({"traffic": measured_traffic("chunk_bwd", spec.name),
+                         "kernel": "gdn_chunk_bwd_saved call: plan, replay table, dS summaries + "
+                                   "scan where needed, dS final pass, gradients (per-chunk states "
+                                   "saved by the forward)"})
+        extra["chunk_bwd_mfma"] = bwd_mfma
+        extra["chunk_bwd_hbm"] = bwd_hbm_roof
         t_cbwd = per_call["conv_bwd"] * 1e-3
         cbwd_b = conv_bwd_bytes_per_token(C, s_bytes) * T + C * K * (s_bytes + 4)
         extra["conv_bwd"] = {"bound": "hbm", "achieved": cbwd_b / t_cbwd / 1e9, "peak": HBM_PEAK / 1e9,
