@@ -582,6 +582,14 @@ GDN_DEV void buffer_store8(const V& v, __amdgpu_buffer_rsrc_t r, uint32_t voff, 
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
 }
+// one element (2 or 4 bytes)
+template <typename E>
+GDN_DEV void buffer_store_elem(E v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(E) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff, 0);
+}
 
 // Loader registers: one chunk's rows and the first RECB bytes of its record,
 // 16-byte vectors.  The loads go through buffer resources
@@ -914,15 +922,22 @@ GDN_DEV void ws_body(const LoopArgs& a, typename WsCfg<E, DK, DV, MODE>::SM* buf
     constexpr bool EMIT = decltype(emit)::value;
       const char* R = C.rec;
       if constexpr (stores_states(MODE) && EMIT) {
-        // the state entering this chunk, for the backward
-        E* dst = (E*)a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV;
+        // the state entering this chunk, for the backward: element stores
+        // through a buffer resource over it, the lane's part of the offset
+        // (row 8 g4 of dk_of_row, its column) fixed and the rest constant,
+        // so the addresses take no registers
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc((E*)a.states + ((int64_t)(chunk0 + it) * Hv + h) * DK * DV,
+                        (uint32_t)(DK * DV * sizeof(E)));
+        const uint32_t soff = (uint32_t)((8 * g4 * DV + c0 + ln) * sizeof(E));
 #pragma unroll
         for (int mt = 0; mt < DKT; mt++)
 #pragma unroll
           for (int nt = 0; nt < NN; nt++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dst[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] = from_f<E>(S[mt][nt][j]);
+              buffer_store_elem<E>(from_f<E>(S[mt][nt][j]), rs, soff,
+                                   (uint32_t)(((32 * (mt >> 1) + 4 * (mt & 1) + j) * DV + 16 * nt) * sizeof(E)));
       }
       // k S (into x) and q S (into o), one contraction step of S at a time
 #pragma unroll

@@ -274,3 +274,45 @@ def test_closed_form_total_decay(dtype):
             a = h // (Hv // Hk)
             want_ht[n, h] = bb[t, h] * np.outer(kh[t, a], v[t, h])
     assert_close("ht", f64(ht), want_ht, dtype)
+
+
+SAVE_SHAPES = [(128, 128), (128, 64), (64, 128), (128, 32), (32, 128), (64, 64), (32, 32),
+               (64, 32), (32, 64)]
+
+
+@pytest.mark.parametrize("dk,dv", SAVE_SHAPES)
+def test_saved_states_every_shape(dk, dv):
+    """gdn_chunk_fwd_save at every bfloat16 shape: o and ht equal
+    gdn_chunk_fwd's bit for bit, and the state entering every chunk (the
+    buffer's second part, [chunk_cap][Hv][dk][dv] in the activation type,
+    chunks numbered sequence by sequence from each start; the first part
+    holds 7424-byte records per (chunk, value head)) equals the oracle's
+    final state of the sequence cut at that chunk's start."""
+    from oracle import capi
+    lengths, Hk, Hv = [1, 63, 64, 65, 0, 200], 2, 4
+    y, g, beta, h0, cu = _inputs(300 + dk + dv, lengths, Hk, Hv, dk, dv, torch.bfloat16)
+    yc, gc, bc, h0c, cut = y.cuda(), g.cuda(), beta.cuda(), h0.cuda(), cu_tensor(cu)
+    T, N = sum(lengths), len(lengths)
+    o1, ht1 = gdn.gdn_chunk_fwd(yc, gc, bc, cut, Hk, Hv, dk, dv, h0=h0c)
+    o2, ht2, saved = gdn.gdn_chunk_fwd_save(yc, gc, bc, cut, Hk, Hv, dk, dv, h0=h0c)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    cap = (T + 63) // 64 + N + 1
+    off = (7424 * cap * Hv + 255) // 256 * 256
+    nbytes = 2 * cap * Hv * dk * dv
+    assert gdn.chunk_saved_size(T, N, Hk, Hv, dk, dv, torch.bfloat16) == off + (nbytes + 255) // 256 * 256
+    states = saved[off:off + nbytes].view(torch.bfloat16).view(cap, Hv, dk, dv).cpu()
+    q, k, v = split_qkv(f64(y), Hk, Hv, dk, dv)
+    c = 0
+    for n in range(N):
+        s, e = cu[n], cu[n + 1]
+        for i in range((e - s + 63) // 64):
+            t = s + 64 * i
+            if i == 0:
+                want = f64(h0[n])
+            else:
+                _, ht = capi.gdn_fwd(q[s:t], k[s:t], v[s:t], f64(g[s:t]), f64(beta[s:t]),
+                                     f64(h0[n:n + 1]), [0, t - s], dk ** -0.5)
+                want = ht[0]
+            assert_close("state(seq %d, chunk %d)" % (n, i), f64(states[c]), want, torch.bfloat16)
+            c += 1
