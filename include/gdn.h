@@ -240,7 +240,10 @@ int gdn_chunk_fwd(const void* q, const void* k, int64_t ld_qk, const void* v, in
  * Forward arguments as in gdn_chunk_fwd.  ws: gdn_chunk_workspace_size(...,1).
  * Errors: the argument checks of gdn_chunk_fwd (GDN_EINVAL, GDN_EWORKSPACE);
  * GDN_EINVAL also for null gradient pointers (d_o, dq, dk_, dv_, dg, dbeta
- * when T > 0) and for ld_dqk < Hk*dk or ld_dv < Hv*dv.  The backward has
+ * when T > 0), for ld_dqk < Hk*dk or ld_dv < Hv*dv, and when 64 rows of dq,
+ * dk or dv (or of the float32 [token, Hv, 2, dk] partial rows kept in the
+ * workspace) span 4 GiB or more (a chunk's rows are addressed with 32-bit
+ * byte offsets).  The backward has
  * kernels for fewer shapes than the forward: GDN_EUNSUPPORTED unless
  * dk == dv and d is 64 or 128 (bfloat16) or 32 or 64 (float32).
  */

@@ -501,29 +501,50 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   // S and dS' as B fragments (K = dk, N = this wave's value columns) and <dS', S>
   typename M::frag sb[NSK][NN], dsb[NSK][NN];
   float dot = 0.f;
+  if constexpr (sizeof(E) == 2) {
+    // 16-bit element loads through buffer resources over the two tiles: the
+    // lane's part of the offset (row 4 g4, its column) is fixed and the rest
+    // constant, so there is no address arithmetic and the halves go straight
+    // into the fragment registers.  <dS', S> over this wave's columns is the
+    // trace of S^T dS' (four products; the diagonal entry of a lane is its
+    // element j = ln % 4 when g4 = ln / 4).
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(Sg, (uint32_t)(DK * DV * sizeof(E)));
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dSg, (uint32_t)(DK * DV * sizeof(E)));
+    const uint32_t voff = (uint32_t)((4 * g4 * DV + c0 + ln) * sizeof(E));
+    floatx4 tr = zero4();
 #pragma unroll
-  for (int s = 0; s < NSK; s++)
+    for (int s = 0; s < NSK; s++)
 #pragma unroll
-    for (int nt = 0; nt < NN; nt++) {
-      constexpr int TPS = KS / 16;  // C-tiles per contraction step
-      floatx4 st[TPS], dt[TPS];
+      for (int nt = 0; nt < NN; nt++) {
 #pragma unroll
-      for (int q = 0; q < TPS; q++)
+        for (int e = 0; e < 8; e++) {
+          const uint32_t soff = (uint32_t)(((32 * s + 16 * (e >> 2) + (e & 3)) * DV + 16 * nt) * sizeof(E));
+          sb[s][nt][e] = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+          dsb[s][nt][e] = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rd, voff, soff, 0));
+        }
+        M::mma(tr, sb[s][nt], dsb[s][nt]);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; j++) dot += (4 * g4 + j == ln) ? tr[j] : 0.f;
+  } else {
+    // fp32 states: one C tile a contraction step, element loads
+    static_assert(KS == 16, "fp32 contraction step");
+#pragma unroll
+    for (int s = 0; s < NSK; s++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) {
+        floatx4 st, dt;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int idx = (16 * (TPS * s + q) + 4 * g4 + j) * DV + c0 + 16 * nt + ln;
-          st[q][j] = to_f(Sg[idx]);
-          dt[q][j] = to_f(dSg[idx]);
-          dot += st[q][j] * dt[q][j];
+          const int idx = (16 * s + 4 * g4 + j) * DV + c0 + 16 * nt + ln;
+          st[j] = to_f(Sg[idx]);
+          dt[j] = to_f(dSg[idx]);
+          dot += st[j] * dt[j];
         }
-      if constexpr (TPS == 2) {
-        sb[s][nt] = M::from_acc(st[0], st[1]);
-        dsb[s][nt] = M::from_acc(dt[0], dt[1]);
-      } else {
-        sb[s][nt] = M::from_acc(st[0]);
-        dsb[s][nt] = M::from_acc(dt[0]);
+        sb[s][nt] = M::from_acc(st);
+        dsb[s][nt] = M::from_acc(dt);
       }
-    }
+  }
 
   // Vn = u - W S; QS; KS; K dS'
   floatx4 ks[4][NN], kds[4][NN];
@@ -594,7 +615,14 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   // Y = T^T dVn; dv = beta o Y
   floatx4 y[4][NN];
   float r_b[4][4], r_yks[4][4];
-  E* dvp = (E*)a.dv + (int64_t)h * DV + c0 + ln;
+  // dv, dq and dk rows of this chunk through buffer resources (rows past the
+  // sequence end fall outside the range and their stores are dropped); the
+  // lane's part of the offset (row 4 g4, its column) is fixed
+  const int64_t nrows = te - tc;
+  const __amdgpu_buffer_rsrc_t rdv =
+      buffer_rsrc((E*)a.dv + tc * a.ld_dv + (int64_t)h * DV,
+                  (uint32_t)(((nrows - 1) * a.ld_dv + DV) * (int64_t)sizeof(E)));
+  const uint32_t dvoff = (uint32_t)((4 * g4 * a.ld_dv + c0 + ln) * (int64_t)sizeof(E));
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
     floatx4 yy[NN];
@@ -617,8 +645,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
         const int row = 16 * mt + 4 * g4 + j;
         r_b[mt][j] += yy[nt][j] * vv[j];
         r_yks[mt][j] += yy[nt][j] * ks[mt][nt][j];
-        const int64_t t = tc + row;
-        if (t < te) dvp[t * a.ld_dv + 16 * nt] = from_f<E>(sm.beta[row] * yy[nt][j]);
+        buffer_store_elem<E>(from_f<E>(sm.beta[row] * yy[nt][j]), rdv, dvoff,
+                             (uint32_t)(((16 * mt + j) * a.ld_dv + 16 * nt) * (int64_t)sizeof(E)));
       }
     }
   }
@@ -755,7 +783,12 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   // here (fused) and dq, dk are written directly; otherwise dq-hat, dk-hat go
   // to the fp32 partials for finalize_qk_kernel.
   const bool fused = a.Hv == a.Hk;
-  float* dqk = a.dqk + (int64_t)h * 2 * DK;
+  // fp32 partial rows [token][Hv][2][dk] of this chunk and head (a buffer
+  // resource: rows past the sequence end are dropped)
+  const __amdgpu_buffer_rsrc_t rqk =
+      buffer_rsrc(a.dqk + (tc * Hv + h) * 2 * DK,
+                  (uint32_t)(((nrows - 1) * Hv * 2 * DK + 2 * DK) * (int64_t)sizeof(float)));
+  const uint32_t qkoff = (uint32_t)((4 * g4 * Hv * 2 * DK + ln) * (int64_t)sizeof(float));
   float fq[NN][4][4], fk[NN][4][4];
 #pragma unroll
   for (int nt = 0; nt < NN; nt++) {
@@ -789,16 +822,16 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int row = 16 * mt + 4 * g4 + j;
-        const int64_t t = tc + row;
         const float gm = sm.eg[row];
         const float d = __expf(GC - sm.G[row]);
         const float dqv = gm * a1[j] + a2[j];
         const float dkv = b3[j] + d * b4[j] - sm.beta[row] * gm * b5[j] + b6[j];
         fq[nt][mt][j] = dqv;
         fk[nt][mt][j] = dkv;
-        if (!fused && t < te) {
-          dqk[t * Hv * 2 * DK + dc + ln] = dqv;
-          dqk[t * Hv * 2 * DK + DK + dc + ln] = dkv;
+        if (!fused) {
+          const uint32_t so = (uint32_t)(((16 * mt + j) * Hv * 2 * DK + dc) * sizeof(float));
+          buffer_store_elem<float>(dqv, rqk, qkoff, so);
+          buffer_store_elem<float>(dkv, rqk, qkoff, so + (uint32_t)(DK * sizeof(float)));
         }
       }
     }
@@ -836,15 +869,15 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
       gs.etot[kind][row] = acc;
     }
     __syncthreads();
-    E* dqo = (E*)a.dq + (int64_t)qa * DK + c0 + ln;
-    E* dko = (E*)a.dk + (int64_t)qa * DK + c0 + ln;
+    const uint32_t span = (uint32_t)(((nrows - 1) * a.ld_dqk + DK) * (int64_t)sizeof(E));
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc((E*)a.dq + tc * a.ld_dqk + (int64_t)qa * DK, span);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((E*)a.dk + tc * a.ld_dqk + (int64_t)qa * DK, span);
+    const uint32_t qoff = (uint32_t)((4 * g4 * a.ld_dqk + c0 + ln) * (int64_t)sizeof(E));
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int row = 16 * mt + 4 * g4 + j;
-        const int64_t t = tc + row;
-        if (t >= te) continue;
         const float nq = sm.rnq[row], nk = sm.rnk[row];
         const float qd = gs.etot[0][row], kd = gs.etot[1][row];
 #pragma unroll
@@ -855,8 +888,9 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
             gq = a.scale * nq * (fq[nt][mt][j] - to_f(sm.q[row * SM::LDK + col]) * inv_scale * qd);
             gk = nk * (fk[nt][mt][j] - to_f(sm.k[row * SM::LDK + col]) * kd);
           }
-          dqo[t * a.ld_dqk + 16 * nt] = from_f<E>(gq);
-          dko[t * a.ld_dqk + 16 * nt] = from_f<E>(gk);
+          const uint32_t so = (uint32_t)(((16 * mt + j) * a.ld_dqk + 16 * nt) * (int64_t)sizeof(E));
+          buffer_store_elem<E>(from_f<E>(gq), rq, qoff, so);
+          buffer_store_elem<E>(from_f<E>(gk), rk, qoff, so);
         }
       }
   }
@@ -1118,6 +1152,13 @@ int chunk_bwd(const char* fn, const void* q, const void* k, int64_t ld_qk, const
     return gdn::fail(GDN_EINVAL, "%s: null gradient pointer", fn);
   if (ld_dqk < (int64_t)Hk * dk || ld_dv < (int64_t)Hv * dv)
     return gdn::fail(GDN_EINVAL, "%s: gradient row strides smaller than the head blocks", fn);
+  {
+    // a chunk's 64 rows of dq, dk, dv and of the fp32 partial rows are
+    // addressed with 32-bit byte offsets
+    const int64_t lim = (int64_t)1 << 32, es = dt == GDN_BF16 ? 2 : 4;
+    if (64 * ld_dqk * es >= lim || 64 * ld_dv * es >= lim || 64 * (int64_t)Hv * 2 * dk * 4 >= lim)
+      return gdn::fail(GDN_EINVAL, "%s: 64 rows of dq, dk or dv must span less than 4 GiB", fn);
+  }
   const BwdLayout L = bwd_layout(T, N, Hv, dk, dv, dt);
   if (!ws || ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return gdn::fail(GDN_EWORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned", fn, L.end);

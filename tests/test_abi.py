@@ -189,6 +189,9 @@ def test_chunk_bwd_rejects_shapes_it_has_no_kernel_for(lib):
     assert _chunk_bwd(lib, dq=None) == gdn.GDN_EINVAL
     assert _chunk_bwd(lib, dg=None) == gdn.GDN_EINVAL
     assert _chunk_bwd(lib, ld_dqk=100) == gdn.GDN_EINVAL
+    assert _chunk_bwd(lib, ld_dqk=1 << 25) == gdn.GDN_EINVAL   # 64 rows past 32-bit offsets
+    assert b"4 GiB" in lib.gdn_last_error()
+    assert _chunk_bwd(lib, ld_dv=1 << 25) == gdn.GDN_EINVAL
     assert _chunk_bwd(lib, ws_bytes=16) == gdn.GDN_EWORKSPACE
 
 
