@@ -294,9 +294,12 @@ template <int WIDTH> GDN_DEV float group_sum(float v) {
 }
 
 // Sum over aligned groups of W <= 16 consecutive lanes with DPP lane moves
-// (quad swaps, then the half-row and row mirrors), no LDS round trip.
+// (quad swaps, then the half-row and row mirrors), no LDS round trip.  Every
+// lane has a source under these patterns, so bound_ctrl and the zero "old"
+// value never take effect; with them the compiler folds each move into its
+// add (one v_add_f32_dpp a step instead of a move and an add).
 template <int CTRL> GDN_DEV float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int W> GDN_DEV float row_group_sum(float v) {
   static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16, "group of 1..16 lanes");
