@@ -416,6 +416,323 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dS final pass with the forward state pass's loader / consumer split
+// ---------------------------------------------------------------------------
+// Per chunk, with dS' the state gradient leaving it (carried back from the
+// chunk after), the adjoint of the state pass's three steps
+//   x = T (v - fk o (k S)),  o = fo o (q S) + P x,  S' = eC S + k^T (fd o x)
+// is
+//   dx = P^T dO + fd o (k dS'),   dy = T^T dx,
+//   dS = eC dS' + q^T (fo o dO) - k^T (fk o dy).
+// Four loader waves stage q, k, dO and the record of the chunk before (the
+// chunks run in reverse) and make P^T and T^T as A fragments; eight consumer
+// waves carry 16 columns of dS each in MFMA accumulators (dk rows permuted as
+// in the forward), store dS' of every chunk for the gradient kernel and write
+// dh0 at a sequence's first segment.  Replay and the initial dS as in
+// dstate_kernel's final mode.
+
+// Halves of P^T being made by the loaders: (row block mt of P^T = token block
+// of k, token block jq of q), the two that lie below the diagonal (all zero)
+// last.
+constexpr int kPtHalves = 12;
+__host__ __device__ constexpr int pt_half_mt(int u) {
+  return u < 4 ? 0 : u < 7 ? 1 : u < 9 ? 2 : u == 9 ? 3 : u == 10 ? 1 : 3;
+}
+__host__ __device__ constexpr int pt_half_jq(int u) {
+  return u < 4 ? u : u < 7 ? u - 3 : u < 9 ? u - 5 : u == 9 ? 3 : u == 10 ? 0 : 2;
+}
+
+// Half (mt, jq): the tile q_jq k_mt^T (rows = tokens tok of q, columns =
+// tokens tok' of k) holds in lane l the elements P[tok = 16 jq + 4(l/16) + e]
+// [tok' = 16 mt + l%16], exactly half jq % 2 of the A fragment (mt, jq / 2) of
+// P^T.  P[tok][tok'] = rq_tok rk_tok' e^{G_tok - G_tok'} q_tok . k_tok' for
+// tok' <= tok, else 0, as in the output pass.
+template <int DK>
+struct PtHalf {
+  int mt, jq;
+  floatx4 acc;
+  template <class SM>
+  GDN_DEV void begin(const SM& C, int u, int lane) {
+    mt = pt_half_mt(u);
+    jq = pt_half_jq(u);
+    acc = zero4();
+    if (u < 10) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ks++)
+        Mfma<bf16>::mma(acc, Mfma<bf16>::load_k8(C.q, SM::LDK, 16 * jq, 32 * ks, lane),
+                        Mfma<bf16>::load_k8(C.k, SM::LDK, 16 * mt, 32 * ks, lane));
+    }
+  }
+  template <class SM>
+  GDN_DEV void finish(SM& C, int lane) const {
+    const int g4 = lane >> 4, ln = lane & 15;
+    const float* Gv = reinterpret_cast<const float*>(C.rec + kRecG);
+    const int tokp = 16 * mt + ln, t0 = 16 * jq + 4 * g4;
+    const float rkp = Gv[64 + tokp], Gp = Gv[tokp];
+    const floatx4 rq4 = *reinterpret_cast<const floatx4*>(C.rq + t0);
+    const floatx4 G4 = *reinterpret_cast<const floatx4*>(Gv + t0);
+    bf16x4 f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float val = acc[e] * rq4[e] * rkp * __expf(fminf(G4[e] - Gp, 0.f));
+      f[e] = (bf16)(tokp <= t0 + e ? val : 0.f);
+    }
+    *reinterpret_cast<bf16x4*>(C.p + pt_frag(mt, jq >> 1) * 1024 + lane * 16 + (jq & 1) * 8) = f;
+  }
+};
+
+template <int DK, int DV>
+struct DsrCfg {
+  static constexpr int CW = 16;          // dS columns a consumer wave
+  static constexpr int NC = DV / CW;     // consumer waves
+  static constexpr int NL = 4;           // loader waves
+  static constexpr int NT = (NC + NL) * 64;
+  typedef WsSmem<bf16, DK, DV, true> SM;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__((DsrCfg<DK, DV>::NT)) void dsr_kernel(BwdArgs a) {
+  typedef DsrCfg<DK, DV> CF;
+  typedef typename CF::SM SM;
+  typedef Mfma<bf16> M;
+  typedef M::frag Fr;
+  constexpr int NC = CF::NC, NL = CF::NL, CW = CF::CW, NN = CW / 16;
+  constexpr int KS = M::KSTEP, NSK = DK / KS, NSB = BT / KS, DKT = DK / 16;
+  static_assert(KS == 32 && NSB == 2, "bf16 fragments of 64-token chunks");
+  __shared__ SM buf[2];
+  __shared__ unsigned p_count;  // loader waves' stored chunks (P^T hand-off)
+  if (threadIdx.x == 0) p_count = 0u;
+  __syncthreads();
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= a.counts[0]) return;
+  const int4 ent = a.seg_table[seg];
+  const int n = ent.x, Hv = a.Hv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, ln = lane & 15;
+  const int64_t s0 = ent.y, e0 = ent.z;
+  const int nch = (int)((e0 - s0 + BT - 1) / BT);
+  const int chunk0 = a.seg_chunk0[seg];
+  const bool replay = a.seq_rev_warm && a.seq_rev_warm[(int64_t)n * Hv + h];
+  // a replaying sequence: the chunks after the segment run first (no dS'
+  // stores), from zero or, reaching the sequence end, from dht
+  int nwarm = 0;
+  bool warm_dht = false;
+  if (replay && !(ent.w & kLast)) {
+    const int v = a.rev_warm[(int64_t)seg * Hv + h];
+    nwarm = v & ~kWarmFromStart;
+    warm_dht = (v & kWarmFromStart) != 0;
+  }
+  const int64_t te = nwarm > 0 ? (a.cu[n + 1] < a.T ? (int64_t)a.cu[n + 1] : a.T) : e0;
+  const int nsteps = nch + nwarm;  // step i runs chunk nsteps - 1 - i
+  const char* recs = a.rec + (int64_t)h * kRecBytes;
+  const int64_t rstride = (int64_t)Hv * kRecBytes;
+
+  if (wave >= NC) {
+    // ======================= loaders =======================
+    typedef WsLoad<bf16, DK, DV, true, SM::REC> LD;
+    const int ltid = tid - NC * 64, lw = wave - NC;
+    const int qa = h / (Hv / a.Hk);
+    const bf16* qp = (const bf16*)a.q + (int64_t)qa * DK;
+    const bf16* kp = (const bf16*)a.k + (int64_t)qa * DK;
+    const bf16* op = (const bf16*)a.d_o + (int64_t)h * DV;
+    const int64_t ld_o = (int64_t)Hv * DV;
+    const typename LD::Off off = LD::offsets(a.ld_qk, ld_o, ltid);
+    LD ld;
+    if (nsteps > 0) {
+      const int c = nsteps - 1;
+      ld.load(qp, kp, a.ld_qk, op, ld_o, recs + (int64_t)(chunk0 + c) * rstride, s0 + (int64_t)c * BT,
+              te, off, ltid);
+    }
+    for (int it = -1; it < nsteps; it++) {
+      const int pc = it + 1;
+      if (pc < nsteps) {
+        SM& B = buf[pc & 1];
+        ld.template store<true>(B, ltid, a.scale, a.use_l2norm);
+        if (pc + 1 < nsteps) {
+          const int c = nsteps - 2 - pc;
+          ld.load(qp, kp, a.ld_qk, op, ld_o, recs + (int64_t)(chunk0 + c) * rstride,
+                  s0 + (int64_t)c * BT, te, off, ltid);
+        }
+        // P^T and fo of the chunk just stored, once every loader wave's rows
+        // are in place
+        count_arrive(&p_count, lane);
+        count_wait(&p_count, (unsigned)NL * (unsigned)(pc + 1));
+        constexpr int NR = kPtHalves / NL;
+        PtHalf<DK> ph[NR];
+#pragma unroll
+        for (int r = 0; r < NR; r++) ph[r].begin(B, lw + r * NL, lane);
+#pragma unroll
+        for (int r = 0; r < NR; r++) ph[r].finish(B, lane);
+        if (lw == 0) B.fo[lane] = __expf(reinterpret_cast<const float*>(B.rec + kRecG)[lane]) * B.rq[lane];
+      }
+      lds_barrier();  // the chunk (with P^T, T^T and fo) is published
+    }
+    return;
+  }
+
+  // ======================= consumers =======================
+  const int c0 = wave * CW;  // first dS column of this wave
+  // dS tiles: rows dk_of_row(mt, 4(lane/16) + j), cols c0 + 16 nt + lane%16
+  floatx4 dS[DKT][NN];
+  {
+    const float* dhtn = a.dht ? a.dht + ((int64_t)n * Hv + h) * DK * DV : nullptr;
+    const float* src;
+    if (nwarm > 0) src = warm_dht ? dhtn : nullptr;
+    else if (!(ent.w & kLast)) src = a.seg_in + ((int64_t)seg * Hv + h) * DK * DV;
+    else src = dhtn;
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          dS[mt][nt][j] = src ? src[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] : 0.f;
+  }
+  lds_barrier();  // the first chunk is published
+  for (int i = 0; i < nsteps; i++) {
+    SM& C = buf[i & 1];
+    const int c = nsteps - 1 - i;
+    if (c < nch) {
+      // dS' of this chunk for the gradient kernel ([dk][dv], the activation
+      // type): element stores through a buffer resource over it, the lane's
+      // part of the offset (row 8 g4 of dk_of_row, its column) fixed
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc((bf16*)a.dstates + ((int64_t)(chunk0 + c) * Hv + h) * DK * DV,
+                      (uint32_t)(DK * DV * sizeof(bf16)));
+      const uint32_t soff = (uint32_t)((8 * g4 * DV + c0 + ln) * sizeof(bf16));
+#pragma unroll
+      for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            buffer_store_elem<bf16>((bf16)dS[mt][nt][j], rs, soff,
+                                    (uint32_t)(((32 * (mt >> 1) + 4 * (mt & 1) + j) * DV + 16 * nt) * sizeof(bf16)));
+    }
+    // x = k dS' (token rows), one contraction step of dS' at a time
+    floatx4 x[4][NN];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) x[mt][nt] = zero4();
+#pragma unroll
+    for (int s = 0; s < NSK; s++) {
+      Fr b[NN];
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) b[nt] = acc_as_b<bf16>(dS, s, nt);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const Fr kf = M::load_k8(C.k, SM::LDK, 16 * mt, s * KS, lane);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], kf, b[nt]);
+      }
+    }
+    const float* Fd = reinterpret_cast<const float*>(C.rec + kRecF);
+    const float* Fk = Fd + 64;
+    const float eC = Fd[128];
+    // dx = fd o x + P^T dO (dO of this wave's columns as B fragments, token
+    // rows in the convention's order)
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      const floatx4 fd = *reinterpret_cast<const floatx4*>(Fd + 16 * mt + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) x[mt][nt] *= fd;
+    }
+    Fr dob[NSB][NN];
+#pragma unroll
+    for (int s = 0; s < NSB; s++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) dob[s][nt] = M::load_col(C.v, SM::LDV, c0 + 16 * nt, s * KS, lane);
+#pragma unroll
+    for (int s = 0; s < NSB; s++)
+#pragma unroll
+      for (int mt = 0; mt < 2 + 2 * s; mt++) {
+        const Fr pf = *reinterpret_cast<const Fr*>(C.p + pt_frag(mt, s) * 1024 + lane * 16);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], pf, dob[s][nt]);
+      }
+    // dy = T^T dx
+    {
+      Fr ys[NSB][NN];
+#pragma unroll
+      for (int s = 0; s < NSB; s++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) ys[s][nt] = acc_as_b<bf16>(x, s, nt);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) x[mt][nt] = zero4();
+#pragma unroll
+      for (int s = 0; s < NSB; s++)
+#pragma unroll
+        for (int mt = 0; mt < 2 + 2 * s; mt++) {
+          const Fr tf = *reinterpret_cast<const Fr*>(C.rec + kRecT + pt_frag(mt, s) * 1024 + lane * 16);
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) M::mma(x[mt][nt], tf, ys[s][nt]);
+        }
+    }
+    // dS <- eC dS' + q^T (fo o dO) - k^T (fk o dy)
+    Fr bq[NSB][NN], bk[NSB][NN];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      const floatx4 fk = *reinterpret_cast<const floatx4*>(Fk + 16 * mt + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) x[mt][nt] *= -fk;
+    }
+#pragma unroll
+    for (int s = 0; s < NSB; s++) {
+      const floatx4 flo = *reinterpret_cast<const floatx4*>(C.fo + s * KS + 4 * g4);
+      const floatx4 fhi = *reinterpret_cast<const floatx4*>(C.fo + s * KS + 16 + 4 * g4);
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) {
+        bk[s][nt] = acc_as_b<bf16>(x, s, nt);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          bq[s][nt][e] = (bf16)((float)dob[s][nt][e] * flo[e]);
+          bq[s][nt][4 + e] = (bf16)((float)dob[s][nt][4 + e] * fhi[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++) {
+      floatx4 acc[NN];
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) acc[nt] = dS[mt][nt] * eC;
+      const int cdk = 32 * (mt >> 1) + 4 * (mt & 1);
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        const bf16x4 qlo = lds_rows4_tr(C.q, SM::LDK, s * KS, cdk, lane, 8);
+        const bf16x4 qhi = lds_rows4_tr(C.q, SM::LDK, s * KS + 16, cdk, lane, 8);
+        const Fr qf{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+        const bf16x4 klo = lds_rows4_tr(C.k, SM::LDK, s * KS, cdk, lane, 8);
+        const bf16x4 khi = lds_rows4_tr(C.k, SM::LDK, s * KS + 16, cdk, lane, 8);
+        const Fr kf{klo[0], klo[1], klo[2], klo[3], khi[0], khi[1], khi[2], khi[3]};
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) {
+          M::mma(acc[nt], qf, bq[s][nt]);
+          M::mma(acc[nt], kf, bk[s][nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) dS[mt][nt] = acc[nt];
+    }
+    lds_barrier();
+  }
+  // dh0 from a sequence's first segment
+  if ((ent.w & kFirst) && a.dh0) {
+    float* dst = a.dh0 + ((int64_t)n * Hv + h) * DK * DV;
+#pragma unroll
+    for (int mt = 0; mt < DKT; mt++)
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) dst[dk_of_row(mt, 4 * g4 + j) * DV + c0 + 16 * nt + ln] = dS[mt][nt][j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. local gradients of one (chunk, head)
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
@@ -1094,8 +1411,14 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
                        b.seq_rev_warm);
     if (int rc = gdn::check_launch("gdn_chunk_bwd(dS scan)")) return rc;
   }
-  hipLaunchKernelGGL((dstate_kernel<E, DK, DV, false>), sgrid, dim3(DsCfg<E, DK, DV, false>::NT), 0,
-                     stream, b);
+  if constexpr (std::is_same<E, bf16>::value && DK == 128 && DV == 128) {
+    // bfloat16 128 x 128 keeps records: the loader / consumer final pass
+    static_assert(uses_prep<E, DK, DV, kStates>(), "the final pass reads the prep's records");
+    hipLaunchKernelGGL((dsr_kernel<DK, DV>), sgrid, dim3(DsrCfg<DK, DV>::NT), 0, stream, b);
+  } else {
+    hipLaunchKernelGGL((dstate_kernel<E, DK, DV, false>), sgrid, dim3(DsCfg<E, DK, DV, false>::NT), 0,
+                       stream, b);
+  }
   if (int rc = gdn::check_launch("gdn_chunk_bwd(dstate)")) return rc;
   if (b.dh0) {  // empty sequences: dh0 = dht (or zero)
     hipLaunchKernelGGL(empty_seq_state_kernel, dim3(N, b.Hv), dim3(256), 0, stream, b.cu, b.dht,

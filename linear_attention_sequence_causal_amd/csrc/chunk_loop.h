@@ -591,6 +591,32 @@ GDN_DEV void buffer_store_elem(E v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uin
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff, 0);
 }
 
+// Fragments of a 64 x 64 upper-triangular operator (P^T, T^T) as A operands
+// that are not entirely below the diagonal: (row block mt, contraction half
+// s) -> index, for (0,0) (0,1) (1,0) (1,1) (2,1) (3,1).
+__host__ __device__ constexpr int pt_frag(int mt, int s) { return mt < 2 ? 2 * mt + s : mt + 2; }
+
+// One 16-byte vector i (< 384) of a record's T fragments, element e of lane l
+// of fragment p_frag(mt, s) = i / 64 being T[16 mt + l%16][32 s + 16 (e/4) +
+// 4 (l/16) + e%4], written to LDS (dst) at its place in the fragments of T^T
+// (the same convention, pt_frag order): the lower fragments of T fill the
+// upper ones of T^T exactly.
+GDN_DEV void store_t_transposed(char* dst, int i, const floatx4& v) {
+  const bf16x8 t = __builtin_bit_cast(bf16x8, v);
+  const int fp = i >> 6, l = i & 63;
+  const int mt = fp < 2 ? fp : (fp + 2) >> 1, s = fp < 2 ? 0 : (fp & 1);
+  const int g = l >> 4, ln = l & 15;
+  // row r = 16 mt + ln of T is column r of T^T: contraction half s' = mt / 2,
+  // lane group (r % 16) / 4, element 4 (mt % 2) + r % 4
+  const int ep = 4 * (mt & 1) + (ln & 3);
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    // column c = 32 s + 16 (e/4) + 4 g + e%4 of T is row c of T^T
+    const int mtp = 2 * s + (e >> 2), lanep = 16 * (ln >> 2) + 4 * g + (e & 3);
+    *reinterpret_cast<bf16*>(dst + pt_frag(mtp, mt >> 1) * 1024 + lanep * 16 + ep * 2) = t[e];
+  }
+}
+
 // Loader registers: one chunk's rows and the first RECB bytes of its record,
 // 16-byte vectors.  The loads go through buffer resources
 // based at the chunk's first row, so a thread's byte offsets are the same for
@@ -644,8 +670,10 @@ struct WsLoad {
     for (int p = 0; p < PR; p++) r[p] = buffer_load16<floatx4>(rr, 16u * tid, 16u * NTL * p);
   }
   // rows into LDS; with q, also its l2norm factors
-  // (with the scale): a q row is QPR consecutive lanes
-  template <class SM>
+  // (with the scale): a q row is QPR consecutive lanes.  T_TRANSPOSED: the
+  // record's T fragments go to LDS as the fragments of T^T (see
+  // store_t_transposed), the rest of the record as it is.
+  template <bool T_TRANSPOSED = false, class SM>
   GDN_DEV void store(SM& sm, int tid, float scale, int use_l2norm) const {
 #pragma unroll
     for (int p = 0; p < PQ; p++) {
@@ -668,7 +696,10 @@ struct WsLoad {
 #pragma unroll
     for (int p = 0; p < PR; p++) {
       const int i = tid + NTL * p;
-      if (i < RV) *reinterpret_cast<floatx4*>(sm.rec + 16 * i) = r[p];
+      if (T_TRANSPOSED && i < 6 * 64)
+        store_t_transposed(sm.rec + kRecT, i, r[p]);
+      else if (i < RV)
+        *reinterpret_cast<floatx4*>(sm.rec + 16 * i) = r[p];
     }
   }
 };
