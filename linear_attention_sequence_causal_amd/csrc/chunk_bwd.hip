@@ -786,11 +786,30 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
   constexpr int CW = CF::CW, NN = CW / 16;
   const int c0 = wave * CW;
 
+  // bfloat16: T_r = (I + diag(beta) L)^-1 diag(beta) comes from the forward
+  // prep's record (its six A fragments, scattered into a row-major bf16 copy
+  // Trm over Tm's space) instead of a solve here; then T = I - T_r L
+  constexpr bool REC_T = std::is_same<E, bf16>::value;
+  static_assert(!REC_T || uses_prep<E, DK, DV, kStates>(), "bfloat16 keeps the prep's records");
+  O* const Trm = reinterpret_cast<O*>(sm.Tm);
+  constexpr int LDT = SM::LDT;
+  static_assert(sizeof(O) * BT * LDT <= sizeof(sm.Tm), "T_r copy within Tm");
+
   zero_upper<O, true, NT>(sm, tid);
   {
     typename CF::PF pf;
     pf.load((const E*)a.q + (int64_t)qa * DK, (const E*)a.k + (int64_t)qa * DK, a.ld_qk,
             (const E*)a.v + (int64_t)h * DV, a.ld_v, a.g + h, a.beta + h, Hv, tc, te, tid);
+    constexpr int TRV = 6 * 64, TRP = (TRV + NT - 1) / NT;  // record vectors of T_r
+    bf16x8 trv[TRP];
+    if constexpr (REC_T) {
+      const char* R = a.rec + ((int64_t)c * Hv + h) * kRecBytes + kRecT;
+#pragma unroll
+      for (int p = 0; p < TRP; p++) {
+        const int i = tid + NT * p;
+        if (i < TRV) trv[p] = *reinterpret_cast<const bf16x8*>(R + 16 * i);
+      }
+    }
     typedef typename Vec16<E>::type V16;
     constexpr int VE = Vec16<E>::N, VPR = DV / VE;
     const E* dop = (const E*)a.d_o + (int64_t)h * DV;
@@ -801,14 +820,72 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
           t < te ? *reinterpret_cast<const V16*>(dop + (t * Hv) * DV + vi * VE) : zero_vec16<E>();
     }
     stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
+    if constexpr (REC_T) {
+      // vector i: fragment p_frag(mt, s) = i / 64, lane l = i % 64, elements
+      // T_r[16 mt + l%16][32 s + 16 h + 4(l/16) + e], h = 0, 1, e = 0..3
+#pragma unroll
+      for (int p = 0; p < TRP; p++) {
+        const int i = tid + NT * p;
+        if (i < TRV) {
+          const int fp = i >> 6, l = i & 63;
+          const int mt = fp < 2 ? fp : (fp + 2) >> 1, s2 = fp < 2 ? 0 : (fp & 1);
+          O* dst = Trm + (16 * mt + (l & 15)) * LDT + 32 * s2 + 4 * (l >> 4);
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{trv[p][0], trv[p][1], trv[p][2], trv[p][3]};
+          *reinterpret_cast<bf16x4*>(dst + 16) = bf16x4{trv[p][4], trv[p][5], trv[p][6], trv[p][7]};
+        }
+      }
+    }
   }
   __syncthreads();
-  gram_kk<O, DK, NW>(sm, wave, lane);
-  __syncthreads();
-  solve<O, DK, NW, true>(sm, wave, lane);
   floatx4 vn[4][NN];
-  compute_u<O, NN>(sm, c0, lane, vn);  // u, turned into Vn below
-  compute_w<O, DK, NW>(sm, wave, lane);
+  if constexpr (REC_T) {
+    // L and P tiles; u = T_r v (this wave's columns); W = T_r diag(e^G) kh
+    for (int t = wave; t < 20; t += NW) {
+      int ti, tj;
+      lower_tile_ij(t % 10, ti, tj);
+      gram_tile<O, DK>(sm, t >= 10, ti, tj, lane);
+    }
+    {
+      typename M::frag b[NSB][NN];
+#pragma unroll
+      for (int s = 0; s < NSB; s++)
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) b[s][nt] = M::load_col(sm.v, LDV, c0 + 16 * nt, s * KS, lane);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) vn[mt][nt] = zero4();
+#pragma unroll
+        for (int s = 0; s < NSB; s++)
+          if (2 * s <= mt) {  // the fragments right of the diagonal are zero
+            const typename M::frag tf = M::load(Trm, LDT, 16 * mt, s * KS, lane);
+#pragma unroll
+            for (int nt = 0; nt < NN; nt++) M::mma(vn[mt][nt], tf, b[s][nt]);
+          }
+      }
+    }
+    {
+      constexpr int NTILE = 4 * (DK / 16);
+      for (int tt = wave; tt < NTILE; tt += NW) {
+        const int mt = tt % 4, nt = tt / 4;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < NSB; s++)
+          if (2 * s <= mt)
+            M::mma(acc, M::load(Trm, LDT, 16 * mt, s * KS, lane),
+                   M::load_col_scaled(sm.k, SM::LDK, 16 * nt, s * KS, sm.eg, lane));
+        const int rb = 16 * mt + 4 * g4, cc = 16 * nt + ln;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) sm.w[(rb + jj) * SM::LDK + cc] = from_f<O>(acc[jj]);
+      }
+    }
+  } else {
+    gram_kk<O, DK, NW>(sm, wave, lane);
+    __syncthreads();
+    solve<O, DK, NW, true>(sm, wave, lane);
+    compute_u<O, NN>(sm, c0, lane, vn);  // u, turned into Vn below
+    compute_w<O, DK, NW>(sm, wave, lane);
+  }
   __syncthreads();
 
   const float GC = sm.G[BT - 1];
@@ -929,7 +1006,23 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 #pragma unroll
     for (int nt = 0; nt < NN; nt++) dvn[mt][nt] = pp[nt];
   }
-  // Y = T^T dVn; dv = beta o Y
+  // Y = T^T dVn; dv = beta o Y (bfloat16: dv = T_r^T dVn, then Y = dVn -
+  // L^T dv, since T = I - T_r L)
+  floatx4 dvr[REC_T ? 4 : 1][NN];
+  if constexpr (REC_T) {
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) dvr[mt][nt] = zero4();
+#pragma unroll
+      for (int s = 0; s < NSB; s++)
+        if (mt < 2 + 2 * s) {  // the fragments left of the diagonal are zero
+          const typename M::frag tt = M::load_col(Trm, LDT, 16 * mt, s * KS, lane);
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) M::mma(dvr[mt][nt], tt, acc_as_b<O>(dvn, s, nt));
+        }
+    }
+  }
   floatx4 y[4][NN];
   float r_b[4][4], r_yks[4][4];
   // dv, dq and dk rows of this chunk through buffer resources (rows past the
@@ -943,13 +1036,27 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
     floatx4 yy[NN];
+    if constexpr (REC_T) {
 #pragma unroll
-    for (int nt = 0; nt < NN; nt++) yy[nt] = zero4();
+      for (int nt = 0; nt < NN; nt++) yy[nt] = dvn[mt][nt];
 #pragma unroll
-    for (int s = 0; s < NSB; s++) {
-      const typename M::frag tt = M::load_col_f32(sm.Tm, SM::LDF, 16 * mt, s * KS, nullptr, lane);
+      for (int s = 0; s < NSB; s++)
+        if (mt < 2 + 2 * s) {
+          typename M::frag lt = M::load_col_f32(sm.L, SM::LDF, 16 * mt, s * KS, nullptr, lane);
 #pragma unroll
-      for (int nt = 0; nt < NN; nt++) M::mma(yy[nt], tt, acc_as_b<O>(dvn, s, nt));
+          for (int e = 0; e < 8; e++) lt[e] = -lt[e];  // -L^T
+#pragma unroll
+          for (int nt = 0; nt < NN; nt++) M::mma(yy[nt], lt, acc_as_b<O>(dvr, s, nt));
+        }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NN; nt++) yy[nt] = zero4();
+#pragma unroll
+      for (int s = 0; s < NSB; s++) {
+        const typename M::frag tt = M::load_col_f32(sm.Tm, SM::LDF, 16 * mt, s * KS, nullptr, lane);
+#pragma unroll
+        for (int nt = 0; nt < NN; nt++) M::mma(yy[nt], tt, acc_as_b<O>(dvn, s, nt));
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) r_b[mt][j] = r_yks[mt][j] = 0.f;
@@ -962,7 +1069,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
         const int row = 16 * mt + 4 * g4 + j;
         r_b[mt][j] += yy[nt][j] * vv[j];
         r_yks[mt][j] += yy[nt][j] * ks[mt][nt][j];
-        buffer_store_elem<E>(from_f<E>(sm.beta[row] * yy[nt][j]), rdv, dvoff,
+        const float dvj = REC_T ? dvr[REC_T ? mt : 0][nt][j] : sm.beta[row] * yy[nt][j];
+        buffer_store_elem<E>(from_f<E>(dvj), rdv, dvoff,
                              (uint32_t)(((16 * mt + j) * a.ld_dv + 16 * nt) * (int64_t)sizeof(E)));
       }
     }
