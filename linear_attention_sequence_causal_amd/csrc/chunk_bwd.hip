@@ -736,7 +736,7 @@ __global__ __launch_bounds__((DsrCfg<DK, DV>::NT)) void dsr_kernel(BwdArgs a) {
 // 3. local gradients of one (chunk, head)
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
-struct GradSmem {
+struct GradSmemCore {
   typedef Smem<E, DK, DV, true> SM;
   static constexpr int LDA = BT + 4;  // dA, dA^T, M1 + M1^T: [64][68] operand type
   static constexpr int NW = BwdCfg<E, DK, DV>::NW;
@@ -752,6 +752,16 @@ struct GradSmem {
   // backward in place)
   alignas(16) float epi[2][NW][BT];
   alignas(16) float etot[2][BT];
+};
+// bfloat16, with room in LDS: dA gets its own array (else it goes over L,
+// which the dL tiles read, and the dL and dP tiles run in two phases; the
+// float32 kernels, short of registers, keep that form).
+template <typename E, int DK, int DV>
+struct GradSmem : GradSmemCore<E, DK, DV> {
+  typedef GradSmemCore<E, DK, DV> Core;
+  static constexpr bool DA_OWN =
+      std::is_same<E, bf16>::value && sizeof(Core) + sizeof(E) * BT * Core::LDA + 256 <= 160 * 1024;
+  alignas(16) E da_own[DA_OWN ? BT * Core::LDA : 8];
 };
 
 // row-partials kinds
@@ -1111,7 +1121,7 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
 
   // dL = -Y Vn^T (strict lower): M1 + M1^T, dbeta and dG partials
   O* sMs = GS::MS_IN_V ? sm.v : gs.ms_own;
-  for (int t = wave; t < 10; t += NW) {
+  auto dl_tile = [&](int t) {
     int i, j;
     lower_tile_ij(t, i, j);
     floatx4 acc = zero4();
@@ -1149,14 +1159,10 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     cl += __shfl_xor(cl, 16, 64);
     cl += __shfl_xor(cl, 32, 64);
     if (g4 == 0) gs.tp[kColL][i][col] = cl;
-  }
-  __syncthreads();
-
-  // dP = dO Vn^T (lower incl): dA = dP o Gamma into L's region; dG partials
-  O* sdA = reinterpret_cast<O*>(sm.L);
-  floatx4 dat[(10 + NW - 1) / NW];
-  int nmine = 0;
-  for (int t = wave; t < 10; t += NW, nmine++) {
+  };
+  // dP = dO Vn^T (lower incl): dA = dP o Gamma; dG partials
+  O* sdA = GS::DA_OWN ? gs.da_own : reinterpret_cast<O*>(sm.L);
+  auto dp_tile = [&](int t) -> floatx4 {
     int i, j;
     lower_tile_ij(t, i, j);
     floatx4 acc = zero4();
@@ -1177,7 +1183,6 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
       sdA[row * LDA + col] = from_f<O>(da[jj]);
       if (i > j) sdA[(16 * j + 4 * g4 + jj) * LDA + 16 * i + ln] = from_f<O>(0.f);
     }
-    dat[nmine] = da;
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) {
       const float a1 = row16_sum(rp[jj]);
@@ -1186,18 +1191,41 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     cp += __shfl_xor(cp, 16, 64);
     cp += __shfl_xor(cp, 32, 64);
     if (g4 == 0) gs.tp[kColP][i][col] = cp;
+    return da;
+  };
+  // the dP tiles of this wave (tile index, dA values) for dA^T below
+  constexpr int NDP = GS::DA_OWN ? (20 + NW - 1) / NW : (10 + NW - 1) / NW;
+  floatx4 dat[NDP];
+  int dpt[NDP];
+  int nmine = 0;
+  if constexpr (GS::DA_OWN) {
+    // the dL and dP tiles in one phase (dA does not go over L)
+    for (int t = wave; t < 20; t += NW) {
+      if (t < 10) {
+        dl_tile(t);
+      } else {
+        dat[nmine] = dp_tile(t - 10);
+        dpt[nmine++] = t - 10;
+      }
+    }
+  } else {
+    for (int t = wave; t < 10; t += NW) dl_tile(t);
+    __syncthreads();  // L reads done: dA goes over L
+    for (int t = wave; t < 10; t += NW) {
+      dat[nmine] = dp_tile(t);
+      dpt[nmine++] = t;
+    }
   }
   __syncthreads();  // P reads done: dA^T goes over p
   O* sdAT = sm.p;
-  nmine = 0;
-  for (int t = wave; t < 10; t += NW, nmine++) {
+  for (int m = 0; m < nmine; m++) {
     int i, j;
-    lower_tile_ij(t, i, j);
+    lower_tile_ij(dpt[m], i, j);
     const int col = 16 * j + ln;
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) {
       const int row = 16 * i + 4 * g4 + jj;
-      sdAT[col * LDA + row] = from_f<O>(dat[nmine][jj]);
+      sdAT[col * LDA + row] = from_f<O>(dat[m][jj]);
       if (i > j) sdAT[(16 * i + 4 * g4 + jj) * LDA + 16 * j + ln] = from_f<O>(0.f);
     }
   }
