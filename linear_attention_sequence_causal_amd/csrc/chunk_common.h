@@ -155,13 +155,8 @@ GDN_DEV void stage(SM& sm, const Prefetch<E, DK, DV, NT, HAS_Q>& pf, float scale
     const int row = i / PF::VPR, vi = i % PF::VPR;
     if (i < PF::VV) *reinterpret_cast<OV*>(sm.v + row * SM::LDV + vi * VE) = pf.v[p];
   }
-  if (tid < BT) {  // wave 0: inclusive scan of g over the 64 rows
-    float G = pf.g;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(G, off, 64);
-      if (tid >= off) G += o;
-    }
+  if (tid < BT) {  // wave 0: inclusive scan of g over the 64 rows (DPP, as the prep's)
+    const float G = wave_incl_scan(pf.g);
     const float eG = __expf(G);
     sm.G[tid] = G;
     sm.beta[tid] = pf.beta;
