@@ -1086,7 +1086,7 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     }
   }
   // row sums over this wave's columns
-  dot = group_sum<64>(dot);
+  dot = wave_sum(dot);
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
 #pragma unroll
@@ -1156,8 +1156,7 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
         gs.tp[kRowL][j][16 * i + 4 * g4 + jj] = a2;
       }
     }
-    cl += __shfl_xor(cl, 16, 64);
-    cl += __shfl_xor(cl, 32, 64);
+    cl = rows4_sum(cl);
     if (g4 == 0) gs.tp[kColL][i][col] = cl;
   };
   // dP = dO Vn^T (lower incl): dA = dP o Gamma; dG partials
@@ -1188,8 +1187,7 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
       const float a1 = row16_sum(rp[jj]);
       if (ln == 0) gs.tp[kRowP][j][16 * i + 4 * g4 + jj] = a1;
     }
-    cp += __shfl_xor(cp, 16, 64);
-    cp += __shfl_xor(cp, 32, 64);
+    cp = rows4_sum(cp);
     if (g4 == 0) gs.tp[kColP][i][col] = cp;
     return da;
   };
@@ -1375,15 +1373,11 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     const float d = __expf(GC - sm.G[r]);
     const float dbeta = rB - gm * rYKS + rowKK;
     float dG = gm * rDOQS - d * rKDSVN - bt * gm * rYKS + rowP - colP + rowL - colL;
-    const float tail = group_sum<64>(d * rKDSVN) + __expf(GC) * dotS;  // d/dG_C terms
+    const float tail = wave_sum(d * rKDSVN) + __expf(GC) * dotS;  // d/dG_C terms
     if (r == BT - 1) dG += tail;
-    // dg_t = sum_{s >= t} dG_s within the chunk
-    float suf = dG;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_down(suf, off, 64);
-      if (r + off < 64) suf += o;
-    }
+    // dg_t = sum_{s >= t} dG_s within the chunk: a prefix scan of the rows
+    // in reverse order
+    const float suf = __shfl(wave_incl_scan(__shfl(dG, BT - 1 - r, 64)), BT - 1 - r, 64);
     const int64_t t = tc + r;
     if (t < te) {
       a.dbeta[t * Hv + h] = dbeta;

@@ -327,6 +327,24 @@ GDN_DEV float wave_incl_scan(float v) {
   return v;
 }
 
+// Sum over the whole wave (the inclusive scan's last lane), in every lane.
+GDN_DEV float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan(v)), 63));
+}
+
+// Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows at one
+// position) with the gfx950 row swaps: v_permlane16_swap of a register with
+// itself leaves rows (0, 0, 2, 2) and (1, 1, 3, 3), v_permlane32_swap halves
+// (lo, lo) and (hi, hi), so each sum of the pair is a sum over the partners.
+GDN_DEV float rows4_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float s16 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(s16);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum of squares of a 16-byte activation vector (bf16: pairwise dot
 // products accumulated in fp32).
 GDN_DEV float sum_sq(const floatx4& v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
