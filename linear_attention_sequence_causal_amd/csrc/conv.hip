@@ -27,14 +27,22 @@ constexpr int kRunsPerBlock = 4;   // blockDim.y
 constexpr int kLanes = 64;         // blockDim.x: channel vectors per block
 constexpr int kFwdRows = 8;        // tokens per thread run, forward
 constexpr int kBwdRows = 16;       // tokens per thread run, backward
-constexpr int kBwdPrefetch = 3;    // rows in flight ahead of the one formed, backward
+// backward shape: four channels a thread (8-byte rows for bfloat16, which
+// leaves registers for three waves a SIMD and four rows in flight ahead of
+// the one formed; 16-byte rows, two waves a SIMD and three rows for float32)
+template <typename E> struct BwdShape {
+  static constexpr int V = 4;
+  static constexpr int PD = sizeof(E) == 2 ? 4 : 3;
+  static constexpr int WAVES = sizeof(E) == 2 ? 3 : 2;  // a SIMD; also four-wave blocks a CU
+};
 constexpr int kBwdMaxSplits = 64;  // most token splits of the backward grid (dw partial rows)
 
 // V channels of one row: a packed 16-byte vector when V*sizeof(E) == 16
 // (bf16 stays two to a register), else V scalars.
-template <typename E, int V, bool VEC = (V * sizeof(E) == 16)> struct Row;
+template <typename E, int V, bool VEC = (V * sizeof(E) == 16 || V * sizeof(E) == 8)> struct Row;
 template <typename E, int V> struct Row<E, V, true> {
-  typename Vec16<E>::type v;
+  typedef E VT __attribute__((ext_vector_type(V)));
+  VT v;
   GDN_DEV float at(int i) const { return to_f(v[i]); }
 };
 template <typename E, int V> struct Row<E, V, false> {
@@ -45,8 +53,8 @@ template <typename E, int V> struct Row<E, V, false> {
 template <typename E, int V>
 __device__ __forceinline__ Row<E, V> load_row(const E* p) {
   Row<E, V> r;
-  if constexpr (V * sizeof(E) == 16) {
-    r.v = *reinterpret_cast<const typename Vec16<E>::type*>(p);
+  if constexpr (V * sizeof(E) == 16 || V * sizeof(E) == 8) {
+    r.v = *reinterpret_cast<const typename Row<E, V>::VT*>(p);
   } else {
 #pragma unroll
     for (int i = 0; i < V; i++) r.v[i] = p[i];
@@ -58,8 +66,8 @@ __device__ __forceinline__ Row<E, V> load_row(const E* p) {
 // and dx, are not read again before they would leave them)
 template <typename E, int V, bool NT = false>
 __device__ __forceinline__ void store_row(E* p, const float* f) {
-  if constexpr (V * sizeof(E) == 16) {
-    typedef typename Vec16<E>::type VT;
+  if constexpr (V * sizeof(E) == 16 || V * sizeof(E) == 8) {
+    typedef typename Row<E, V>::VT VT;
     VT t;
 #pragma unroll
     for (int i = 0; i < V; i++) t[i] = from_f<E>(f[i]);
@@ -76,8 +84,8 @@ __device__ __forceinline__ void store_row(E* p, const float* f) {
 template <typename E, int V>
 __device__ __forceinline__ Row<E, V> zero_row() {
   Row<E, V> r;
-  if constexpr (V * sizeof(E) == 16) {
-    r.v = zero_vec16<E>();
+  if constexpr (V * sizeof(E) == 16 || V * sizeof(E) == 8) {
+    r.v = typename Row<E, V>::VT{};
   } else {
 #pragma unroll
     for (int i = 0; i < V; i++) r.v[i] = from_f<E>(0.f);
@@ -203,20 +211,21 @@ __global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_fwd_kernel(
 // sequence 0, and accumulates dw/dbias over its own tokens.  The rows stream
 // through windows of the last K x rows, dz rows and sequence ends: dx of
 // token t - (K-1) is formed once dz[t] is known, while the x and dy rows of
-// the next kBwdPrefetch tokens are already being read.  A block loops over
+// the next few tokens (BwdShape::PD) are already being read.  A block loops over
 // token tiles with a fixed grid stride (the grid is at most one round of
 // blocks); its four runs' sums are added in LDS and written as one partial
 // row, and a second kernel adds the partial rows in a fixed order
 // (deterministic dw).
 template <typename E, int K, int V>
-__global__ __launch_bounds__(kLanes* kRunsPerBlock) void conv_bwd_kernel(
+__global__ __launch_bounds__(kLanes* kRunsPerBlock) __attribute__((amdgpu_waves_per_eu(BwdShape<E>::WAVES)))
+void conv_bwd_kernel(
     const E* __restrict__ x, const E* __restrict__ w, const E* __restrict__ bias,
     const E* __restrict__ halo, const int32_t* __restrict__ cu, int N, int64_t T, int C,
     const gdn_cp_meta* __restrict__ meta, const E* __restrict__ dy, E* __restrict__ dx,
     E* __restrict__ dhalo, float* __restrict__ part_w, float* __restrict__ part_b) {
   constexpr int R = kBwdRows;
   constexpr int DR = R + K - 1;  // dz rows t0 .. t0+R+K-2
-  constexpr int PD = kBwdPrefetch < DR ? kBwdPrefetch : DR;
+  constexpr int PD = BwdShape<E>::PD < DR ? BwdShape<E>::PD : DR;
   __shared__ float red[kLanes][V * (K + 1)];
   const int c0 = (blockIdx.y * kLanes + threadIdx.x) * V;
   const bool active = c0 < C;
@@ -490,19 +499,19 @@ int bwd_splits(int64_t T) {
   return (int)(tiles < kBwdMaxSplits ? (tiles < 1 ? 1 : tiles) : kBwdMaxSplits);
 }
 
-// the splits a launch uses: no more blocks than run at once (two four-wave
-// blocks a CU at two waves a SIMD), since a second, partial round of these
+// the splits a launch uses: no more blocks than run at once (as many four-wave
+// blocks a CU as waves a SIMD), since a second, partial round of these
 // long-running blocks would keep part of the chip idle
-int bwd_launch_splits(int64_t T, int cgroups) {
+int bwd_launch_splits(int64_t T, int cgroups, int blocks_per_cu) {
   const int cap = bwd_splits(T);
-  const int64_t fit = 2 * (int64_t)gdn::device_cu_count() / (cgroups > 0 ? cgroups : 1);
+  const int64_t fit = blocks_per_cu * (int64_t)gdn::device_cu_count() / (cgroups > 0 ? cgroups : 1);
   return (int)(fit < 1 ? 1 : (fit < cap ? fit : cap));
 }
 
 template <typename E, int K>
 int launch_bwd_k(const ConvArgs& a, const void* dy, void* dx, float* dw, float* dbias, void* dhalo,
                  void* ws, hipStream_t stream) {
-  constexpr int VE = Vec16<E>::N;
+  constexpr int VE = BwdShape<E>::V;
   const bool vec = (a.C % VE == 0) && gdn::aligned16(a.x) && gdn::aligned16(dy) &&
                    gdn::aligned16(dx) && (a.halo == nullptr || gdn::aligned16(a.halo)) &&
                    (dhalo == nullptr || gdn::aligned16(dhalo));
@@ -510,7 +519,7 @@ int launch_bwd_k(const ConvArgs& a, const void* dy, void* dx, float* dw, float* 
   const int cvec = (a.C + V - 1) / V;
   const int cgroups = (cvec + kLanes - 1) / kLanes;
   if (cgroups > 65535) return gdn::fail(GDN_EINVAL, "conv: C too large");
-  const int P = a.T > 0 ? bwd_launch_splits(a.T, cgroups) : 0;
+  const int P = a.T > 0 ? bwd_launch_splits(a.T, cgroups, BwdShape<E>::WAVES) : 0;
   float* part_w = (float*)ws;
   float* part_b = part_w + (size_t)P * a.C * K;
   dim3 block(kLanes, kRunsPerBlock);
