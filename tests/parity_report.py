@@ -1,7 +1,7 @@
 """Turns the parity log of a GPU test run into a markdown table.
 
-    GDN_PARITY_LOG=gpurun_out/parity.jsonl python -m pytest tests -m gpu ...
-    python tests/parity_report.py gpurun_out/parity.jsonl > profiles/parity.md
+    GDN_PARITY_LOG=/tmp/parity.jsonl python -m pytest tests -m gpu ...
+    python tests/parity_report.py /tmp/parity.jsonl "<the test command>" > profiles/parity.md
 
 Each line of the log is one comparison made by tests/helpers.assert_close:
 the test id, the tensor, max|got - ref| / max|ref| and the tolerance.  The
