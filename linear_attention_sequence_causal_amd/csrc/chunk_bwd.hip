@@ -1119,6 +1119,16 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     }
   __syncthreads();
 
+  // the key side's S and dS' fragments (B[k = value idx][n = key idx] =
+  // S[n][k]), loaded here so that they arrive during the dL and dP tiles
+  typename M::frag kst[NN][NSK], kdst[NN][NSK];
+#pragma unroll
+  for (int nt = 0; nt < NN; nt++)
+#pragma unroll
+    for (int s = 0; s < NSK; s++) {
+      kst[nt][s] = M::load(Sg, DV, c0 + 16 * nt, s * KS, lane);
+      kdst[nt][s] = M::load(dSg, DV, c0 + 16 * nt, s * KS, lane);
+    }
   // dL = -Y Vn^T (strict lower): M1 + M1^T, dbeta and dG partials
   O* sMs = GS::MS_IN_V ? sm.v : gs.ms_own;
   auto dl_tile = [&](int t) {
@@ -1247,8 +1257,8 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     typename M::frag st[NSK], dst[NSK], kc[NSB], qc[NSB];
 #pragma unroll
     for (int s = 0; s < NSK; s++) {
-      st[s] = M::load(Sg, DV, dc, s * KS, lane);    // B[k = value idx][n = key idx] = S[n][k]
-      dst[s] = M::load(dSg, DV, dc, s * KS, lane);
+      st[s] = kst[nt][s];
+      dst[s] = kdst[nt][s];
     }
 #pragma unroll
     for (int s = 0; s < NSB; s++) {
