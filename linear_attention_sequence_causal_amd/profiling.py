@@ -15,6 +15,11 @@ profiles/, and the plain copy used to calibrate the HBM byte counters.
         --match chunk_ws_kernel --match chunk_loop_kernel --match seg_scan --match plan_kernel \
         --cmd "<commands>" --out profiles/<name>.md --json profiles/<name>.json
 
+    # SQ counter passes -> per-kernel table (mean over each kernel's dispatches)
+    python -m linear_attention_sequence_causal_amd.profiling counters \
+        --csv <pass1>/run_counter_collection.csv --csv <pass2>/run_counter_collection.csv \
+        --match grad_kernel --match dsr_kernel --cmd "<commands>" --out profiles/<name>.md
+
 FETCH_SIZE and WRITE_SIZE are reported by rocprofv3 in KiB per dispatch.
 Each is divided by what the same counter reads per byte of the plain copy
 (which reads and writes exactly its size once), giving HBM bytes.
@@ -142,6 +147,42 @@ def stats(args) -> None:
     print(text)
 
 
+def counters(args) -> None:
+    """SQ counters of several rocprofv3 --pmc passes: for each kernel whose name
+    contains one of the --match strings, the mean over its dispatches of each
+    counter (summed over the device as rocprofv3 reports it), and per wave."""
+    per = defaultdict(lambda: defaultdict(list))  # kernel -> counter -> values
+    for path in args.csv:
+        for kname, vals in _read_counters(path).values():
+            if not any(m in kname for m in args.match):
+                continue
+            for cn, v in vals.items():
+                per[kname][cn].append(v)
+    kernels = sorted(per)
+    names = sorted({cn for k in kernels for cn in per[k]})
+    short = [k if len(k) < 70 else k[:67] + "..." for k in kernels]
+    lines = ["# SQ counters: %s" % args.title, "", "Commands (each under `timeout -s KILL 90`, from "
+             "the repository root):", ""] + ["    %s" % c for c in args.cmd] + [
+             "", "Values per dispatch (mean over the dispatches of each kernel in a run), summed "
+             "over the device as rocprofv3 reports them; the second column of each kernel is per "
+             "wave (SQ_WAVES).", "",
+             "| counter | " + " | ".join("`%s` | per wave" % k for k in short) + " |",
+             "|---|" + "---|---|" * len(kernels)]
+    for cn in names:
+        cells = []
+        for k in kernels:
+            v = per[k].get(cn, [])
+            m = sum(v) / len(v) if v else float("nan")
+            w = per[k].get("SQ_WAVES", [])
+            waves = sum(w) / len(w) if w else float("nan")
+            cells.append("%.4g | %.4g" % (m, m / waves if waves else float("nan")))
+        lines.append("| `%s` | %s |" % (cn, " | ".join(cells)))
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -163,11 +204,19 @@ def main(argv=None) -> None:
     t.add_argument("--title", default="")
     t.add_argument("--json", default=None)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    q = sub.add_parser("counters")
+    q.add_argument("--csv", action="append", required=True)
+    q.add_argument("--match", action="append", required=True)
+    q.add_argument("--cmd", action="append", default=[])
+    q.add_argument("--title", default="")
+    q.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd_name == "copy":
         _copy(a.mib, a.reps)
     elif a.cmd_name == "stats":
         stats(a)
+    elif a.cmd_name == "counters":
+        counters(a)
     else:
         traffic(a)
 
