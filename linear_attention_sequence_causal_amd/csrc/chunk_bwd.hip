@@ -1551,8 +1551,8 @@ int launch_bwd(BwdArgs b, const LoopArgs& la_in, int N, int64_t T, const BwdLayo
                        b.seq_rev_warm);
     if (int rc = gdn::check_launch("gdn_chunk_bwd(dS scan)")) return rc;
   }
-  if constexpr (std::is_same<E, bf16>::value && DK == 128 && DV == 128) {
-    // bfloat16 128 x 128 keeps records: the loader / consumer final pass
+  if constexpr (std::is_same<E, bf16>::value && DK == DV && (DV == 128 || DV == 64)) {
+    // bfloat16 keeps records: the loader / consumer final pass
     static_assert(uses_prep<E, DK, DV, kStates>(), "the final pass reads the prep's records");
     hipLaunchKernelGGL((dsr_kernel<DK, DV>), sgrid, dim3(DsrCfg<DK, DV>::NT), 0, stream, b);
   } else {

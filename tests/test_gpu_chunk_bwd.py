@@ -81,6 +81,14 @@ def test_segmented_state_pass(seg):
     _check_bwd(y, g * 0.05, beta, h0, do, dht, cu, 2, 4, 128, seg=seg)
 
 
+def test_segmented_state_pass_d64():
+    """Head size 64 in bfloat16 with segments of 2 chunks: the final dS pass
+    from segment inputs, with replay and summaries both taken."""
+    y, g, beta, h0, do, dht, cu = _inputs(61, [1, 64, 130, 0, 400], 2, 4, 64, torch.bfloat16)
+    g[:, 2:] *= 0.02
+    _check_bwd(y, g, beta, h0, do, dht, cu, 2, 4, 64, seg=2)
+
+
 @pytest.mark.parametrize("variant", ["mixed_heads", "beta_above_one"])
 def test_replay_and_summaries(variant):
     """Both recurrences (the forward's states and the backward's dS) choose
