@@ -425,8 +425,8 @@ __global__ __launch_bounds__((DsCfg<E, DK, DV, SUM>::NT)) void dstate_kernel(Bwd
 //   dx = P^T dO + fd o (k dS'),   dy = T^T dx,
 //   dS = eC dS' + q^T (fo o dO) - k^T (fk o dy).
 // Four loader waves stage q, k, dO and the record of the chunk before (the
-// chunks run in reverse) and make P^T and T^T as A fragments; eight consumer
-// waves carry 16 columns of dS each in MFMA accumulators (dk rows permuted as
+// chunks run in reverse) and make P^T and T^T as A fragments; dv / 32 consumer
+// waves carry 32 columns of dS each in MFMA accumulators (dk rows permuted as
 // in the forward), store dS' of every chunk for the gradient kernel and write
 // dh0 at a sequence's first segment.  Replay and the initial dS as in
 // dstate_kernel's final mode.
@@ -483,7 +483,7 @@ struct PtHalf {
 
 template <int DK, int DV>
 struct DsrCfg {
-  static constexpr int CW = 16;          // dS columns a consumer wave
+  static constexpr int CW = 32;          // dS columns a consumer wave
   static constexpr int NC = DV / CW;     // consumer waves
   static constexpr int NL = 4;           // loader waves
   static constexpr int NT = (NC + NL) * 64;
