@@ -822,8 +822,9 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     }
     typedef typename Vec16<E>::type V16;
     constexpr int VE = Vec16<E>::N, VPR = DV / VE;
-    // dO rows: every vector of the thread loaded before any is stored, so the
-    // loads are in flight together
+    // dO rows: every vector of the thread loaded (from a valid row: past the
+    // sequence end the chunk's first, zeroed after) before any is stored, so
+    // the loads are in flight together
     const E* dop = (const E*)a.d_o + (int64_t)h * DV;
     constexpr int DOP = (BT * VPR + NT - 1) / NT;
     V16 dov[DOP];
@@ -831,13 +832,15 @@ __global__ __launch_bounds__((BwdCfg<E, DK, DV>::NT)) void grad_kernel(BwdArgs a
     for (int p = 0; p < DOP; p++) {
       const int i = tid + NT * p;
       const int64_t t = tc + i / VPR;
-      dov[p] = (i < BT * VPR && t < te) ? *reinterpret_cast<const V16*>(dop + (t * Hv) * DV + (i % VPR) * VE)
-                                        : zero_vec16<E>();
+      const bool ok = i < BT * VPR && t < te;
+      dov[p] = *reinterpret_cast<const V16*>(dop + ((ok ? t : tc) * Hv) * DV + (ok ? i % VPR : 0) * VE);
     }
 #pragma unroll
     for (int p = 0; p < DOP; p++) {
       const int i = tid + NT * p;
-      if (i < BT * VPR) *reinterpret_cast<V16*>(gs.dO + (i / VPR) * LDV + (i % VPR) * VE) = dov[p];
+      if (i < BT * VPR)
+        *reinterpret_cast<V16*>(gs.dO + (i / VPR) * LDV + (i % VPR) * VE) =
+            tc + i / VPR < te ? dov[p] : zero_vec16<E>();
     }
     stage<E, O, DK, DV, NT, true>(sm, pf, a.scale, a.use_l2norm, tid);
     if constexpr (REC_T) {

@@ -75,23 +75,38 @@ struct Prefetch {
   GDN_DEV void load(const E* __restrict__ qp, const E* __restrict__ kp, int64_t ld_qk,
                     const E* __restrict__ vp, int64_t ld_v, const float* __restrict__ gp,
                     const float* __restrict__ bp, int Hv, int64_t tc, int64_t te, int tid) {
+    // Every load reads a valid row (past the sequence end or the tile: the
+    // chunk's first row, which always holds a token) and the unused ones are
+    // zeroed after, so no load sits behind a branch and all are in flight at
+    // once.
 #pragma unroll
     for (int p = 0; p < PQ; p++) {
       const int i = tid + NT * p;
-      const int row = i / QPR, vi = i % QPR;
-      const int64_t t = tc + row;
+      const int64_t t = tc + i / QPR;
       const bool ok = (i < QV) && (t < te);
-      if constexpr (HAS_Q)
-        q[p] = ok ? *reinterpret_cast<const V16*>(qp + t * ld_qk + vi * VE) : zero_vec16<E>();
-      k[p] = ok ? *reinterpret_cast<const V16*>(kp + t * ld_qk + vi * VE) : zero_vec16<E>();
+      const int64_t off = (ok ? t : tc) * ld_qk + (ok ? i % QPR : 0) * VE;
+      if constexpr (HAS_Q) q[p] = *reinterpret_cast<const V16*>(qp + off);
+      k[p] = *reinterpret_cast<const V16*>(kp + off);
     }
 #pragma unroll
     for (int p = 0; p < PV; p++) {
       const int i = tid + NT * p;
-      const int row = i / VPR, vi = i % VPR;
-      const int64_t t = tc + row;
+      const int64_t t = tc + i / VPR;
       const bool ok = (i < VV) && (t < te);
-      v[p] = ok ? *reinterpret_cast<const V16*>(vp + t * ld_v + vi * VE) : zero_vec16<E>();
+      v[p] = *reinterpret_cast<const V16*>(vp + (ok ? t : tc) * ld_v + (ok ? i % VPR : 0) * VE);
+    }
+#pragma unroll
+    for (int p = 0; p < PQ; p++) {
+      const int i = tid + NT * p;
+      if (!((i < QV) && (tc + i / QPR < te))) {
+        if constexpr (HAS_Q) q[p] = zero_vec16<E>();
+        k[p] = zero_vec16<E>();
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PV; p++) {
+      const int i = tid + NT * p;
+      if (!((i < VV) && (tc + i / VPR < te))) v[p] = zero_vec16<E>();
     }
     g = 0.f;
     beta = 0.f;

@@ -200,18 +200,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GDN_PREP_WA
   float gn = 0.f, bn = 0.f;
   if (tg < te) gdn_gate::load_gates<bf16>(a.gates, tg, qa * GR, a.Hv, gn, bn);
 
-  // raw k rows (zero past the sequence end) and their l2norm factors
+  // raw k rows (zero past the sequence end) and their l2norm factors; every
+  // load reads a valid row (past the end the chunk's first, zeroed after) and
+  // all are issued before the first store, so they are in flight together
   {
     typedef bf16x8 V;
-    constexpr int QPR = DK / 8;
+    constexpr int QPR = DK / 8, KP = 64 * QPR / 256;
     const bf16* kp = (const bf16*)a.k + (int64_t)qa * DK;
+    V kr[KP];
 #pragma unroll
-    for (int p = 0; p < 64 * QPR / 256; p++) {
+    for (int p = 0; p < KP; p++) {
+      const int i = tid + 256 * p;
+      const int64_t t = tc + i / QPR;
+      kr[p] = *reinterpret_cast<const V*>(kp + (t < te ? t : tc) * a.ld_qk + (i % QPR) * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < KP; p++) {
       const int i = tid + 256 * p;
       const int row = i / QPR, vi = i % QPR;
-      const int64_t t = tc + row;
-      V kv = zero_vec16<bf16>();
-      if (t < te) kv = *reinterpret_cast<const V*>(kp + t * a.ld_qk + vi * 8);
+      const V kv = tc + row < te ? kr[p] : zero_vec16<bf16>();
       *reinterpret_cast<V*>(sm.u.k + row * LDK + vi * 8) = kv;
       const float ks = row_group_sum<QPR>(sum_sq(kv));
       if (vi == 0) sm.rk[row] = a.use_l2norm ? __builtin_amdgcn_rsqf(ks + 1e-6f) : 1.f;
