@@ -239,13 +239,22 @@ void conv_bwd_kernel(
     for (int j = 0; j < K; j++) dwacc[j][i] = 0.f;
   }
   // taps and bias kept in the activation type (exact: they are read from it),
-  // which leaves registers for the rows in flight
+  // which leaves registers for the rows in flight.  Every lane reads a valid
+  // channel group (an inactive one the first, zeroed after: V > 1 only when V
+  // divides C), so the loads are not behind per-lane branches and are in
+  // flight together.
   Row<E, V> wv[K], bv;
+  const int cw = active ? c0 : 0;
 #pragma unroll
   for (int i = 0; i < V; i++) {
-    bv.v[i] = (active && bias) ? bias[c0 + i] : from_f<E>(0.f);
+    bv.v[i] = bias ? bias[cw + i] : from_f<E>(0.f);
 #pragma unroll
-    for (int j = 0; j < K; j++) wv[j].v[i] = active ? w[(c0 + i) * K + j] : from_f<E>(0.f);
+    for (int j = 0; j < K; j++) wv[j].v[i] = w[(cw + i) * K + j];
+  }
+  if (!active) {
+    bv = zero_row<E, V>();
+#pragma unroll
+    for (int j = 0; j < K; j++) wv[j] = zero_row<E, V>();
   }
   const int64_t cu0 = cu[0];
 
