@@ -259,6 +259,14 @@ void conv_bwd_kernel(
   const int64_t cu0 = cu[0];
 
   const int64_t tile_tokens = (int64_t)R * kRunsPerBlock;
+  // row t of x or dy, zero outside [0, T): the load reads a valid row (row 0
+  // outside; T >= 1 here) and the select zeroes it, so no load sits behind a
+  // per-lane branch and the waits count the rows in flight exactly
+  auto row_at = [&](const E* base, int64_t t) {
+    const bool ok = t >= 0 && t < T;
+    const Row<E, V> r = load_row<E, V>(base + (ok ? t : 0) * C + c0);
+    return ok ? r : zero_row<E, V>();
+  };
   for (int64_t tile = blockIdx.x; active && tile * tile_tokens < T; tile += gridDim.x) {
     const int64_t t0 = tile * tile_tokens + (int64_t)threadIdx.y * R;
     if (t0 >= T) continue;
@@ -276,8 +284,7 @@ void conv_bwd_kernel(
     xw[0] = zero_row<E, V>();
 #pragma unroll
     for (int i = 0; i < K - 1; i++) {
-      const int64_t tau = t0 - (K - 1) + i;
-      xw[i + 1] = (tau >= 0 && tau < T) ? load_row<E, V>(x + tau * C + c0) : zero_row<E, V>();
+      xw[i + 1] = row_at(x, t0 - (K - 1) + i);
     }
 
     // the x and dy rows of the next PD tokens are in flight while a row is
@@ -285,9 +292,8 @@ void conv_bwd_kernel(
     Row<E, V> px[PD], pg[PD];
 #pragma unroll
     for (int d = 0; d < PD; d++) {
-      const int64_t t = t0 + d;
-      px[d] = t < T ? load_row<E, V>(x + t * C + c0) : zero_row<E, V>();
-      pg[d] = t < T ? load_row<E, V>(dy + t * C + c0) : zero_row<E, V>();
+      px[d] = row_at(x, t0 + d);
+      pg[d] = row_at(dy, t0 + d);
     }
 
     int n = find_seq(cu, N, t0);
@@ -307,9 +313,8 @@ void conv_bwd_kernel(
       xw[K - 1] = px[r % PD];
       const Row<E, V> gr = pg[r % PD];
       if (r + PD < DR) {
-        const int64_t tn = t + PD;
-        px[r % PD] = tn < T ? load_row<E, V>(x + tn * C + c0) : zero_row<E, V>();
-        pg[r % PD] = tn < T ? load_row<E, V>(dy + tn * C + c0) : zero_row<E, V>();
+        px[r % PD] = row_at(x, t + PD);
+        pg[r % PD] = row_at(dy, t + PD);
       }
       if (t < T) {
         while (t >= e) {
